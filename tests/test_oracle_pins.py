@@ -1,0 +1,331 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Method source: summary of "Folding Tensor and Sequence Parallelism for Memory-Efficient
+Transformer Training & Inference" (gist.science 2604.26294), §2 (unified sharding,
+zigzag partitioning, all-gathered K/V + FlashAttention, gated-MLP ring with local
+accumulation and no all-reduce). The pages print no numeric example, so the pins are:
+closed forms, invariants the method states, special cases that reduce to textbook or
+library routines, and a scalar-loop brute force on tiny inputs. The last test plants
+plausible mistakes in the oracle and checks that some pin catches each one.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute
+from oracle import tsp_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _read_ranges(name):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            a, b = line.split("-")
+            out.extend(range(int(a), int(b) + 1))
+    return np.array(out, dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------- pins
+# Each pin is a plain function that raises AssertionError on failure, so the planted
+# mistake test at the end can run all of them against a broken oracle.
+
+def pin_zigzag_golden():
+    """S=256, D=4, rank 0 -> chunks 0 and 7 (hand-written fixture)."""
+    np.testing.assert_array_equal(O.zigzag_index(256, 4, 0), _read_ranges("zigzag_s256_d4_r0.txt"))
+
+
+def pin_zigzag_partition():
+    """Over all ranks the maps partition 0..S-1; each map ascends and has S/D rows."""
+    for S, D in [(256, 4), (48, 3), (16384, 8), (16, 1), (40, 5)]:
+        seen = np.zeros(S, dtype=np.int64)
+        for r in range(D):
+            idx = O.zigzag_index(S, D, r)
+            assert idx.shape == (S // D,)
+            assert np.all(np.diff(idx) > 0)
+            seen[idx] += 1
+        assert np.all(seen == 1), (S, D)
+
+
+def pin_zigzag_balance():
+    """Every rank sees exactly C(S+1) causal (query, key) pairs: sum of (pos+1).
+
+    Chunk r contributes C(rC) + C(C+1)/2 and chunk 2D-1-r contributes
+    C(2D-1-r)C + C(C+1)/2, which add to C(2DC + C... ) = C(S+1) for every r; a
+    contiguous split instead grows linearly with r.
+    """
+    for S, D in [(256, 4), (131072, 8), (48, 3)]:
+        C = S // (2 * D)
+        for r in range(D):
+            assert int((O.zigzag_index(S, D, r) + 1).sum()) == C * (S + 1), (S, D, r)
+
+
+def pin_zigzag_identity():
+    np.testing.assert_array_equal(O.zigzag_index(64, 1, 0), np.arange(64))
+
+
+def pin_attention_vs_brute():
+    """Oracle attention equals scalar loops on a tiny input, for every rank of a fold."""
+    rng = _rng(11)
+    B, S, H, hd, D = 1, 16, 2, 4, 2
+    k = rng.standard_normal((B, S, H, hd))
+    v = rng.standard_normal((B, S, H, hd))
+    for r in range(D):
+        pos = brute.zigzag_positions(S, D, r)
+        q = rng.standard_normal((B, len(pos), H, hd))
+        o, lse = O.causal_attention(q, O.zigzag_index(S, D, r), k, v)
+        for i, p in enumerate(pos):
+            for h in range(H):
+                ob, lb = brute.attention_row(list(q[0, i, h]), p, k[0, :, h].tolist(),
+                                             v[0, :, h].tolist(), 1.0 / math.sqrt(hd))
+                np.testing.assert_allclose(o[0, i, h], ob, rtol=1e-12, atol=1e-12)
+                assert abs(lse[0, h, i] - lb) < 1e-12
+
+
+def _sdpa(q, k, v, scale=None):
+    """torch's fp64 CPU causal SDPA on [B, S, H, hd] tensors (a library routine)."""
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def pin_attention_vs_library():
+    """D = 1 is textbook causal attention: torch SDPA in fp64 on the CPU."""
+    rng = _rng(12)
+    B, S, H, hd = 2, 96, 3, 16
+    q, k, v = (rng.standard_normal((B, S, H, hd)) for _ in range(3))
+    o, _ = O.causal_attention(q, O.zigzag_index(S, 1, 0), k, v, row_block=40)
+    np.testing.assert_allclose(o, _sdpa(q, k, v), rtol=1e-10, atol=1e-12)
+
+
+def pin_attention_concat_ranks():
+    """All D ranks' outputs, put back in position order, equal full causal attention."""
+    rng = _rng(13)
+    B, S, H, hd, D = 2, 64, 2, 8, 4
+    q, k, v = (rng.standard_normal((B, S, H, hd)) for _ in range(3))
+    full = _sdpa(q, k, v)
+    glued = np.zeros_like(full)
+    for r in range(D):
+        idx = O.zigzag_index(S, D, r)
+        o, _ = O.causal_attention(q[:, idx], idx, k, v)
+        glued[:, idx] = o
+    np.testing.assert_allclose(glued, full, rtol=1e-10, atol=1e-12)
+
+
+def pin_attention_special_cases():
+    """Rows sum to one; constant V; zero keys give the prefix mean; position 0 gives V_0."""
+    rng = _rng(14)
+    B, S, H, hd, D, r = 1, 48, 2, 8, 3, 1
+    idx = O.zigzag_index(S, D, r)
+    q = rng.standard_normal((B, len(idx), H, hd))
+    k = rng.standard_normal((B, S, H, hd))
+    ones = np.ones((B, S, H, hd))
+    o, _ = O.causal_attention(q, idx, k, ones)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-13)
+    c = rng.standard_normal(hd)
+    o, _ = O.causal_attention(q, idx, k, np.broadcast_to(c, (B, S, H, hd)))
+    np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), rtol=0, atol=1e-13)
+    v = rng.standard_normal((B, S, H, hd))
+    o, lse = O.causal_attention(q, idx, np.zeros((B, S, H, hd)), v)
+    for i, p in enumerate(idx):
+        np.testing.assert_allclose(o[0, i], v[0, :p + 1].mean(axis=0), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[0, :, i], math.log(p + 1), rtol=1e-13)
+    idx0 = O.zigzag_index(S, D, 0)
+    o, _ = O.causal_attention(q, idx0, k, v)
+    assert idx0[0] == 0
+    np.testing.assert_array_equal(o[0, 0], v[0, 0])
+
+
+def pin_attention_scale():
+    """The default scale is 1/sqrt(hd): doubling q equals scale 2/sqrt(hd) (SDPA agrees)."""
+    rng = _rng(15)
+    B, S, H, hd = 1, 32, 1, 16
+    q, k, v = (rng.standard_normal((B, S, H, hd)) for _ in range(3))
+    o, _ = O.causal_attention(q, np.arange(S), k, v)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, scale=1.0 / math.sqrt(hd)), rtol=1e-10, atol=1e-12)
+    o2, _ = O.causal_attention(2 * q, np.arange(S), k, v)
+    np.testing.assert_allclose(o2, _sdpa(q, k, v, scale=2.0 / math.sqrt(hd)), rtol=1e-10, atol=1e-12)
+
+
+def pin_silu_closed_form():
+    """silu(0)=0, silu(1)=e/(1+e), silu(-1)=-1/(1+e), silu(x)->x for large x."""
+    e = math.e
+    got = O.silu(np.array([0.0, 1.0, -1.0, 40.0, -40.0]))
+    want = np.array([0.0, e / (1 + e), -1 / (1 + e), 40.0, -40.0 * math.exp(-40.0)])
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-300)
+
+
+def pin_mlp_vs_brute():
+    rng = _rng(16)
+    d, F = 6, 10
+    x = rng.standard_normal((3, d))
+    w1, w3 = rng.standard_normal((F, d)), rng.standard_normal((F, d))
+    w2 = rng.standard_normal((d, F))
+    y = O.swiglu_mlp(x, w1, w3, w2)
+    for i in range(3):
+        np.testing.assert_allclose(y[i], brute.mlp_row(list(x[i]), w1.tolist(), w3.tolist(), w2.tolist()),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def pin_mlp_shards_sum():
+    """Summing the D ffn-shard partials gives the unsharded MLP (no all-reduce needed)."""
+    rng = _rng(17)
+    d, F = 8, 24
+    x = rng.standard_normal((5, d))
+    w1, w3 = rng.standard_normal((F, d)), rng.standard_normal((F, d))
+    w2 = rng.standard_normal((d, F))
+    full = O.swiglu_mlp(x, w1, w3, w2)
+    for D in (1, 2, 3, 4, 8):
+        parts = [O.mlp_shard_partial(x, w1, w3, w2, j, D) for j in range(D)]
+        np.testing.assert_allclose(sum(parts), full, rtol=1e-12, atol=1e-12)
+        # a single shard is not the whole (unless D = 1)
+        if D > 1:
+            assert np.abs(parts[0] - full).max() > 1e-6
+    np.testing.assert_array_equal(O.swiglu_mlp(np.zeros((2, d)), w1, w3, w2), 0.0)
+
+
+def _tiny_layer(seed, S=16, D=2, d=8, H=2, F=12):
+    rng = _rng(seed)
+    x = rng.standard_normal((1, S, d))
+    w_qkv = rng.standard_normal((3 * d, d)) * 0.3
+    w_o = rng.standard_normal((d, d)) * 0.3
+    w1, w3 = rng.standard_normal((F, d)) * 0.3, rng.standard_normal((F, d)) * 0.3
+    w2 = rng.standard_normal((d, F)) * 0.3
+    return x, w_qkv, w_o, w1, w3, w2
+
+
+def pin_layer_vs_brute():
+    S, D, H = 16, 2, 2
+    x, w_qkv, w_o, w1, w3, w2 = _tiny_layer(18, S=S, D=D, H=H)
+    for r in range(D):
+        got = O.rank_layer(x, w_qkv, w_o, w1, w3, w2, S, D, r, H)
+        want = brute.rank_layer(x[0].tolist(), w_qkv.tolist(), w_o.tolist(), w1.tolist(),
+                                w3.tolist(), w2.tolist(), S, D, r, H)
+        np.testing.assert_array_equal(got["pos"], want["pos"])
+        np.testing.assert_allclose(got["o"][0], np.array(want["o"]), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(got["attn_out"][0], np.array(want["attn_out"]), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(got["mlp_out"][0], np.array(want["mlp_out"]), rtol=1e-11, atol=1e-12)
+
+
+def pin_layer_concat_ranks():
+    """Every rank's layer rows, glued in position order, equal the unsharded layer."""
+    S, D, H = 32, 4, 2
+    x, w_qkv, w_o, w1, w3, w2 = _tiny_layer(19, S=S, D=D, H=H)
+    full = O.rank_layer(x, w_qkv, w_o, w1, w3, w2, S, 1, 0, H)
+    glued = np.zeros_like(full["mlp_out"])
+    for r in range(D):
+        got = O.rank_layer(x, w_qkv, w_o, w1, w3, w2, S, D, r, H)
+        glued[:, got["idx"]] = got["mlp_out"]
+    np.testing.assert_allclose(glued, full["mlp_out"], rtol=1e-11, atol=1e-12)
+
+
+def pin_layer_rows_subset():
+    """Evaluating a subset of rows gives the same values as the full shard at those rows."""
+    S, D, H = 32, 2, 2
+    x, w_qkv, w_o, w1, w3, w2 = _tiny_layer(20, S=S, D=D, H=H)
+    full = O.rank_layer(x, w_qkv, w_o, w1, w3, w2, S, D, 1, H)
+    rows = np.array([0, 3, 9, 15])
+    sub = O.rank_layer(x, w_qkv, w_o, w1, w3, w2, S, D, 1, H, rows=rows)
+    np.testing.assert_allclose(sub["mlp_out"], full["mlp_out"][:, rows], rtol=1e-12, atol=1e-13)
+
+
+def pin_layer_flops():
+    """Closed-form FLOPs equal an explicit count over causal pairs and GEMM shapes."""
+    for (B, S, D, d, H, hd, F) in [(1, 256, 4, 256, 4, 64, 688), (2, 48, 3, 16, 2, 8, 12)]:
+        pairs = 0
+        for r in [0]:
+            pairs = sum(p + 1 for p in brute.zigzag_positions(S, D, r))
+        M = B * S // D
+        count = 2 * M * d * 3 * d + B * H * pairs * 2 * hd * 2 + 2 * M * d * d + 3 * 2 * M * d * F
+        assert O.layer_flops(B, S, D, d, H, hd, F) == count
+    assert O.layer_flops(1, 256, 4, 256, 4, 64, 688) == 109_608_960
+
+
+PINS = [pin_zigzag_golden, pin_zigzag_partition, pin_zigzag_balance, pin_zigzag_identity,
+        pin_attention_vs_brute, pin_attention_vs_library, pin_attention_concat_ranks,
+        pin_attention_special_cases, pin_attention_scale, pin_silu_closed_form,
+        pin_mlp_vs_brute, pin_mlp_shards_sum, pin_layer_vs_brute, pin_layer_concat_ranks,
+        pin_layer_rows_subset, pin_layer_flops]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+def test_zigzag_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        O.zigzag_index(100, 8, 0)  # S not a multiple of 2D
+    with pytest.raises(ValueError):
+        O.zigzag_index(64, 4, 4)   # rank out of range
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _bad_zigzag(S, D, rank):
+    C = S // (2 * D)
+    late = 2 * D - rank  # off by one in the mirror chunk
+    return np.concatenate([np.arange(rank * C, rank * C + C),
+                           np.arange((late % (2 * D)) * C, (late % (2 * D)) * C + C)])
+
+
+def _bad_mask(q_pos, n_keys):
+    keys = np.arange(n_keys)
+    return keys[None, :] < np.asarray(q_pos)[:, None]  # drops the diagonal
+
+
+def _bad_mask_off(q_pos, n_keys):
+    keys = np.arange(n_keys)
+    return keys[None, :] <= np.asarray(q_pos)[:, None] + 1  # one key too many
+
+
+def _bad_project(x, w):
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64)  # transposed operand
+
+
+def _bad_silu(g):
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(g))  # wrong sign
+
+
+def _bad_split_heads(t, n_heads):
+    # interleaves heads instead of giving head h a contiguous block of features
+    return t.reshape(*t.shape[:-1], t.shape[-1] // n_heads, n_heads).swapaxes(-1, -2)
+
+
+MUTANTS = {
+    "zigzag_mirror_off_by_one": ("zigzag_index", _bad_zigzag),
+    "mask_drops_diagonal": ("causal_scores_mask", _bad_mask),
+    "mask_one_key_late": ("causal_scores_mask", _bad_mask_off),
+    "weight_not_transposed": ("project", _bad_project),
+    "silu_sign": ("silu", _bad_silu),
+    "heads_interleaved": ("split_heads", _bad_split_heads),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, bad = MUTANTS[name]
+    monkeypatch.setattr(O, attr, bad)
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
