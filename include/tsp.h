@@ -1,0 +1,183 @@
+/*
+ * tsp.h -- C ABI of the TSP rank-shard layer forward for AMD MI355X (gfx950).
+ *
+ * Method: "Folding Tensor and Sequence Parallelism for Memory-Efficient Transformer
+ * Training & Inference" (summary pages on gist.science, paper 2604.26294), cited here
+ * as [TSP §n] for section n of that summary. TSP folds tensor and sequence parallelism
+ * onto one axis of D ranks: each rank holds a zigzag shard of the tokens and sees the
+ * weights as D shards [TSP §2, unified sharding]. This library computes ONE rank's share
+ * of a transformer layer on one GPU:
+ *
+ *   a1  zigzag map      rank r's local rows are chunks r and 2D-1-r of 2D equal chunks
+ *   a2  QKV projection  [Q|K|V] = X_r W_qkv^T; own K/V rows land in the full-sequence
+ *                       K/V buffers at their global positions       [TSP §2, attention]
+ *   a3  attention       causal softmax attention of the rank's queries against the
+ *                       full-sequence K/V (what the all-gather delivers) [TSP §2]
+ *   a4  W_O projection  A = O W_o^T
+ *   a5  gated MLP ring  for each of the D ffn shards j seen in ring order,
+ *                       acc (+)= (silu(A W1_j^T) * (A W3_j^T)) W2_j^T, fp32, no
+ *                       all-reduce                                 [TSP §2, gated MLP]
+ *
+ * Conventions shared by every entry point
+ *   - Element types: "bf16" is IEEE bfloat16 (uint16 storage); "f32" is float.
+ *   - Layouts are row-major and dense unless a leading dimension is given.
+ *     Weights are [out_features, in_features], so every GEMM operand is contiguous
+ *     along its reduction dimension. W_qkv rows are [W_q; W_k; W_v]; head h owns rows
+ *     h*hd .. h*hd+hd-1 of each block. Feature f of a token vector belongs to head
+ *     f / hd.
+ *   - Local row order: a rank's 2C = S/D rows per sequence list chunk r (positions
+ *     r*C .. r*C+C-1) then chunk 2D-1-r, both ascending; C = S/(2D).
+ *   - Device pointers are allocated and owned by the caller, must be 16-byte aligned,
+ *     and outputs must not alias inputs. The library never allocates or frees memory,
+ *     never synchronises, and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Kernels are enqueued on it
+ *     and run asynchronously; errors raised while they run surface at the caller's
+ *     next synchronisation of that stream.
+ *   - Every entry point returns a tsp_status. Argument errors are decided on the host
+ *     before any HIP call, so they are deterministic and safe without a GPU. The
+ *     message of the last error on the calling thread is tsp_last_error().
+ *   - Numerics: bf16 inputs, fp32 accumulation, fp32 softmax; intermediates stored as
+ *     bf16 use round-to-nearest-even; the MLP accumulator is fp32.
+ */
+#ifndef TSP_H
+#define TSP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define TSP_API __attribute__((visibility("default")))
+#else
+#define TSP_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* tsp_stream_t; /* a hipStream_t */
+
+typedef enum {
+  TSP_OK = 0,
+  TSP_ERR_NULL = 1,        /* a required pointer is NULL */
+  TSP_ERR_SHAPE = 2,       /* S % (2D) != 0, d != H*hd, F % D != 0, a size <= 0 ... */
+  TSP_ERR_RANK = 3,        /* rank outside [0, D) */
+  TSP_ERR_UNSUPPORTED = 4, /* head_dim not in {64, 128}, size beyond int32 limits */
+  TSP_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returns */
+  TSP_ERR_ALIGN = 6,       /* a device pointer is not 16-byte aligned */
+  TSP_ERR_HIP = 7          /* a HIP launch failed (message has the HIP error string) */
+} tsp_status;
+
+/* Shape of one rank's layer.  [TSP §2] */
+typedef struct {
+  int32_t batch;     /* B: sequences per call */
+  int32_t fold;      /* D: number of ranks on the TSP axis */
+  int64_t seq_len;   /* S: tokens per sequence over all ranks; S % (2D) == 0 */
+  int32_t rank;      /* r in [0, D) */
+  int32_t d_model;   /* d = n_heads * head_dim */
+  int32_t n_heads;   /* H */
+  int32_t head_dim;  /* hd in {64, 128} */
+  int32_t ffn;       /* F: SwiGLU hidden size over all shards; F % D == 0 */
+  int32_t reserved;  /* must be 0 */
+  int64_t w2_ld;     /* row stride (elements) of each W2 shard; 0 means F/D (a
+                        contiguous [d, F/D] shard); F for views into a full W2 */
+  float scale;       /* softmax scale; <= 0 means 1/sqrt(head_dim) */
+} tsp_layer_desc;
+
+/* Library version, (major << 16) | minor. */
+TSP_API int tsp_version(void);
+
+/* Message of the last non-OK status returned on the calling thread ("" if none). */
+TSP_API const char* tsp_last_error(void);
+
+/*
+ * a1  Zigzag index map.  [TSP §2, zigzag partitioning]
+ * Writes the global positions of rank `rank`'s idx_len = S/D local rows to HOST memory
+ * idx_out: idx[i] = r*C + i for i < C, and (2D-1-r)*C + (i-C) for C <= i < 2C, with
+ * C = S/(2D). Pairing chunk r with its mirror 2D-1-r gives every rank C*(S+1) causal
+ * (query, key) pairs per sequence and head. Exact integer arithmetic.
+ * Errors: TSP_ERR_NULL (idx_out), TSP_ERR_SHAPE (S <= 0, D <= 0, S % 2D != 0,
+ * idx_len != S/D), TSP_ERR_RANK.
+ */
+TSP_API int tsp_zigzag_index(int64_t S, int32_t D, int32_t rank, int64_t* idx_out, int64_t idx_len);
+
+/*
+ * a2  Packed QKV projection of a rank's token shard.  [TSP §2, attention layers: local
+ * projections with the packed W_Q/W_K/W_V shards]
+ *   x      bf16 [B, 2C, d]   the rank's tokens in local row order
+ *   w_qkv  bf16 [3d, d]      [W_q; W_k; W_v]
+ *   q_out  bf16 [B, 2C, d]   Q in local row order (= [B, 2C, H, hd]); may be NULL when
+ *                            only K/V are wanted (filling the rows of a peer rank)
+ *   k_full, v_full bf16 [B, S, d]  full-sequence K and V in natural position order; the
+ *                            call writes ONLY rows b*S + idx[i] (the rank's own rows)
+ * This is also how a test or benchmark on one GPU stands in for the K/V all-gather:
+ * calling it for every peer rank fills the peers' rows.
+ */
+TSP_API int tsp_qkv_fwd(const void* x, const void* w_qkv, void* q_out, void* k_full, void* v_full,
+                int32_t B, int64_t S, int32_t D, int32_t rank, int32_t n_heads,
+                int32_t head_dim, tsp_stream_t stream);
+
+/*
+ * a3  Causal attention of a rank's queries against the full-sequence K/V.
+ * [TSP §2, attention layers: all-gathered K/V, FlashAttention, zigzag balance]
+ *   q       bf16 [B, 2C, H, hd]  local row order
+ *   k_full, v_full bf16 [B, S, H, hd]  natural order
+ *   o       bf16 [B, 2C, H, hd]  output, local row order
+ *   lse     f32  [B, H, 2C] natural-log sum of exp of the scaled visible scores, or
+ *           NULL
+ * Row i at position p = idx[i] attends keys 0..p (diagonal included) with weights
+ * softmax(scale * q.k). Only key rows < (2D-rank)*C are read: rows after the rank's
+ * last position are never touched, so the caller need not fill them.
+ */
+TSP_API int tsp_attn_fwd(const void* q, const void* k_full, const void* v_full, void* o, float* lse,
+                 int32_t B, int64_t S, int32_t D, int32_t rank, int32_t n_heads,
+                 int32_t head_dim, float scale, tsp_stream_t stream);
+
+/* Workspace bytes tsp_mlp_shard_accum needs for M rows and shard width Fs. */
+TSP_API size_t tsp_mlp_workspace_size(int64_t M, int32_t Fs);
+
+/*
+ * a5  One ring step of the gated MLP.  [TSP §2, gated MLP layers: the W1/W2/W3 shards
+ * rotate; each rank accumulates the partial outputs locally, no all-reduce]
+ *   x     bf16 [M, d]        MLP input rows (the W_O output)
+ *   w1_j  bf16 [Fs, d]       gate rows of shard j
+ *   w3_j  bf16 [Fs, d]       up rows of shard j
+ *   w2_j  bf16 [d, Fs] with row stride ld_w2 >= Fs (Fs for a received contiguous
+ *         shard, F for a column block of a full W2)
+ *   acc   f32 [M, d]         accumulate == 0: acc = partial;  != 0: acc += partial
+ *   ws    device workspace of at least tsp_mlp_workspace_size(M, Fs) bytes (holds the
+ *         bf16 gated hidden H = silu(x W1_j^T) * (x W3_j^T), [M, Fs])
+ * Calls on one stream applied in ring order give a deterministic fp32 sum.
+ */
+TSP_API int tsp_mlp_shard_accum(const void* x, const void* w1_j, const void* w3_j, const void* w2_j,
+                        int64_t ld_w2, float* acc, int64_t M, int32_t d, int32_t Fs,
+                        int32_t accumulate, void* ws, size_t ws_bytes, tsp_stream_t stream);
+
+/* Workspace bytes tsp_layer_fwd needs for `desc` (0 if desc is invalid). */
+TSP_API size_t tsp_layer_workspace_size(const tsp_layer_desc* desc);
+
+/*
+ * a2 -> a5  One rank's whole layer forward.  [TSP §2]
+ *   x_shard  bf16 [B, 2C, d]  the rank's tokens, local row order
+ *   w_qkv    bf16 [3d, d]; w_o bf16 [d, d]
+ *   w1, w3   arrays of D device pointers; w1[j], w3[j] bf16 [F/D, d] = ffn shard j
+ *   w2       array of D device pointers; w2[j] bf16 [d, F/D] with row stride
+ *            desc->w2_ld (0 = F/D)
+ *   k_full, v_full  bf16 [B, S, H, hd], IN/OUT: on entry the rows of the other ranks
+ *            hold what the K/V all-gather delivers; the call writes the rank's own rows
+ *   attn_out bf16 [B, 2C, d]  A = O W_o^T (the MLP input)
+ *   mlp_out  f32  [B, 2C, d]  sum over the D shards, taken in ring order
+ *            j = (r - t) mod D for t = 0 .. D-1
+ *   ws       device workspace, at least tsp_layer_workspace_size(desc) bytes
+ * The pointer arrays w1/w3/w2 live in HOST memory.
+ */
+TSP_API int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const void* w_qkv,
+                  const void* w_o, const void* const* w1, const void* const* w3,
+                  const void* const* w2, void* k_full, void* v_full, void* attn_out,
+                  float* mlp_out, void* ws, size_t ws_bytes, tsp_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSP_H */

@@ -1,0 +1,225 @@
+// tsp_api.hip -- the C ABI declared in include/tsp.h: argument checks on the host,
+// workspace carving, and the launch sequence of one TSP rank's layer on the caller's
+// stream. The library allocates nothing and keeps no state between calls.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/tsp.h"
+#include "tsp_device.h"
+#include "tsp_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return TSP_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TSP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return TSP_OK;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+constexpr int64_t kMaxI32 = 2147483647;
+
+// Checks shared by every entry point that knows (B, S, D, rank): S % 2D == 0, rank
+// in range, and local-row counts that fit the kernels' 32-bit row indices.
+int check_fold(int64_t B, int64_t S, int64_t D, int64_t rank) {
+  if (B < 1) return fail(TSP_ERR_SHAPE, "batch must be >= 1 (got %lld)", (long long)B);
+  if (D < 1) return fail(TSP_ERR_SHAPE, "fold D must be >= 1 (got %lld)", (long long)D);
+  if (S < 1 || S % (2 * D) != 0)
+    return fail(TSP_ERR_SHAPE, "seq_len S=%lld must be a positive multiple of 2D=%lld", (long long)S,
+                (long long)(2 * D));
+  if (rank < 0 || rank >= D) return fail(TSP_ERR_RANK, "rank %lld outside [0, %lld)", (long long)rank, (long long)D);
+  if (B * (S / D) > kMaxI32 / 4) return fail(TSP_ERR_UNSUPPORTED, "B*S/D too large for 32-bit row indices");
+  return TSP_OK;
+}
+
+int check_heads(int64_t H, int64_t hd) {
+  if (H < 1) return fail(TSP_ERR_SHAPE, "n_heads must be >= 1 (got %lld)", (long long)H);
+  if (hd != 64 && hd != 128) return fail(TSP_ERR_UNSUPPORTED, "head_dim %lld not in {64, 128}", (long long)hd);
+  if (H * hd > 65536) return fail(TSP_ERR_UNSUPPORTED, "d_model = H*hd = %lld above 65536", (long long)(H * hd));
+  return TSP_OK;
+}
+
+size_t mlp_ws_bytes(int64_t M, int64_t Fs) { return round_up((size_t)M * (size_t)round_up((size_t)Fs, 8) * 2, kAlign); }
+
+}  // namespace
+
+extern "C" {
+
+int tsp_version(void) { return (1 << 16) | 0; }
+
+const char* tsp_last_error(void) { return g_err; }
+
+int tsp_zigzag_index(int64_t S, int32_t D, int32_t rank, int64_t* idx_out, int64_t idx_len) {
+  if (!idx_out) return fail(TSP_ERR_NULL, "idx_out is NULL");
+  if (int rc = check_fold(1, S, D, rank)) return rc;
+  if (idx_len != S / D)
+    return fail(TSP_ERR_SHAPE, "idx_len %lld != S/D = %lld", (long long)idx_len, (long long)(S / D));
+  const int64_t C = S / (2 * (int64_t)D);
+  for (int64_t i = 0; i < 2 * C; ++i) idx_out[i] = tsp::zigzag_pos(i, C, rank, D);
+  return ok();
+}
+
+int tsp_qkv_fwd(const void* x, const void* w_qkv, void* q_out, void* k_full, void* v_full, int32_t B, int64_t S,
+                int32_t D, int32_t rank, int32_t n_heads, int32_t head_dim, tsp_stream_t stream) {
+  if (!x || !w_qkv || !k_full || !v_full) return fail(TSP_ERR_NULL, "x, w_qkv, k_full and v_full must be non-NULL");
+  if (int rc = check_fold(B, S, D, rank)) return rc;
+  if (int rc = check_heads(n_heads, head_dim)) return rc;
+  if (misaligned(x) || misaligned(w_qkv) || misaligned(k_full) || misaligned(v_full) || misaligned(q_out))
+    return fail(TSP_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const int d = n_heads * head_dim;
+  if (int rc = hip_status(tsp::launch_qkv(x, w_qkv, q_out, k_full, v_full, B, S, D, rank, d,
+                                          static_cast<hipStream_t>(stream)),
+                          "qkv projection launch"))
+    return rc;
+  return ok();
+}
+
+int tsp_attn_fwd(const void* q, const void* k_full, const void* v_full, void* o, float* lse, int32_t B, int64_t S,
+                 int32_t D, int32_t rank, int32_t n_heads, int32_t head_dim, float scale, tsp_stream_t stream) {
+  if (!q || !k_full || !v_full || !o) return fail(TSP_ERR_NULL, "q, k_full, v_full and o must be non-NULL");
+  if (int rc = check_fold(B, S, D, rank)) return rc;
+  if (int rc = check_heads(n_heads, head_dim)) return rc;
+  if (misaligned(q) || misaligned(k_full) || misaligned(v_full) || misaligned(o) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(TSP_ERR_ALIGN, "q/k/v/o must be 16-byte aligned and lse 4-byte aligned");
+  if (!(scale == scale) || isinf(scale)) return fail(TSP_ERR_SHAPE, "scale must be finite");
+  if (int rc = hip_status(tsp::launch_attn(q, k_full, v_full, o, lse, B, S, D, rank, n_heads, head_dim, scale,
+                                           static_cast<hipStream_t>(stream)),
+                          "attention launch"))
+    return rc;
+  return ok();
+}
+
+size_t tsp_mlp_workspace_size(int64_t M, int32_t Fs) {
+  if (M < 1 || Fs < 1) return 0;
+  return mlp_ws_bytes(M, Fs);
+}
+
+int tsp_mlp_shard_accum(const void* x, const void* w1_j, const void* w3_j, const void* w2_j, int64_t ld_w2, float* acc,
+                        int64_t M, int32_t d, int32_t Fs, int32_t accumulate, void* ws, size_t ws_bytes,
+                        tsp_stream_t stream) {
+  if (!x || !w1_j || !w3_j || !w2_j || !acc || !ws)
+    return fail(TSP_ERR_NULL, "x, w1_j, w3_j, w2_j, acc and ws must be non-NULL");
+  if (M < 1 || d < 1 || Fs < 1) return fail(TSP_ERR_SHAPE, "M, d and Fs must be >= 1");
+  if (M > kMaxI32 / 4) return fail(TSP_ERR_UNSUPPORTED, "M too large for 32-bit row indices");
+  if (ld_w2 < Fs) return fail(TSP_ERR_SHAPE, "ld_w2 %lld < Fs %d", (long long)ld_w2, Fs);
+  if (misaligned(x) || misaligned(w1_j) || misaligned(w3_j) || misaligned(w2_j) || misaligned(acc) || misaligned(ws))
+    return fail(TSP_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  if (ws_bytes < mlp_ws_bytes(M, Fs))
+    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, mlp_ws_bytes(M, Fs));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ldh = (int64_t)round_up((size_t)Fs, 8);
+  if (int rc = hip_status(tsp::launch_gate_up(x, d, w1_j, w3_j, d, ws, ldh, (int)M, Fs, d, s), "gate/up launch"))
+    return rc;
+  if (int rc = hip_status(tsp::launch_down_acc(ws, ldh, w2_j, ld_w2, acc, d, (int)M, d, Fs, accumulate ? 1 : 0, s),
+                          "down projection launch"))
+    return rc;
+  return ok();
+}
+
+namespace {
+
+int check_desc(const tsp_layer_desc* desc) {
+  if (!desc) return fail(TSP_ERR_NULL, "desc is NULL");
+  if (desc->reserved != 0) return fail(TSP_ERR_SHAPE, "desc->reserved must be 0");
+  if (int rc = check_fold(desc->batch, desc->seq_len, desc->fold, desc->rank)) return rc;
+  if (int rc = check_heads(desc->n_heads, desc->head_dim)) return rc;
+  if (desc->d_model != desc->n_heads * desc->head_dim)
+    return fail(TSP_ERR_SHAPE, "d_model %d != n_heads*head_dim = %d", desc->d_model, desc->n_heads * desc->head_dim);
+  if (desc->ffn < 1 || desc->ffn % desc->fold != 0)
+    return fail(TSP_ERR_SHAPE, "ffn %d must be a positive multiple of D=%d", desc->ffn, desc->fold);
+  const int64_t Fs = desc->ffn / desc->fold;
+  if (desc->w2_ld != 0 && desc->w2_ld < Fs)
+    return fail(TSP_ERR_SHAPE, "w2_ld %lld < F/D = %lld", (long long)desc->w2_ld, (long long)Fs);
+  if (!(desc->scale == desc->scale) || isinf(desc->scale)) return fail(TSP_ERR_SHAPE, "scale must be finite");
+  return TSP_OK;
+}
+
+struct LayerCarve {
+  size_t q_off, o_off, h_off, total;
+};
+
+LayerCarve carve(const tsp_layer_desc* d) {
+  const size_t M = (size_t)d->batch * (size_t)(d->seq_len / d->fold);
+  const size_t act = round_up(M * (size_t)d->d_model * 2, kAlign);
+  LayerCarve c;
+  c.q_off = 0;
+  c.o_off = act;
+  c.h_off = 2 * act;
+  c.total = 2 * act + mlp_ws_bytes((int64_t)M, d->ffn / d->fold);
+  return c;
+}
+
+}  // namespace
+
+size_t tsp_layer_workspace_size(const tsp_layer_desc* desc) {
+  if (check_desc(desc) != TSP_OK) return 0;
+  return carve(desc).total;
+}
+
+int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const void* w_qkv, const void* w_o,
+                  const void* const* w1, const void* const* w3, const void* const* w2, void* k_full, void* v_full,
+                  void* attn_out, float* mlp_out, void* ws, size_t ws_bytes, tsp_stream_t stream) {
+  if (int rc = check_desc(desc)) return rc;
+  if (!x_shard || !w_qkv || !w_o || !w1 || !w3 || !w2 || !k_full || !v_full || !attn_out || !mlp_out || !ws)
+    return fail(TSP_ERR_NULL, "a required pointer is NULL");
+  const int D = desc->fold;
+  for (int j = 0; j < D; ++j) {
+    if (!w1[j] || !w3[j] || !w2[j]) return fail(TSP_ERR_NULL, "weight shard %d pointer is NULL", j);
+    if (misaligned(w1[j]) || misaligned(w3[j]) || misaligned(w2[j]))
+      return fail(TSP_ERR_ALIGN, "weight shard %d pointer is not 16-byte aligned", j);
+  }
+  if (misaligned(x_shard) || misaligned(w_qkv) || misaligned(w_o) || misaligned(k_full) || misaligned(v_full) ||
+      misaligned(attn_out) || misaligned(mlp_out) || misaligned(ws))
+    return fail(TSP_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const LayerCarve c = carve(desc);
+  if (ws_bytes < c.total) return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, c.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int B = desc->batch, H = desc->n_heads, hd = desc->head_dim, d = desc->d_model, r = desc->rank;
+  const int64_t S = desc->seq_len;
+  const int M = (int)(B * (S / D));
+  const int Fs = desc->ffn / D;
+  const int64_t ldw2 = desc->w2_ld ? desc->w2_ld : Fs;
+  const int64_t ldh = (int64_t)round_up((size_t)Fs, 8);
+  char* base = static_cast<char*>(ws);
+  void* q = base + c.q_off;
+  void* o = base + c.o_off;
+  void* hbuf = base + c.h_off;
+
+  if (int rc = hip_status(tsp::launch_qkv(x_shard, w_qkv, q, k_full, v_full, B, S, D, r, d, s), "qkv launch"))
+    return rc;
+  if (int rc = hip_status(tsp::launch_attn(q, k_full, v_full, o, nullptr, B, S, D, r, H, hd, desc->scale, s),
+                          "attention launch"))
+    return rc;
+  if (int rc = hip_status(tsp::launch_proj_bf16(o, d, w_o, d, attn_out, d, M, d, d, s), "W_O launch")) return rc;
+  for (int t = 0; t < D; ++t) {
+    const int j = ((r - t) % D + D) % D;  // shard held at ring step t
+    if (int rc = hip_status(tsp::launch_gate_up(attn_out, d, w1[j], w3[j], d, hbuf, ldh, M, Fs, d, s), "gate/up launch"))
+      return rc;
+    if (int rc = hip_status(tsp::launch_down_acc(hbuf, ldh, w2[j], ldw2, mlp_out, d, M, d, Fs, t > 0 ? 1 : 0, s),
+                            "down projection launch"))
+      return rc;
+  }
+  return ok();
+}
+
+}  // extern "C"

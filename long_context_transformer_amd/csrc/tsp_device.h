@@ -1,0 +1,69 @@
+// tsp_device.h -- device helpers shared by the gfx950 kernels of the TSP rank-shard layer.
+//
+// CDNA4 (gfx950) specifics used here:
+//  * wave64; bf16 MFMA v_mfma_f32_32x32x16_bf16: operand A gives row i = lane%32,
+//    operand B gives column j = lane%32, each lane supplying 8 bf16 of the reduction
+//    dimension selected by lane/32; the 32x32 fp32 result puts column j = lane%32 and
+//    rows 8*(r/4) + 4*(lane/32) + r%4 in accumulator register r (r = 0..15).
+//    Only the pairing "lane group g, element e of A meets lane group g, element e of
+//    B" matters for the reduction, so any consistent relabelling of the reduction
+//    index between the two operands gives the same product.
+//  * 8 XCDs: consecutive workgroup ids are dealt round-robin to the XCDs, each with
+//    its own L2; xcd_remap gives every XCD a contiguous range of logical work items
+//    so that items sharing operands share an L2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsp {
+
+typedef uint16_t bf16_t;  // storage type of a bfloat16 in global memory
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even; gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+
+__device__ __forceinline__ bf16_t to_bf16(float x) {
+  __bf16 v = (__bf16)x;
+  return __builtin_bit_cast(bf16_t, v);
+}
+
+// Global position of local row i of rank r, for chunk length C and fold D.
+// Rows 0..C-1 are chunk r, rows C..2C-1 are the mirror chunk 2D-1-r.
+__host__ __device__ __forceinline__ int64_t zigzag_pos(int64_t i, int64_t C, int r, int D) {
+  return i < C ? (int64_t)r * C + i : (int64_t)(2 * D - 1 - r) * C + (i - C);
+}
+
+// Bijection of [0, n) that maps the workgroups of XCD x (blockIdx % 8 == x) onto a
+// contiguous block of logical ids, in dispatch order.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int x = bid % kNumXcd;
+  const int local = bid / kNumXcd;
+  const int q = n / kNumXcd;
+  const int rem = n % kNumXcd;
+  const int start = x * q + (x < rem ? x : rem);
+  return start + local;
+}
+
+}  // namespace tsp

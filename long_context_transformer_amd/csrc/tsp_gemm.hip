@@ -1,0 +1,327 @@
+// tsp_gemm.hip -- bf16 "NT" GEMM family on gfx950 MFMA for the TSP rank-shard layer.
+//
+// Every projection of the layer multiplies activations [M, K] by a weight stored
+// [N, K] (out_features x in_features), so both operands are contiguous along the
+// reduction: C[M, N] = A[M, K] B[N, K]^T. One kernel template serves the four uses
+// (TSP summary §2: local QKV projections, W_O, and the gated-MLP shard passes), each
+// with its own fused epilogue:
+//   EpiQKV      Q to a dense buffer, K/V rows scattered to their global zigzag positions
+//   EpiBf16     plain bf16 store (W_O)
+//   EpiSwiGLU   two weights at once (W1, W3); stores silu(G) * U as bf16
+//   EpiAcc      fp32 accumulator, overwrite or add (the down projection of a shard)
+//
+// Tiling: 256 threads = 4 waves in a 2 x 2 grid over a BM x BN output tile; each wave
+// owns a (BM/2) x (BN/2) block made of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16).
+// K advances in stages of 64 through a double-buffered LDS tile: while the MFMAs run
+// on stage k, the global loads of stage k+1 are in flight in registers, then written to
+// the other LDS buffer; one barrier per stage. In LDS each operand row holds 64 bf16 as
+// eight 16-byte chunks stored at position chunk ^ ((row / 2) % 8), so the 16-byte
+// fragment reads of 16 consecutive rows at one chunk hit 16 distinct bank groups.
+// The MFMA takes the weight tile as its A operand and the activation tile as B, so the
+// 32 x 32 result gives each lane four consecutive output columns of one row: 8-byte
+// bf16 stores or 16-byte fp32 read-modify-writes in the epilogue.
+// Workgroup -> tile: XCD-contiguous ranges (xcd_remap), then groups of 8 row-tiles
+// walked column-major so tiles running together on one XCD share A and B in its L2.
+#include "tsp_device.h"
+#include "tsp_internal.h"
+
+namespace tsp {
+namespace {
+
+constexpr int BK = 64;
+constexpr int kThreads = 256;
+constexpr int kGroupM = 8;
+
+struct Operands {
+  const bf16_t* a;
+  int64_t lda;
+  const bf16_t* b;
+  const bf16_t* b2;  // second weight of the gated pair (same shape and stride as b)
+  int64_t ldb;
+  int M, N, K;
+};
+
+// 16-byte chunk (8 bf16) of `row`, elements k .. k+7, of an operand with `rows` rows;
+// zero outside the operand. VEC: K % 8 == 0, ld % 8 == 0, 16-byte aligned base.
+template <bool VEC>
+__device__ __forceinline__ uint4 load_chunk(const bf16_t* base, int64_t ld, int row, int rows, int k,
+                                            int K) {
+  if constexpr (VEC) {
+    if (row < rows && k < K) return *reinterpret_cast<const uint4*>(base + (int64_t)row * ld + k);
+    return make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (row < rows) {
+      const bf16_t* p = base + (int64_t)row * ld;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t v = (k + e < K) ? (uint32_t)p[k + e] : 0u;
+        w[e >> 1] |= v << (16 * (e & 1));
+      }
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+// ---------------------------------------------------------------------------- epilogues
+struct EpiBf16 {
+  bf16_t* c;
+  int64_t ldc;
+  __device__ __forceinline__ void operator()(int m, int n, const f32x4& v, int M, int N) const {
+    if (m >= M || n >= N) return;
+    bf16_t* p = c + (int64_t)m * ldc + n;
+    if (n + 4 <= N && (ldc & 3) == 0) {
+      *reinterpret_cast<uint2*>(p) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+    } else {
+      for (int e = 0; e < 4 && n + e < N; ++e) p[e] = to_bf16(v[e]);
+    }
+  }
+};
+
+struct EpiQKV {
+  bf16_t* q;  // may be null
+  bf16_t* k;
+  bf16_t* v;
+  int d;       // model width: columns [0,d) are Q, [d,2d) K, [2d,3d) V
+  int R;       // local rows per sequence (2C)
+  int64_t C;   // zigzag chunk length
+  int rank, D;
+  int64_t S;
+  __device__ __forceinline__ void operator()(int m, int n, const f32x4& val, int M, int N) const {
+    if (m >= M || n >= N) return;
+    const int which = n / d;
+    const int col = n - which * d;
+    const uint2 packed = pack_bf16x4(val[0], val[1], val[2], val[3]);
+    if (which == 0) {
+      if (q) *reinterpret_cast<uint2*>(q + (int64_t)m * d + col) = packed;
+      return;
+    }
+    const int b = m / R;
+    const int i = m - b * R;
+    const int64_t row = (int64_t)b * S + zigzag_pos(i, C, rank, D);
+    bf16_t* dst = (which == 1 ? k : v) + row * d + col;
+    *reinterpret_cast<uint2*>(dst) = packed;
+  }
+};
+
+struct EpiSwiGLU {
+  bf16_t* h;
+  int64_t ldh;
+  __device__ __forceinline__ static float silu(float g) { return g / (1.0f + __expf(-g)); }
+  __device__ __forceinline__ void operator()(int m, int n, const f32x4& g, const f32x4& u, int M,
+                                             int N) const {
+    if (m >= M || n >= N) return;
+    float r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = silu(g[e]) * u[e];
+    bf16_t* p = h + (int64_t)m * ldh + n;
+    if (n + 4 <= N && (ldh & 3) == 0) {
+      *reinterpret_cast<uint2*>(p) = pack_bf16x4(r[0], r[1], r[2], r[3]);
+    } else {
+      for (int e = 0; e < 4 && n + e < N; ++e) p[e] = to_bf16(r[e]);
+    }
+  }
+};
+
+struct EpiAcc {
+  float* c;
+  int64_t ldc;
+  int accumulate;
+  __device__ __forceinline__ void operator()(int m, int n, const f32x4& v, int M, int N) const {
+    if (m >= M || n >= N) return;
+    float* p = c + (int64_t)m * ldc + n;
+    if (n + 4 <= N && (ldc & 3) == 0) {
+      f32x4 o = v;
+      if (accumulate) o += *reinterpret_cast<const f32x4*>(p);
+      *reinterpret_cast<f32x4*>(p) = o;
+    } else {
+      for (int e = 0; e < 4 && n + e < N; ++e) p[e] = accumulate ? p[e] + v[e] : v[e];
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------- kernel
+template <int BM, int BN, bool DUAL, bool VEC, class Epi>
+__global__ __launch_bounds__(kThreads) void gemm_nt(Operands op, Epi epi, int tiles_m, int tiles_n) {
+  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int AP = BM / 32, BP = BN / 32;  // load passes: 256 threads cover 32 rows x 8 chunks
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2][(BM + NB * BN) * BK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hl = lane >> 5;
+
+  const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+  const int span = kGroupM * tiles_n;
+  const int first_m = (t / span) * kGroupM;
+  const int gsz = min(tiles_m - first_m, kGroupM);
+  const int in_g = t - (t / span) * span;
+  const int m0 = (first_m + in_g % gsz) * BM;
+  const int n0 = (in_g / gsz) * BN;
+
+  const int lc = tid & 7;  // chunk this thread moves
+  const int lr = tid >> 3;  // first row this thread moves
+
+  uint4 ra[AP];
+  uint4 rb[NB][BP];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < AP; ++p) ra[p] = load_chunk<VEC>(op.a, op.lda, m0 + lr + 32 * p, op.M, k0 + 8 * lc, op.K);
+#pragma unroll
+    for (int p = 0; p < BP; ++p) rb[0][p] = load_chunk<VEC>(op.b, op.ldb, n0 + lr + 32 * p, op.N, k0 + 8 * lc, op.K);
+    if constexpr (DUAL) {
+#pragma unroll
+      for (int p = 0; p < BP; ++p) rb[1][p] = load_chunk<VEC>(op.b2, op.ldb, n0 + lr + 32 * p, op.N, k0 + 8 * lc, op.K);
+    }
+  };
+  auto sstore = [&](int buf) {
+    bf16_t* sa = smem[buf];
+#pragma unroll
+    for (int p = 0; p < AP; ++p) *reinterpret_cast<uint4*>(sa + swz(lr + 32 * p, lc)) = ra[p];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      bf16_t* sb = sa + BM * BK + nb * BN * BK;
+#pragma unroll
+      for (int p = 0; p < BP; ++p) *reinterpret_cast<uint4*>(sb + swz(lr + 32 * p, lc)) = rb[nb][p];
+    }
+  };
+
+  f32x16 acc[NB][MI][NI];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) acc[nb][mi][ni] = f32x16{};
+
+  const int nk = (op.K + BK - 1) / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+    const bf16_t* sa = smem[cur];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int ch = 2 * ks + hl;
+      bf16x8 af[MI];
+      bf16x8 bfr[NB][NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        af[mi] = as_bf16x8(*reinterpret_cast<const uint4*>(sa + swz(wm * WTM + mi * 32 + l32, ch)));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16_t* sb = sa + BM * BK + nb * BN * BK;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          bfr[nb][ni] = as_bf16x8(*reinterpret_cast<const uint4*>(sb + swz(wn * WTN + ni * 32 + l32, ch)));
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) acc[nb][mi][ni] = mfma32x32x16(bfr[nb][ni], af[mi], acc[nb][mi][ni]);
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int m = m0 + wm * WTM + mi * 32 + l32;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WTN + ni * 32 + 8 * g + 4 * hl;
+        const f32x4 v0 = {acc[0][mi][ni][4 * g], acc[0][mi][ni][4 * g + 1], acc[0][mi][ni][4 * g + 2],
+                          acc[0][mi][ni][4 * g + 3]};
+        if constexpr (DUAL) {
+          const f32x4 v1 = {acc[1][mi][ni][4 * g], acc[1][mi][ni][4 * g + 1], acc[1][mi][ni][4 * g + 2],
+                            acc[1][mi][ni][4 * g + 3]};
+          epi(m, n, v0, v1, op.M, op.N);
+        } else {
+          epi(m, n, v0, op.M, op.N);
+        }
+      }
+    }
+  }
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <int BM, int BN, bool DUAL, bool VEC, class Epi>
+hipError_t run_tiles(const Operands& op, const Epi& epi, hipStream_t s) {
+  const int tm = (op.M + BM - 1) / BM;
+  const int tn = (op.N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_nt<BM, BN, DUAL, VEC, Epi>), dim3(tm * tn), dim3(kThreads), 0, s, op, epi, tm, tn);
+  return hipGetLastError();
+}
+
+// Large problems take the 256 x 256 tile (256 x 128 for the gated pair, which carries
+// two accumulators); when that leaves fewer tiles than CUs the 128 x 128 (128 x 64)
+// tile keeps the chip busy. Operands that are not 16-byte vectorisable (odd K or
+// strides, only in tiny shapes) take the element-wise loader with the small tile.
+constexpr int64_t kBigTileMin = 256;
+
+template <class Epi>
+hipError_t run_single(const Operands& op, const Epi& epi, hipStream_t s) {
+  const bool vec = (op.K % 8 == 0) && (op.lda % 8 == 0) && (op.ldb % 8 == 0) && aligned16(op.a) && aligned16(op.b);
+  if (!vec) return run_tiles<128, 128, false, false>(op, epi, s);
+  const int64_t big = (int64_t)((op.M + 255) / 256) * ((op.N + 255) / 256);
+  if (big >= kBigTileMin) return run_tiles<256, 256, false, true>(op, epi, s);
+  return run_tiles<128, 128, false, true>(op, epi, s);
+}
+
+template <class Epi>
+hipError_t run_dual(const Operands& op, const Epi& epi, hipStream_t s) {
+  const bool vec = (op.K % 8 == 0) && (op.lda % 8 == 0) && (op.ldb % 8 == 0) && aligned16(op.a) &&
+                   aligned16(op.b) && aligned16(op.b2);
+  if (!vec) return run_tiles<128, 64, true, false>(op, epi, s);
+  const int64_t big = (int64_t)((op.M + 255) / 256) * ((op.N + 127) / 128);
+  if (big >= kBigTileMin) return run_tiles<256, 128, true, true>(op, epi, s);
+  return run_tiles<128, 64, true, true>(op, epi, s);
+}
+
+}  // namespace
+
+hipError_t launch_qkv(const void* x, const void* w_qkv, void* q_out, void* k_full, void* v_full, int B, int64_t S,
+                      int D, int rank, int d, hipStream_t stream) {
+  const int64_t C = S / (2 * D);
+  const int R = (int)(2 * C);
+  Operands op{static_cast<const bf16_t*>(x), d, static_cast<const bf16_t*>(w_qkv), nullptr, d, B * R, 3 * d, d};
+  EpiQKV epi{static_cast<bf16_t*>(q_out), static_cast<bf16_t*>(k_full), static_cast<bf16_t*>(v_full), d, R, C, rank, D,
+             S};
+  return run_single(op, epi, stream);
+}
+
+hipError_t launch_proj_bf16(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc, int M, int N,
+                            int K, hipStream_t stream) {
+  Operands op{static_cast<const bf16_t*>(a), lda, static_cast<const bf16_t*>(w), nullptr, ldw, M, N, K};
+  EpiBf16 epi{static_cast<bf16_t*>(c), ldc};
+  return run_single(op, epi, stream);
+}
+
+hipError_t launch_gate_up(const void* x, int64_t ldx, const void* w1, const void* w3, int64_t ldw, void* h, int64_t ldh,
+                          int M, int Fs, int K, hipStream_t stream) {
+  Operands op{static_cast<const bf16_t*>(x), ldx, static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w3), ldw,
+              M, Fs, K};
+  EpiSwiGLU epi{static_cast<bf16_t*>(h), ldh};
+  return run_dual(op, epi, stream);
+}
+
+hipError_t launch_down_acc(const void* h, int64_t ldh, const void* w2, int64_t ldw2, float* acc, int64_t ldacc, int M,
+                           int N, int K, int accumulate, hipStream_t stream) {
+  Operands op{static_cast<const bf16_t*>(h), ldh, static_cast<const bf16_t*>(w2), nullptr, ldw2, M, N, K};
+  EpiAcc epi{acc, ldacc, accumulate};
+  return run_single(op, epi, stream);
+}
+
+}  // namespace tsp

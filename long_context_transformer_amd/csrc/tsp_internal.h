@@ -1,0 +1,33 @@
+// tsp_internal.h -- host-side launchers of the gfx950 kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsp {
+
+// QKV projection with the zigzag K/V scatter (step a2).
+//   x [M, d] (M = B * 2C), w_qkv [3d, d]; q_out [M, d] or nullptr;
+//   k_full, v_full [B, S, d]: rows b*S + zigzag_pos(i) receive the rank's K and V.
+hipError_t launch_qkv(const void* x, const void* w_qkv, void* q_out, void* k_full, void* v_full,
+                      int B, int64_t S, int D, int rank, int d, hipStream_t stream);
+
+// Plain projection C[M, N] = A[M, K] W[N, K]^T, bf16 out (step a4, W_O).
+hipError_t launch_proj_bf16(const void* a, int64_t lda, const void* w, int64_t ldw, void* c,
+                            int64_t ldc, int M, int N, int K, hipStream_t stream);
+
+// Gated hidden H[M, Fs] = silu(X W1^T) * (X W3^T), bf16 out (step a5, first half).
+hipError_t launch_gate_up(const void* x, int64_t ldx, const void* w1, const void* w3, int64_t ldw,
+                          void* h, int64_t ldh, int M, int Fs, int K, hipStream_t stream);
+
+// Down projection into the fp32 accumulator: acc[M, N] (=, +=) H[M, K] W2[N, K]^T
+// (step a5, second half).
+hipError_t launch_down_acc(const void* h, int64_t ldh, const void* w2, int64_t ldw2, float* acc,
+                           int64_t ldacc, int M, int N, int K, int accumulate, hipStream_t stream);
+
+// Causal attention of the rank's queries against full-sequence K/V (step a3).
+hipError_t launch_attn(const void* q, const void* k_full, const void* v_full, void* o, float* lse,
+                       int B, int64_t S, int D, int rank, int H, int hd, float scale,
+                       hipStream_t stream);
+
+}  // namespace tsp

@@ -1,0 +1,160 @@
+"""Python binding of libtsp.so (the C ABI in include/tsp.h): argument marshalling only.
+
+Every function takes device tensors (torch, on a ROCm GPU) or raw integer device
+addresses, passes pointers and sizes to the library, and raises TspError on a non-OK
+status. No arithmetic of the layer happens here; every step runs in the library's
+HIP kernels. If libtsp.so is missing the import of this module still works, but the
+first call raises: there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtsp.so")
+
+TSP_OK = 0
+STATUS_NAMES = {0: "TSP_OK", 1: "TSP_ERR_NULL", 2: "TSP_ERR_SHAPE", 3: "TSP_ERR_RANK",
+                4: "TSP_ERR_UNSUPPORTED", 5: "TSP_ERR_WORKSPACE", 6: "TSP_ERR_ALIGN",
+                7: "TSP_ERR_HIP"}
+
+
+class TspError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class LayerDesc(ctypes.Structure):
+    """Mirror of tsp_layer_desc."""
+    _fields_ = [("batch", ctypes.c_int32), ("fold", ctypes.c_int32), ("seq_len", ctypes.c_int64),
+                ("rank", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("w2_ld", ctypes.c_int64), ("scale", ctypes.c_float)]
+
+
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SIGS = {
+    "tsp_version": (_I32, []),
+    "tsp_last_error": (ctypes.c_char_p, []),
+    "tsp_zigzag_index": (_I32, [_I64, _I32, _I32, _VP, _I64]),
+    "tsp_qkv_fwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32, _I32, _VP]),
+    "tsp_attn_fwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32, _I32,
+                            ctypes.c_float, _VP]),
+    "tsp_mlp_workspace_size": (ctypes.c_size_t, [_I64, _I32]),
+    "tsp_mlp_shard_accum": (_I32, [_VP, _VP, _VP, _VP, _I64, _VP, _I64, _I32, _I32, _I32, _VP,
+                                   ctypes.c_size_t, _VP]),
+    "tsp_layer_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc)]),
+    "tsp_layer_fwd": (_I32, [ctypes.POINTER(LayerDesc), _VP, _VP, _VP, ctypes.POINTER(_VP),
+                             ctypes.POINTER(_VP), ctypes.POINTER(_VP), _VP, _VP, _VP, _VP, _VP,
+                             ctypes.c_size_t, _VP]),
+}
+
+_lib = None
+
+
+def load(path=None):
+    """Load libtsp.so (once). Raises OSError if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise OSError(f"{p} not found: build it with `python -m long_context_transformer_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(code):
+    if code != TSP_OK:
+        raise TspError(code, load().tsp_last_error().decode())
+
+
+def _ptr(t):
+    """Device address of a tensor (must live on a GPU) or pass through an int / None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not getattr(t, "is_cuda", False):
+        raise TypeError("expected a GPU tensor (or a raw device address)")
+    if not t.is_contiguous():
+        raise TypeError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    for t in tensors:
+        if getattr(t, "is_cuda", False):
+            import torch
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def version():
+    return load().tsp_version()
+
+
+def zigzag_index(S, D, rank):
+    """Global positions of a rank's local rows (host computation, int64 numpy)."""
+    out = np.empty(S // D if D > 0 else 0, dtype=np.int64)
+    _check(load().tsp_zigzag_index(S, D, rank, out.ctypes.data if out.size else None, out.size))
+    return out
+
+
+def qkv_fwd(x, w_qkv, q_out, k_full, v_full, B, S, D, rank, n_heads, head_dim, stream=None):
+    _check(load().tsp_qkv_fwd(_ptr(x), _ptr(w_qkv), _ptr(q_out), _ptr(k_full), _ptr(v_full), B, S, D,
+                              rank, n_heads, head_dim, _stream(stream, x)))
+
+
+def attn_fwd(q, k_full, v_full, o, lse, B, S, D, rank, n_heads, head_dim, scale=0.0, stream=None):
+    _check(load().tsp_attn_fwd(_ptr(q), _ptr(k_full), _ptr(v_full), _ptr(o), _ptr(lse), B, S, D, rank,
+                               n_heads, head_dim, scale, _stream(stream, q)))
+
+
+def mlp_workspace_size(M, Fs):
+    return int(load().tsp_mlp_workspace_size(M, Fs))
+
+
+def mlp_shard_accum(x, w1_j, w3_j, w2_j, ld_w2, acc, M, d, Fs, accumulate, ws, ws_bytes=None,
+                    stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load().tsp_mlp_shard_accum(_ptr(x), _ptr(w1_j), _ptr(w3_j), _ptr(w2_j), ld_w2, _ptr(acc), M,
+                                      d, Fs, 1 if accumulate else 0, _ptr(ws), ws_bytes,
+                                      _stream(stream, x)))
+
+
+def make_desc(B, S, D, rank, d_model, n_heads, head_dim, ffn, w2_ld=0, scale=0.0):
+    return LayerDesc(B, D, S, rank, d_model, n_heads, head_dim, ffn, 0, w2_ld, scale)
+
+
+def layer_workspace_size(desc):
+    return int(load().tsp_layer_workspace_size(ctypes.byref(desc)))
+
+
+def layer_fwd(desc, x_shard, w_qkv, w_o, w1, w3, w2, k_full, v_full, attn_out, mlp_out, ws,
+              ws_bytes=None, stream=None):
+    """w1, w3, w2: sequences of D shard tensors (or addresses), indexed by shard id."""
+    D = desc.fold
+    arr = _VP * D
+    a1 = arr(*[_ptr(t) for t in w1])
+    a3 = arr(*[_ptr(t) for t in w3])
+    a2 = arr(*[_ptr(t) for t in w2])
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load().tsp_layer_fwd(ctypes.byref(desc), _ptr(x_shard), _ptr(w_qkv), _ptr(w_o), a1, a3, a2,
+                                _ptr(k_full), _ptr(v_full), _ptr(attn_out), _ptr(mlp_out), _ptr(ws),
+                                ws_bytes, _stream(stream, x_shard)))

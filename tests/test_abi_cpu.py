@@ -1,0 +1,147 @@
+"""CPU checks of the C ABI: every declared symbol is exported, the host-only zigzag map is
+bit-exact against the oracle, and invalid arguments return the documented status before
+any HIP call. No test here launches a kernel: every compute entry point is called with
+arguments its host-side checks reject."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from long_context_transformer_amd import tsp
+from oracle import tsp_oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tsp.LIB_PATH),
+                                reason="libtsp.so not built (python -m long_context_transformer_amd.build)")
+
+# Fake device addresses: 16-byte aligned, never dereferenced (every call below fails a
+# host check first).
+A = 0x7F0000000000
+MIS = A + 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_contract_entry_points():
+    names = declared_functions()
+    for required in ("tsp_zigzag_index", "tsp_attn_fwd", "tsp_mlp_shard_accum", "tsp_layer_fwd"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tsp.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_clean_error():
+    assert tsp.version() >> 16 == 1
+    tsp.zigzag_index(64, 2, 1)
+    assert tsp.load().tsp_last_error() == b""
+
+
+@pytest.mark.parametrize("S,D", [(256, 4), (16384, 8), (131072, 8), (48, 3), (64, 1), (40, 5)])
+def test_zigzag_bit_exact_vs_oracle(S, D):
+    for r in range(D):
+        np.testing.assert_array_equal(tsp.zigzag_index(S, D, r), tsp_oracle.zigzag_index(S, D, r))
+
+
+def _code(fn, *args):
+    with pytest.raises(tsp.TspError) as e:
+        fn(*args)
+    return e.value.code
+
+
+def test_zigzag_errors():
+    lib = tsp.load()
+    buf = np.zeros(64, dtype=np.int64)
+    assert lib.tsp_zigzag_index(256, 4, 0, None, 64) == 1
+    assert lib.tsp_zigzag_index(250, 4, 0, buf.ctypes.data, 64) == 2
+    assert lib.tsp_zigzag_index(256, 4, 4, buf.ctypes.data, 64) == 3
+    assert lib.tsp_zigzag_index(256, 4, -1, buf.ctypes.data, 64) == 3
+    assert lib.tsp_zigzag_index(256, 4, 0, buf.ctypes.data, 63) == 2
+    assert lib.tsp_zigzag_index(256, 0, 0, buf.ctypes.data, 64) == 2
+    assert b"rank" in lib.tsp_last_error() or b"idx_len" in lib.tsp_last_error() or lib.tsp_last_error()
+
+
+def test_attn_errors():
+    f = tsp.attn_fwd
+    assert _code(f, None, A, A, A, None, 1, 256, 4, 0, 4, 64, 0.0, 0) == 1
+    assert _code(f, A, A, A, A, None, 1, 250, 4, 0, 4, 64, 0.0, 0) == 2
+    assert _code(f, A, A, A, A, None, 0, 256, 4, 0, 4, 64, 0.0, 0) == 2
+    assert _code(f, A, A, A, A, None, 1, 256, 4, 5, 4, 64, 0.0, 0) == 3
+    assert _code(f, A, A, A, A, None, 1, 256, 4, 0, 4, 96, 0.0, 0) == 4
+    assert _code(f, A, MIS, A, A, None, 1, 256, 4, 0, 4, 64, 0.0, 0) == 6
+    assert _code(f, A, A, A, A, A + 2, 1, 256, 4, 0, 4, 64, 0.0, 0) == 6
+    assert _code(f, A, A, A, A, None, 1, 256, 4, 0, 4, 64, float("nan"), 0) == 2
+
+
+def test_qkv_errors():
+    f = tsp.qkv_fwd
+    assert _code(f, A, None, None, A, A, 1, 256, 4, 0, 4, 64, 0) == 1
+    assert _code(f, A, A, None, A, A, 1, 256, 3, 0, 4, 64, 0) == 2
+    assert _code(f, A, A, None, A, A, 1, 256, 4, 0, 4, 32, 0) == 4
+    assert _code(f, A, A, MIS, A, A, 1, 256, 4, 0, 4, 64, 0) == 6
+
+
+def test_mlp_errors():
+    f = tsp.mlp_shard_accum
+    need = tsp.mlp_workspace_size(64, 172)
+    assert need >= 64 * 176 * 2
+    assert _code(f, A, A, A, None, 172, A, 64, 256, 172, 0, A, need, 0) == 1
+    assert _code(f, A, A, A, A, 171, A, 64, 256, 172, 0, A, need, 0) == 2
+    assert _code(f, A, A, A, A, 172, A, 0, 256, 172, 0, A, need, 0) == 2
+    assert _code(f, A, A, A, A, 172, MIS, 64, 256, 172, 0, A, need, 0) == 6
+    assert _code(f, A, A, A, A, 172, A, 64, 256, 172, 0, A, need - 1, 0) == 5
+    assert tsp.mlp_workspace_size(0, 172) == 0
+
+
+def _desc(**kw):
+    base = dict(B=1, S=256, D=4, rank=0, d_model=256, n_heads=4, head_dim=64, ffn=688)
+    base.update(kw)
+    return tsp.make_desc(**base)
+
+
+def test_layer_desc_and_workspace():
+    assert ctypes.sizeof(tsp.LayerDesc) == 56
+    good = _desc()
+    M = 64
+    ws = tsp.layer_workspace_size(good)
+    assert ws >= 2 * M * 256 * 2 + M * 176 * 2
+    assert tsp.layer_workspace_size(_desc(ffn=690)) == 0      # F % D != 0
+    assert tsp.layer_workspace_size(_desc(d_model=250)) == 0  # d != H*hd
+    assert tsp.layer_workspace_size(_desc(head_dim=80, d_model=320)) == 0
+    assert tsp.layer_workspace_size(_desc(rank=4)) == 0
+
+
+def test_layer_errors():
+    good = _desc()
+    ws = tsp.layer_workspace_size(good)
+    sh = [A] * 4
+    f = tsp.layer_fwd
+    assert _code(f, _desc(S=100), A, A, A, sh, sh, sh, A, A, A, A, A, ws, 0) == 2
+    assert _code(f, _desc(rank=7), A, A, A, sh, sh, sh, A, A, A, A, A, ws, 0) == 3
+    assert _code(f, good, None, A, A, sh, sh, sh, A, A, A, A, A, ws, 0) == 1
+    assert _code(f, good, A, A, A, [A, A, None, A], sh, sh, A, A, A, A, A, ws, 0) == 1
+    assert _code(f, good, A, A, A, sh, [A, MIS, A, A], sh, A, A, A, A, A, ws, 0) == 6
+    assert _code(f, good, A, A, A, sh, sh, sh, A, A, A, A, A, ws - 16, 0) == 5
+    assert _code(f, _desc(w2_ld=100), A, A, A, sh, sh, sh, A, A, A, A, A, ws, 0) == 2
+    bad = _desc()
+    bad.reserved = 1
+    assert _code(f, bad, A, A, A, sh, sh, sh, A, A, A, A, A, ws, 0) == 2
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        tsp.attn_fwd(x, x, x, x, None, 1, 256, 4, 0, 4, 64)
