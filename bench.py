@@ -1,0 +1,254 @@
+"""Benchmark of one TSP rank's layer forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rank R]
+                [--no-cpu-baseline] [--sweep PATH]
+
+A step is one tsp_layer_fwd call: QKV projection of the rank's zigzag shard, causal
+attention against the full-sequence K/V, W_O, and the D-shard SwiGLU ring accumulated in
+fp32 (TSP summary "Folding Tensor and Sequence Parallelism ...", §2). Inputs are seeded
+synthetic tensors already resident in HBM; the peers' K/V rows (what the all-gather
+delivers) are filled before timing by the peers' own QKV projections.
+
+Prints ONE JSON line: whole-step throughput in TFLOP/s of algorithmic work (exact
+causal pairs), the attention kernel's roofline (its own launches timed with HIP events
+on the stream it runs on), and the CPU oracle timed on a bounded sample of the same
+workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+METRIC = "TSP rank-shard layer fwd TFLOP/s (% bf16 MFMA peak), 7B layer, S=16K-128K"
+DEFAULT_WORKLOAD = "7b_s128k_d8"
+
+
+def layer_flops(B, S, D, d, H, hd, F):
+    """Algorithmic FLOPs of one rank's layer: QKV + causal attention (C(S+1) exact pairs
+    per sequence and head, 2 matmuls) + W_O + SwiGLU over all D shards."""
+    C = S // (2 * D)
+    M = B * 2 * C
+    attn = 4 * B * H * hd * C * (S + 1)
+    return 2 * M * d * 3 * d + attn + 2 * M * d * d + 6 * M * d * F, attn
+
+
+def setup(w, rank):
+    import torch
+    from long_context_transformer_amd import synth, tsp
+    t0 = time.time()
+    inp = synth.layer_inputs(w)
+    dev = {k: synth.to_torch(v).cuda() for k, v in inp.items()}
+    B, S, D, H, hd, d, F = w.B, w.S, w.D, w.n_heads, w.head_dim, w.d_model, w.ffn
+    Fs = F // D
+    kf = torch.empty((B, S, d), dtype=torch.bfloat16, device="cuda")
+    vf = torch.empty_like(kf)
+    for peer in range(D):
+        if peer != rank:
+            idx = torch.from_numpy(tsp.zigzag_index(S, D, peer)).cuda()
+            tsp.qkv_fwd(dev["x_full"].index_select(1, idx).contiguous(), dev["w_qkv"], None, kf, vf,
+                        B, S, D, peer, H, hd)
+    idx = torch.from_numpy(tsp.zigzag_index(S, D, rank)).cuda()
+    xs = dev["x_full"].index_select(1, idx).contiguous()
+    st = {
+        "inputs": inp, "dev": dev, "kf": kf, "vf": vf, "xs": xs,
+        "w1": [dev["w1"][j * Fs:(j + 1) * Fs] for j in range(D)],
+        "w3": [dev["w3"][j * Fs:(j + 1) * Fs] for j in range(D)],
+        "w2": [dev["w2"][:, j * Fs:(j + 1) * Fs].contiguous() for j in range(D)],
+        "desc": tsp.make_desc(B, S, D, rank, d, H, hd, F),
+        "attn_out": torch.empty((B, S // D, d), dtype=torch.bfloat16, device="cuda"),
+        "mlp_out": torch.empty((B, S // D, d), dtype=torch.float32, device="cuda"),
+        "q": torch.empty((B, S // D, d), dtype=torch.bfloat16, device="cuda"),
+        "o": torch.empty((B, S // D, d), dtype=torch.bfloat16, device="cuda"),
+    }
+    st["ws"] = torch.empty(tsp.layer_workspace_size(st["desc"]), dtype=torch.uint8, device="cuda")
+    # Q of the rank for the attention-only timing
+    tsp.qkv_fwd(xs, dev["w_qkv"], st["q"], kf, vf, B, S, D, rank, H, hd)
+    torch.cuda.synchronize()
+    st["setup_s"] = time.time() - t0
+    return st
+
+
+def step(st):
+    from long_context_transformer_amd import tsp
+    tsp.layer_fwd(st["desc"], st["xs"], st["dev"]["w_qkv"], st["dev"]["w_o"], st["w1"], st["w3"],
+                  st["w2"], st["kf"], st["vf"], st["attn_out"], st["mlp_out"], st["ws"])
+
+
+def time_layer(st, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step(st)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step(st)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return ev0.elapsed_time(ev1) / steps, wall
+
+
+def time_attention(st, w, rank, launches):
+    """Average duration of the attention kernel alone, HIP events on its own stream."""
+    import torch
+    from long_context_transformer_amd import tsp
+    args = (st["q"], st["kf"], st["vf"], st["o"], None, w.B, w.S, w.D, rank, w.n_heads, w.head_dim)
+    tsp.attn_fwd(*args)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(launches):
+        tsp.attn_fwd(*args)
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / launches
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return int(info[0]["num_threads"]), info[0].get("internal_api", "blas")
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0)), "unknown"
+
+
+def cpu_baseline(w, inputs, rank, rows_sample):
+    """The fp64 oracle on a bounded sample of the same workload: the last `rows_sample`
+    local rows of the rank's early chunk, with the K/V projection of every position
+    those rows see. Returns TFLOP/s of the algorithmic work of that sample."""
+    import numpy as np
+    from long_context_transformer_amd import synth
+    from oracle import tsp_oracle as O
+    C = w.C
+    rows = np.arange(C - rows_sample, C)
+    idx = O.zigzag_index(w.S, w.D, rank)
+    kmax = int(idx[rows].max()) + 1
+    b_sel = slice(0, 1)
+    f64 = {k: synth.to_f64(v) for k, v in inputs.items() if k != "x_full"}
+    x = synth.to_f64(inputs["x_full"][b_sel, :kmax])
+    d, H, hd, F = w.d_model, w.n_heads, w.head_dim, w.ffn
+    t0 = time.perf_counter()
+    # The prefix [0, kmax) as a one-rank sequence: its local rows are positions, so the
+    # sampled positions are evaluated with keys 0..position, exactly as in the full layer.
+    O.rank_layer(x, f64["w_qkv"], f64["w_o"], f64["w1"], f64["w3"], f64["w2"], kmax, 1, 0, H,
+                 rows=idx[rows])
+    dt = time.perf_counter() - t0
+    pairs = int((idx[rows] + 1).sum())
+    R = len(rows)
+    flops = (2 * 2 * kmax * d * d + 2 * R * d * d + 4 * H * hd * pairs + 2 * R * d * d
+             + 6 * R * d * F)
+    threads, api = blas_threads()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{w.name} rank {rank}, batch 0: local rows {C - R}..{C - 1} (positions "
+                       f"{int(idx[rows].min())}..{int(idx[rows].max())}) through QKV, causal "
+                       f"attention, W_O and SwiGLU, plus K/V projections of positions 0..{kmax - 1}; "
+                       f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64 numpy ({api})"),
+            "wall_s": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--attn-launches", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--sweep", default=None, help="also time every workload (and every rank of the "
+                    "S=32K one) and write one JSON line each to this file")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one rank's share on ONE GPU; runs on more than one GPU are not "
+              "part of this build (see the sharding design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_transformer_amd import synth, tsp
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tsp.load()
+
+    w = synth.WORKLOADS[args.workload].with_rank(args.rank)
+    st = setup(w, args.rank)
+    print(f"# setup {st['setup_s']:.1f}s", file=sys.stderr, flush=True)
+    ms, wall = time_layer(st, args.steps, args.warmup)
+    flops, attn_flops = layer_flops(w.B, w.S, w.D, w.d_model, w.n_heads, w.head_dim, w.ffn)
+    tflops = flops / (ms * 1e-3) / 1e12
+    attn_ms = time_attention(st, w, args.rank, args.attn_launches)
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    print(f"# layer {ms:.3f} ms  {tflops:.1f} TFLOP/s  attention {attn_ms:.3f} ms "
+          f"{attn_tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, st["inputs"], args.rank, args.cpu_rows)
+        print(f"# cpu baseline {cpu['value']:.4f} TFLOP/s in {cpu['wall_s']} s", file=sys.stderr,
+              flush=True)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, bf16)",
+        "config": {"workload": w.name, "batch": w.B, "seq_len": w.S, "fold": w.D, "rank": args.rank,
+                   "d_model": w.d_model, "n_heads": w.n_heads, "head_dim": w.head_dim,
+                   "ffn": w.ffn, "flops_per_step": flops},
+        "roofline": {"kernel": "attention (attn_fwd<128>)", "bound": "mfma",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(attn_ms, 4),
+                     "flops_per_launch": attn_flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+    if args.sweep:
+        with open(args.sweep, "w") as f:
+            for name, base in synth.WORKLOADS.items():
+                ranks = range(base.D) if name == "7b_s32k_d8" else [0]
+                for r in ranks:
+                    ww = base.with_rank(r)
+                    s2 = setup(ww, r)
+                    ms2, _ = time_layer(s2, 10 if ww.S >= 65536 else 20, 3)
+                    fl, afl = layer_flops(ww.B, ww.S, ww.D, ww.d_model, ww.n_heads, ww.head_dim, ww.ffn)
+                    ams = time_attention(s2, ww, r, 5)
+                    line = {"workload": name, "rank": r, "ms": round(ms2, 4),
+                            "tflops": round(fl / ms2 / 1e9, 2),
+                            "pct_peak": round(100 * fl / ms2 / 1e9 / PEAK_BF16_TFLOPS, 2),
+                            "attn_ms": round(ams, 4), "attn_tflops": round(afl / ams / 1e9, 2)}
+                    f.write(json.dumps(line) + "\n")
+                    f.flush()
+                    print("# sweep " + json.dumps(line), file=sys.stderr, flush=True)
+                    del s2
+                    torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()
