@@ -18,6 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtsp.so")
 SOURCES = ["tsp_api.hip", "tsp_gemm.hip", "tsp_attn.hip"]
+# Per-source code generation flags. The attention kernel keeps its O accumulator and
+# scores in VGPRs (MFMA "VGPR form"); the rescale of O then stays a plain VALU multiply
+# instead of AGPR<->VGPR copies on every key block.
+SOURCE_FLAGS = {"tsp_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -58,7 +62,8 @@ def build(verbose=False, resource_usage=False):
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        out = _run([hipcc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        flags = [*HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra]
+        out = _run([hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         return obj, out
 
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:

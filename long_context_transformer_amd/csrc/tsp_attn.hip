@@ -6,28 +6,43 @@
 // (chunk r with its mirror 2D-1-r) balances the causal work between ranks. This kernel
 // is that step for one rank: online softmax in fp32, S x S never materialised.
 //
-// Work decomposition. One workgroup (4 waves) owns 128 consecutive local query rows of
-// one (sequence, head); each wave owns 32 of them. Local rows ascend in position, so a
-// tile's last row bounds its keys: the tile streams keys [0, pos(last)+1) in stages of
-// 64 and never reads a key row after the rank's last position. Stages at or before the
-// tile's first position need no mask (only the last two or three are masked per
-// element). Within one (sequence, head) the heaviest tile is dispatched first, and each
-// XCD takes a contiguous range of (sequence, head) work so the query tiles running
-// together on it stream the same K/V through its L2.
+// Work decomposition. One workgroup (4 waves, one per SIMD) owns 256 consecutive local
+// query rows of one (sequence, head); each wave owns 64 of them as two 32-row blocks.
+// Local rows ascend in position, so a tile's last row bounds its keys: the workgroup
+// streams keys [0, pos(last)+1) in stages of 64 and never reads a key row after the
+// rank's last position (the final stage repeats that row instead; those keys are masked).
+// Within one (sequence, head) the heaviest tile is dispatched first, and each XCD takes a
+// contiguous range of (sequence, head) work so the tiles running together on it stream
+// the same K/V through its L2.
 //
-// MFMA formulation (v_mfma_f32_32x32x16_bf16, see tsp_device.h for the lane layout):
-//   S^T = K Q^T   A = K rows from LDS, B = this wave's Q (registers). Each lane ends up
-//                 holding 16 of the 32 keys of one 32-key block for ITS query
-//                 (column lane%32); the other 16 sit in lane^32. Row max / row sum
-//                 therefore need one exchange with lane^32 per stage.
-//   O^T += V^T P^T  B = P straight from the S^T registers (converted to bf16); A = V^T
-//                 read from LDS with the same key labelling. O^T keeps each lane on its
-//                 own query, so the online-softmax rescale is a per-lane scalar.
-// V is stored transposed in LDS ([dim][key], padded) so a lane's A fragment is two
-// 8-byte reads; K is stored [key][dim] padded by 16 bytes so 16-byte fragment reads of
-// consecutive keys fall in distinct banks. Both are double buffered: the global loads
-// of stage t+1 are in flight while stage t computes.
-// The softmax runs in base 2: s2 = s * scale * log2(e), p = exp2(s2 - m2).
+// Data movement. K and V stages go straight from global memory into LDS with 16-byte
+// global_load_lds (no register staging), into a 4-deep ring of separate LDS buffers, two
+// stages ahead of use; one barrier per stage. Rows are stored unpadded and XOR-swizzled
+// in 16-byte chunks so the MFMA fragment reads are free of bank conflicts:
+//   K: chunk c of row r lives at c ^ fk(r); 16 lanes read 16 rows at one chunk.
+//   V: chunk c of row r lives at c ^ fv(r); V^T fragments come from ds_read_b64_tr_b16,
+//      whose 16-lane groups each read a 4 key x 16 dim block and hand lane i the four
+//      keys of dim i.
+// The ring buffers are distinct LDS objects and the stage loop is unrolled by the ring
+// depth, so every LDS access names its buffer statically and the compiler does not
+// serialise fragment reads behind the loads still in flight for other stages.
+//
+// MFMA formulation (v_mfma_f32_32x32x16_bf16, lane layout in tsp_device.h):
+//   S^T = K Q^T     A = K rows (LDS), B = this wave's Q (registers). A lane holds 16 of the
+//                   32 keys of a 32-key block for ITS query (column lane%32); the other 16
+//                   sit in lane^32, so the row max needs one exchange per block.
+//   O^T += V^T P^T  B = P straight from the S^T registers (bf16); A = V^T via transpose
+//                   reads with the same key labelling. O^T keeps each lane on its own
+//                   query, so the online-softmax rescale is a per-lane scalar.
+// Each K and V fragment feeds both 32-row query blocks.
+//
+// Pipeline inside a wave, per 32-key block j: the S MFMAs of block j+1 are issued in the
+// same straight-line region as the softmax of block j (the matrix cores work while the
+// VALU computes exponentials), then the rare O rescale, then the PV MFMAs of block j.
+// Softmax in base 2 with the scale folded into one FMA: p = exp2(s*c - m), c =
+// scale*log2(e), m a running max of s*c. O is rescaled only when the running max grows by
+// more than 8 (p <= 2^8 stays exact in fp32 and bf16); the row sum adds the bf16-rounded
+// p with v_dot2, so numerator and denominator use the same p.
 #include <math.h>
 
 #include "tsp_device.h"
@@ -36,9 +51,16 @@
 namespace tsp {
 namespace {
 
-constexpr int BR = 128;  // query rows per workgroup
-constexpr int BC = 64;   // keys per stage
+constexpr int QB = 2;             // 32-row query blocks per wave
+constexpr int BR = 4 * 32 * QB;   // query rows per workgroup (4 waves)
+constexpr int BC = 64;            // keys per stage (two 32-key softmax blocks)
 constexpr int kThreads = 256;
+constexpr float kLazy = 8.0f;     // rescale O only when the max grows by more than this (log2)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct AttnArgs {
   const bf16_t* q;
@@ -55,29 +77,42 @@ struct AttnArgs {
   float scale_log2;
 };
 
-// Element e (0..7) of x0 in the low half and of x1 in the high half of a word.
-__device__ __forceinline__ uint32_t pair_elem(const uint4& x0, const uint4& x1, int e) {
-  const uint32_t w0 = e < 2 ? x0.x : e < 4 ? x0.y : e < 6 ? x0.z : x0.w;
-  const uint32_t w1 = e < 2 ? x1.x : e < 4 ? x1.y : e < 6 ? x1.z : x1.w;
-  return (e & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
+template <int HD>
+struct Lay {
+  static constexpr int KS = HD / 16;            // 16-dim reduction steps of Q K^T
+  static constexpr int DB = HD / 32;            // 32-dim output blocks
+  static constexpr int ROWB = HD * 2;           // bytes per key row
+  static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+  static constexpr int TILEB = BC * ROWB;       // bytes of one K (or V) tile
+  static constexpr int NDMA = TILEB / (kThreads * 16);  // 16-byte loads per thread per tile
+  // K fragment reads touch 16 consecutive rows at one chunk; V transpose reads touch 4
+  // consecutive rows (aligned to 4) x 4 chunks. Both swizzles spread those over all banks.
+  __device__ static int fk(int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int fv(int r) { return HD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
+
+// 16-byte global -> LDS load (global_load_lds_dwordx4): lane i's bytes land at
+// lds + 16 * i; `lds` must be the same for the whole wave.
+__device__ __forceinline__ void load_lds16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
 
+// s_waitcnt immediate: wait until at most `vm` vector-memory loads of this wave are in
+// flight; the export and LDS counters are left unconstrained.
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 template <int HD>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd(AttnArgs a) {
-  constexpr int KS = HD / 16;       // 16-dim reduction steps of Q K^T
-  constexpr int DB = HD / 32;       // 32-dim output blocks
-  constexpr int KSTR = HD + 8;      // padded K row (elements)
-  constexpr int VSTR = BC + 4;      // padded V^T row (elements)
-  constexpr int VCH = HD / 8;       // 16-byte chunks per key row
-  constexpr int KCH = BC * VCH / kThreads;  // K chunks per thread per stage
-  constexpr int KPT = HD / 32;      // keys per thread in the V^T fill (4 or 2)
-  static_assert(KPT * (kThreads / VCH) == BC, "V^T fill must cover the stage");
-  static_assert(KPT == 2 || KPT == 4, "head_dim 64 or 128");
-  __shared__ __attribute__((aligned(16))) bf16_t ks[2][BC * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[2][HD * VSTR];
+__global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
+  using L = Lay<HD>;
+  constexpr int KS = L::KS, DB = L::DB, ROWB = L::ROWB, CPR = L::CPR, TILEB = L::TILEB, NDMA = L::NDMA;
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds2[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char lds3[2 * TILEB];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
 
   const int item = xcd_remap(blockIdx.x, a.items);
@@ -85,153 +120,250 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int qt = a.n_qt - 1 - (item - bh * a.n_qt);  // heaviest tile of the (b, h) first
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
   const int row0 = qt * BR;
-  const int last_row = min(row0 + BR, a.rows) - 1;
-  const int64_t pmin = zigzag_pos(row0, a.C, a.rank, a.D);
-  const int64_t kv_end = zigzag_pos(last_row, a.C, a.rank, a.D) + 1;
-  const int n_kt = (int)((kv_end + BC - 1) / BC);
-  const int n_full = (int)((pmin + 1) / BC);
+  const int kv_end = (int)zigzag_pos(min(row0 + BR, a.rows) - 1, a.C, a.rank, a.D) + 1;
+  const int n_kt = (kv_end + BC - 1) / BC;
 
-  const int qi = row0 + wave * 32 + l32;
-  const bool qvalid = qi < a.rows;
-  const int qic = qvalid ? qi : a.rows - 1;
-  const int64_t qpos = zigzag_pos(qic, a.C, a.rank, a.D);
+  const int wrow0 = row0 + wave * (32 * QB);
+  const int wmin_pos = wrow0 < a.rows ? (int)zigzag_pos(wrow0, a.C, a.rank, a.D) : 0;
   const int64_t tok = (int64_t)a.H * HD;  // elements between consecutive tokens
 
-  bf16x8 qf[KS];
-  {
+  // This lane's two query rows and their Q fragments (dims 16s + 8hl .. +7).
+  int qi[QB], qpos[QB];
+  bf16x8 qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    qi[qb] = wrow0 + 32 * qb + l32;
+    const bool valid = qi[qb] < a.rows;
+    const int qic = valid ? qi[qb] : a.rows - 1;
+    qpos[qb] = (int)zigzag_pos(qic, a.C, a.rank, a.D);
     const bf16_t* qp = a.q + ((int64_t)b * a.rows + qic) * tok + (int64_t)h * HD + 8 * hl;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qf[s] = qvalid ? as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s)) : bf16x8{};
+      qf[qb][s] = valid ? as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s)) : bf16x8{};
   }
 
-  const bf16_t* kbase = a.k + (int64_t)b * a.S * tok + (int64_t)h * HD;
-  const bf16_t* vbase = a.v + (int64_t)b * a.S * tok + (int64_t)h * HD;
-
-  uint4 rk[KCH];
-  uint4 rv[KPT];
-  const int vg = tid / VCH, vdc = tid % VCH;
-  auto gload = [&](int t) {
-    const int64_t key0 = (int64_t)t * BC;
+  // ---- stage loads: global -> LDS, 16 bytes per lane, lane-linear within the 1 KB a wave
+  // instruction writes. Load p of this wave covers linear chunks (4p + wave) * 64 + lane.
+  const char* kseq = reinterpret_cast<const char*>(a.k + (int64_t)b * a.S * tok + (int64_t)h * HD);
+  const char* vseq = reinterpret_cast<const char*>(a.v + (int64_t)b * a.S * tok + (int64_t)h * HD);
+  int drow[NDMA], dck[NDMA], dcv[NDMA];
 #pragma unroll
-    for (int p = 0; p < KCH; ++p) {
-      const int c = tid + kThreads * p;
-      const int64_t kg = key0 + c / VCH;
-      rk[p] = kg < kv_end ? *reinterpret_cast<const uint4*>(kbase + kg * tok + 8 * (c % VCH)) : make_uint4(0u, 0u, 0u, 0u);
-    }
+  for (int p = 0; p < NDMA; ++p) {
+    const int lin = (4 * p + wave) * 64 + lane;
+    drow[p] = lin / CPR;
+    const int pc = lin % CPR;
+    dck[p] = 16 * (pc ^ L::fk(drow[p]));
+    dcv[p] = 16 * (pc ^ L::fv(drow[p]));
+  }
+  const uint32_t tokb = (uint32_t)(tok * 2);
+  auto issue = [&] __device__(char* stage, int t) {
+    const int key0 = t * BC;
+    const int lim = kv_end - 1 - key0;  // rows past the tile's last key repeat it (masked)
+    const char* kb = kseq + (int64_t)key0 * tok * 2;
+    const char* vb = vseq + (int64_t)key0 * tok * 2;
 #pragma unroll
-    for (int kk = 0; kk < KPT; ++kk) {
-      const int64_t kg = key0 + vg * KPT + kk;
-      rv[kk] = kg < kv_end ? *reinterpret_cast<const uint4*>(vbase + kg * tok + 8 * vdc) : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < KCH; ++p) {
-      const int c = tid + kThreads * p;
-      *reinterpret_cast<uint4*>(&ks[buf][(c / VCH) * KSTR + 8 * (c % VCH)]) = rk[p];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16_t* dst = &vt[buf][(8 * vdc + e) * VSTR + vg * KPT];
-      if constexpr (KPT == 4) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pair_elem(rv[0], rv[1], e), pair_elem(rv[2], rv[3], e));
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = pair_elem(rv[0], rv[1], e);
-      }
+    for (int p = 0; p < NDMA; ++p) {
+      const uint32_t roff = (uint32_t)min(drow[p], lim) * tokb;
+      load_lds16(kb + roff + dck[p], stage + (4 * p + wave) * 1024);
+      load_lds16(vb + roff + dcv[p], stage + TILEB + (4 * p + wave) * 1024);
     }
   };
-
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int t = 0; t < n_kt; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < n_kt) gload(t + 1);
-
-    f32x16 sacc[BC / 32];
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb) {
-      sacc[kb] = f32x16{};
-      const bf16_t* kr = &ks[cur][(kb * 32 + l32) * KSTR + 8 * hl];
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        sacc[kb] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(kr + 16 * s)), qf[s], sacc[kb]);
+  // Wait until at most `stages` later stages of this wave's loads are in flight, then a
+  // bare barrier: every wave's earlier stage loads have landed in LDS.
+  auto sync_stage = [&] __device__(int stages) {
+    if (stages >= 2) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * NDMA));
+    } else if (stages == 1) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NDMA));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
+    __builtin_amdgcn_s_barrier();
+  };
 
-    float mx = m_run;
-    const bool masked = t >= n_full;
+  // ---- fragment addresses (bytes within a stage; block, half and part add constants)
+  int kaddr[KS];
 #pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb) {
+  for (int s = 0; s < KS; ++s) kaddr[s] = l32 * ROWB + 16 * ((2 * s + hl) ^ L::fk(l32));
+  const int G = lane >> 4, j16 = lane & 15;
+  int vaddr[DB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float sv = sacc[kb][r] * a.scale_log2;
-        if (masked) {
-          const int64_t key = (int64_t)t * BC + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key > qpos) sv = -INFINITY;
-        }
-        sacc[kb][r] = sv;
-        mx = fmaxf(mx, sv);
-      }
+  for (int db = 0; db < DB; ++db) {
+    const int r = 4 * hl + (j16 >> 2);  // row within an aligned group of 8 keys
+    const int c = 4 * db + 2 * (G & 1) + ((j16 & 3) >> 1);
+    vaddr[db] = TILEB + r * ROWB + 16 * (c ^ L::fv(r)) + 8 * (j16 & 1);
+  }
+
+  f32x16 oacc[QB][DB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
+  float m_s[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_s[qb] = -INFINITY;
+    l_run[qb] = 0.0f;
+  }
+  const float c2 = a.scale_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // S^T of 32-key block kb (0/1) of a stage, both query blocks.
+  auto qk = [&] __device__(const char* stage, int kb, f32x16 (&sacc)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) sacc[qb] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(stage + kaddr[s] + kb * 32 * ROWB));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb] = mfma32x32x16(kf, qf[qb][s], sacc[qb]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
-    m_run = mx;
-
-    float lsum = 0.0f;
-    bf16x8 pf[BC / 16];
+  };
+  auto mask = [&] __device__(f32x16 (&sacc)[QB], int kstart) {
 #pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb) {
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kstart + 8 * (r >> 2) + 4 * hl + (r & 3) > qpos[qb]) sacc[qb][r] = -INFINITY;
+  };
+  // Row max, reference max, exponentials, bf16 P and their sum. Returns whether this lane
+  // needs the O rescale (then by the factors in alpha).
+  auto softmax = [&] __device__(f32x16 (&sacc)[QB], bf16x8 (&pf)[QB][2], float (&alpha)[QB]) {
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = sacc[qb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[qb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxs = mx * c2;
+      const bool upd = mxs > m_s[qb] + kLazy;
+      const float m_new = upd ? mxs : m_s[qb];
+      alpha[qb] = __builtin_amdgcn_exp2f(m_s[qb] - m_new);
+      any |= upd;
+      m_s[qb] = m_new;
+      const float nm = -m_new;
+      float lsum = 0.0f;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
+        uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sacc[kb][8 * half + e] - mx);
-          lsum += p;
-          pf[2 * kb + half][e] = (__bf16)p;
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][8 * half + 2 * e], c2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][8 * half + 2 * e + 1], c2, nm));
+          w[e] = pack_bf16x2(p0, p1);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, lsum, false);
         }
+        pf[qb][half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
       }
+      l_run[qb] = __builtin_fmaf(l_run[qb], alpha[qb], lsum);
     }
-    l_run = l_run * alpha + lsum;
+    return any;
+  };
+  // Ends a straight-line region [S MFMAs of the next block + softmax of this one]: asks the
+  // scheduler to alternate one MFMA with a run of VALU work, then pins P and the row sums
+  // in registers so the exponentials cannot sink below the rescale branch.
+  auto close_region = [&] __device__(const bf16x8 (&pf)[QB][2]) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-
+    for (int i = 0; i < KS; ++i) {  // per K fragment: one LDS read, two MFMAs, VALU between
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+    }
 #pragma unroll
-    for (int s = 0; s < BC / 16; ++s) {
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pf[qb][half])));
+    asm volatile("" ::"v"(l_run[0]), "v"(l_run[1]));
+  };
+  auto rescale = [&] __device__(const float (&alpha)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha[qb];
+  };
+  // O^T += V^T P^T for 32-key block kb of a stage.
+  auto pv = [&] __device__(const char* stage, int kb, const bf16x8 (&pf)[QB][2]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16_t* vr = &vt[cur][(db * 32 + l32) * VSTR + 16 * s + 4 * hl];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-        oacc[db] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf[s], oacc[db]);
+        const char* vr = stage + vaddr[db] + (32 * kb + 16 * half) * ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr + 8 * ROWB));
+        const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+        const bf16x8 vf = as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32x32x16(vf, pf[qb][half], oacc[qb][db]);
       }
     }
+  };
 
-    if (t + 1 < n_kt) sstore(cur ^ 1);
-    __syncthreads();
+  // Prologue: stages 0..2 in flight, wait for stage 0, first S block.
+  issue(lds0, 0);
+  if (n_kt > 1) issue(lds1, 1);
+  if (n_kt > 2) issue(lds2, 2);
+  sync_stage(n_kt > 2 ? 2 : n_kt - 1);
+
+  f32x16 s_cur[QB], s_nxt[QB];
+  bf16x8 pf[QB][2];
+  float alpha[QB];
+  qk(lds0, 0, s_cur);
+
+  // Stage t: `cur` holds it, `nxt` holds stage t+1 (read ahead for its first block),
+  // `refill` is the buffer of stage t-1, reloaded with stage t+3.
+  auto body = [&] __device__(int t, const char* cur, const char* nxt, char* refill) {
+    sync_stage(t + 2 < n_kt ? 1 : 0);  // stage t+1 landed; stage t+2 may be in flight
+    if (t + 3 < n_kt) issue(refill, t + 3);
+    const int k0 = t * BC;
+    if (k0 + 31 > wmin_pos) mask(s_cur, k0);
+    qk(cur, 1, s_nxt);
+    bool any = softmax(s_cur, pf, alpha);
+    close_region(pf);
+    if (__ballot(any)) rescale(alpha);
+    pv(cur, 0, pf);
+    if (k0 + 63 > wmin_pos) mask(s_nxt, k0 + 32);
+    qk(nxt, 0, s_cur);  // after the last stage this reads a stale buffer; the result is unused
+    any = softmax(s_nxt, pf, alpha);
+    close_region(pf);
+    if (__ballot(any)) rescale(alpha);
+    pv(cur, 1, pf);
+  };
+  for (int t = 0; t < n_kt; t += 4) {
+    body(t, lds0, lds1, lds3);
+    if (t + 1 >= n_kt) break;
+    body(t + 1, lds1, lds2, lds0);
+    if (t + 2 >= n_kt) break;
+    body(t + 2, lds2, lds3, lds1);
+    if (t + 3 >= n_kt) break;
+    body(t + 3, lds3, lds0, lds2);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  if (qvalid) {
-    bf16_t* op = a.o + ((int64_t)b * a.rows + qi) * tok + (int64_t)h * HD;
+  float inv[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    inv[qb] = 1.0f / l_tot;
+    l_run[qb] = l_tot;
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (qi[qb] >= a.rows) continue;
+    bf16_t* op = a.o + ((int64_t)b * a.rows + qi[qb]) * tok + (int64_t)h * HD;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int dim = db * 32 + 8 * g + 4 * hl;
-        *reinterpret_cast<uint2*>(op + dim) = pack_bf16x4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                                                          oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        const f32x16& o = oacc[qb][db];
+        *reinterpret_cast<uint2*>(op + dim) =
+            pack_bf16x4(o[4 * g] * inv[qb], o[4 * g + 1] * inv[qb], o[4 * g + 2] * inv[qb], o[4 * g + 3] * inv[qb]);
       }
     }
     if (a.lse != nullptr && hl == 0)
-      a.lse[((int64_t)b * a.H + h) * a.rows + qi] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+      a.lse[((int64_t)b * a.H + h) * a.rows + qi[qb]] = (m_s[qb] + __log2f(l_run[qb])) * 0.69314718055994531f;
   }
 }
 
