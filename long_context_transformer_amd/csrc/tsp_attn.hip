@@ -51,11 +51,19 @@
 namespace tsp {
 namespace {
 
-constexpr int QB = 2;             // 32-row query blocks per wave
-constexpr int BR = 4 * 32 * QB;   // query rows per workgroup (4 waves)
+constexpr int BR = 256;           // query rows per workgroup
 constexpr int BC = 64;            // keys per stage (two 32-key softmax blocks)
-constexpr int kThreads = 256;
 constexpr float kLazy = 8.0f;     // rescale O only when the max grows by more than this (log2)
+// Wave shape: QB 32-row query blocks per wave, NW = BR / (32 QB) waves per workgroup.
+//   QB = 2, NW = 4: one wave per SIMD; each K/V fragment feeds two query blocks.
+//   QB = 1, NW = 8: two waves per SIMD; one wave's softmax overlaps the other's MFMAs
+//                   and hides its LDS latency.
+#ifndef TSP_ATTN_QB
+#define TSP_ATTN_QB 1
+#endif
+constexpr int QB = TSP_ATTN_QB;
+constexpr int NW = BR / (32 * QB);
+constexpr int kThreads = 64 * NW;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -85,6 +93,7 @@ struct Lay {
   static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
   static constexpr int TILEB = BC * ROWB;       // bytes of one K (or V) tile
   static constexpr int NDMA = TILEB / (kThreads * 16);  // 16-byte loads per thread per tile
+  static_assert(NDMA >= 1 && NDMA * kThreads * 16 == TILEB, "whole tile per stage");
   // K fragment reads touch 16 consecutive rows at one chunk; V transpose reads touch 4
   // consecutive rows (aligned to 4) x 4 chunks. Both swizzles spread those over all banks.
   __device__ static int fk(int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); }
@@ -102,7 +111,7 @@ __device__ __forceinline__ void load_lds16(const void* g, char* lds) {
 constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int HD>
-__global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void attn_fwd(AttnArgs a) {
   using L = Lay<HD>;
   constexpr int KS = L::KS, DB = L::DB, ROWB = L::ROWB, CPR = L::CPR, TILEB = L::TILEB, NDMA = L::NDMA;
   __shared__ __attribute__((aligned(1024))) char lds0[2 * TILEB];
@@ -143,13 +152,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   }
 
   // ---- stage loads: global -> LDS, 16 bytes per lane, lane-linear within the 1 KB a wave
-  // instruction writes. Load p of this wave covers linear chunks (4p + wave) * 64 + lane.
+  // instruction writes. Load p of this wave covers linear chunks (NW p + wave) * 64 + lane.
   const char* kseq = reinterpret_cast<const char*>(a.k + (int64_t)b * a.S * tok + (int64_t)h * HD);
   const char* vseq = reinterpret_cast<const char*>(a.v + (int64_t)b * a.S * tok + (int64_t)h * HD);
   int drow[NDMA], dck[NDMA], dcv[NDMA];
 #pragma unroll
   for (int p = 0; p < NDMA; ++p) {
-    const int lin = (4 * p + wave) * 64 + lane;
+    const int lin = (NW * p + wave) * 64 + lane;
     drow[p] = lin / CPR;
     const int pc = lin % CPR;
     dck[p] = 16 * (pc ^ L::fk(drow[p]));
@@ -164,8 +173,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
 #pragma unroll
     for (int p = 0; p < NDMA; ++p) {
       const uint32_t roff = (uint32_t)min(drow[p], lim) * tokb;
-      load_lds16(kb + roff + dck[p], stage + (4 * p + wave) * 1024);
-      load_lds16(vb + roff + dcv[p], stage + TILEB + (4 * p + wave) * 1024);
+      load_lds16(kb + roff + dck[p], stage + (NW * p + wave) * 1024);
+      load_lds16(vb + roff + dcv[p], stage + TILEB + (NW * p + wave) * 1024);
     }
   };
   // Wait until at most `stages` later stages of this wave's loads are in flight, then a
@@ -265,18 +274,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   // in registers so the exponentials cannot sink below the rescale branch.
   auto close_region = [&] __device__(const bf16x8 (&pf)[QB][2]) {
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {  // per K fragment: one LDS read, two MFMAs, VALU between
+    for (int i = 0; i < KS; ++i) {  // per K fragment: one LDS read, QB MFMAs, VALU between
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      if constexpr (QB == 2) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pf[qb][half])));
-    asm volatile("" ::"v"(l_run[0]), "v"(l_run[1]));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" ::"v"(l_run[qb]));
   };
   auto rescale = [&] __device__(const float (&alpha)[QB]) {
 #pragma unroll
