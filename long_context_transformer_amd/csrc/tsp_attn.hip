@@ -51,19 +51,31 @@
 namespace tsp {
 namespace {
 
-constexpr int BR = 256;           // query rows per workgroup
-constexpr int BC = 64;            // keys per stage (two 32-key softmax blocks)
-constexpr float kLazy = 8.0f;     // rescale O only when the max grows by more than this (log2)
-// Wave shape: QB 32-row query blocks per wave, NW = BR / (32 QB) waves per workgroup.
-//   QB = 2, NW = 4: one wave per SIMD; each K/V fragment feeds two query blocks.
-//   QB = 1, NW = 8: two waves per SIMD; one wave's softmax overlaps the other's MFMAs
-//                   and hides its LDS latency.
+// Tile shape. Each wave owns QB 32-row query blocks; a workgroup owns BR rows (NW = BR /
+// (32 QB) waves) and streams keys through LDS in stages of BC (one or two 32-key softmax
+// blocks), with a 4-stage ring.
+//   BR 256, BC 64, QB 1: 8 waves sharing one ring; two waves per SIMD, so one wave's
+//                        softmax can overlap the other's MFMAs (the default, fastest
+//                        measured at 7B S=128K).
+//   BR 128, BC 32, QB 1: 4 waves and a 64 KB ring per workgroup, two workgroups per CU.
+//   BR 256, BC 64, QB 2: one wave per SIMD; each K/V fragment feeds two query blocks.
+#ifndef TSP_ATTN_BR
+#define TSP_ATTN_BR 256
+#endif
+#ifndef TSP_ATTN_BC
+#define TSP_ATTN_BC 64
+#endif
 #ifndef TSP_ATTN_QB
 #define TSP_ATTN_QB 1
 #endif
+constexpr int BR = TSP_ATTN_BR;
+constexpr int BC = TSP_ATTN_BC;
 constexpr int QB = TSP_ATTN_QB;
 constexpr int NW = BR / (32 * QB);
 constexpr int kThreads = 64 * NW;
+constexpr int kWavesPerSimd = (QB == 1) ? 2 : 1;
+constexpr float kLazy = 8.0f;     // rescale O only when the max grows by more than this (log2)
+static_assert(BC == 32 || BC == 64, "one or two 32-key blocks per stage");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -111,7 +123,7 @@ __device__ __forceinline__ void load_lds16(const void* g, char* lds) {
 constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int HD>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void attn_fwd(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void attn_fwd(AttnArgs a) {
   using L = Lay<HD>;
   constexpr int KS = L::KS, DB = L::DB, ROWB = L::ROWB, CPR = L::CPR, TILEB = L::TILEB, NDMA = L::NDMA;
   __shared__ __attribute__((aligned(1024))) char lds0[2 * TILEB];
@@ -330,18 +342,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NW / 4
     sync_stage(t + 2 < n_kt ? 1 : 0);  // stage t+1 landed; stage t+2 may be in flight
     if (t + 3 < n_kt) issue(refill, t + 3);
     const int k0 = t * BC;
-    if (k0 + 31 > wmin_pos) mask(s_cur, k0);
-    qk(cur, 1, s_nxt);
-    bool any = softmax(s_cur, pf, alpha);
-    close_region(pf);
-    if (__ballot(any)) rescale(alpha);
-    pv(cur, 0, pf);
-    if (k0 + 63 > wmin_pos) mask(s_nxt, k0 + 32);
-    qk(nxt, 0, s_cur);  // after the last stage this reads a stale buffer; the result is unused
-    any = softmax(s_nxt, pf, alpha);
-    close_region(pf);
-    if (__ballot(any)) rescale(alpha);
-    pv(cur, 1, pf);
+    if constexpr (BC == 64) {
+      if (k0 + 31 > wmin_pos) mask(s_cur, k0);
+      qk(cur, 1, s_nxt);
+      bool any = softmax(s_cur, pf, alpha);
+      close_region(pf);
+      if (__ballot(any)) rescale(alpha);
+      pv(cur, 0, pf);
+      if (k0 + 63 > wmin_pos) mask(s_nxt, k0 + 32);
+      qk(nxt, 0, s_cur);  // after the last stage this reads a stale buffer; the result is unused
+      any = softmax(s_nxt, pf, alpha);
+      close_region(pf);
+      if (__ballot(any)) rescale(alpha);
+      pv(cur, 1, pf);
+    } else {
+      if (k0 + 31 > wmin_pos) mask(s_cur, k0);
+      qk(nxt, 0, s_nxt);  // after the last stage this reads a stale buffer; the result is unused
+      bool any = softmax(s_cur, pf, alpha);
+      close_region(pf);
+      if (__ballot(any)) rescale(alpha);
+      pv(cur, 0, pf);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s_cur[qb] = s_nxt[qb];
+    }
   };
   for (int t = 0; t < n_kt; t += 4) {
     body(t, lds0, lds1, lds3);
