@@ -5,7 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/tsp.h"
+#include "tsp.h"
 #include "tsp_device.h"
 #include "tsp_internal.h"
 

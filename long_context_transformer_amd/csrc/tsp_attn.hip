@@ -23,9 +23,10 @@
 //   V: chunk c of row r lives at c ^ fv(r); V^T fragments come from ds_read_b64_tr_b16,
 //      whose 16-lane groups each read a 4 key x 16 dim block and hand lane i the four
 //      keys of dim i.
-// The ring buffers are distinct LDS objects and the stage loop is unrolled by the ring
-// depth, so every LDS access names its buffer statically and the compiler does not
-// serialise fragment reads behind the loads still in flight for other stages.
+// The loads are issued from inline assembly (see dma16_sbase), so the compiler does not
+// serialise fragment reads behind them; explicit vmcnt waits and one barrier per stage
+// order them. The stage loop is unrolled by the ring depth so every stage offset is an
+// immediate.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, lane layout in tsp_device.h):
 //   S^T = K Q^T     A = K rows (LDS), B = this wave's Q (registers). A lane holds 16 of the
@@ -36,9 +37,10 @@
 //                   query, so the online-softmax rescale is a per-lane scalar.
 // Each K and V fragment feeds both 32-row query blocks.
 //
-// Pipeline inside a wave, per 32-key block j: the S MFMAs of block j+1 are issued in the
-// same straight-line region as the softmax of block j (the matrix cores work while the
-// VALU computes exponentials), then the rare O rescale, then the PV MFMAs of block j.
+// Pipeline inside a wave, per 32-key block j: the S MFMAs of block j+1 are issued as one
+// block at raised wave priority, then the softmax of block j, the rare O rescale and the
+// PV MFMAs of block j. With two waves per SIMD, the S MFMAs of one wave run on the matrix
+// core while the other wave computes exponentials on the VALU.
 // Softmax in base 2 with the scale folded into one FMA: p = exp2(s*c - m), c =
 // scale*log2(e), m a running max of s*c. O is rescaled only when the running max grows by
 // more than 8 (p <= 2^8 stays exact in fp32 and bf16); the row sum adds the bf16-rounded
@@ -79,8 +81,8 @@ static_assert(BC == 32 || BC == 64, "one or two 32-key blocks per stage");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef const __attribute__((address_space(3))) s16x4 lds_cs16x4;
 
 struct AttnArgs {
   const bf16_t* q;
@@ -112,24 +114,15 @@ struct Lay {
   __device__ static int fv(int r) { return HD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-// 16-byte global -> LDS load (global_load_lds_dwordx4): lane i's bytes land at
-// lds + 16 * i; `lds` must be the same for the whole wave.
-__device__ __forceinline__ void load_lds16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
-}
-
-// s_waitcnt immediate: wait until at most `vm` vector-memory loads of this wave are in
-// flight; the export and LDS counters are left unconstrained.
-constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 template <int HD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void attn_fwd(AttnArgs a) {
   using L = Lay<HD>;
   constexpr int KS = L::KS, DB = L::DB, ROWB = L::ROWB, CPR = L::CPR, TILEB = L::TILEB, NDMA = L::NDMA;
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) char lds2[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) char lds3[2 * TILEB];
+  // K and V rings: stage st of K at kring + st * TILEB, of V at vring + st * TILEB. With
+  // 4 stages each ring spans 64 KB, so every fragment address is a per-lane base plus an
+  // immediate offset.
+  __shared__ __attribute__((aligned(1024))) char kring[4 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char vring[4 * TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -177,16 +170,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     dcv[p] = 16 * (pc ^ L::fv(drow[p]));
   }
   const uint32_t tokb = (uint32_t)(tok * 2);
-  auto issue = [&] __device__(char* stage, int t) {
+  auto issue = [&] __device__(int st, int t) {
     const int key0 = t * BC;
     const int lim = kv_end - 1 - key0;  // rows past the tile's last key repeat it (masked)
     const char* kb = kseq + (int64_t)key0 * tok * 2;
     const char* vb = vseq + (int64_t)key0 * tok * 2;
+    const uint32_t lk = lds_addr(kring) + st * TILEB + wave * 1024;
+    const uint32_t lv = lds_addr(vring) + st * TILEB + wave * 1024;
 #pragma unroll
     for (int p = 0; p < NDMA; ++p) {
       const uint32_t roff = (uint32_t)min(drow[p], lim) * tokb;
-      load_lds16(kb + roff + dck[p], stage + (NW * p + wave) * 1024);
-      load_lds16(vb + roff + dcv[p], stage + TILEB + (NW * p + wave) * 1024);
+      dma16_sbase(kb, roff + dck[p], lk + NW * p * 1024);
+      dma16_sbase(vb, roff + dcv[p], lv + NW * p * 1024);
     }
   };
   // Wait until at most `stages` later stages of this wave's loads are in flight, then a
@@ -200,6 +195,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS read moves above the barrier
   };
 
   // ---- fragment addresses (bytes within a stage; block, half and part add constants)
@@ -207,12 +203,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
   for (int s = 0; s < KS; ++s) kaddr[s] = l32 * ROWB + 16 * ((2 * s + hl) ^ L::fk(l32));
   const int G = lane >> 4, j16 = lane & 15;
-  int vaddr[DB];
+  // V^T fragment bases as LDS-typed pointers, so stage / block / part offsets fold into
+  // the transpose reads' immediate offset field (units of 8 bytes).
+  const lds_s16x4* vbase[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const int r = 4 * hl + (j16 >> 2);  // row within an aligned group of 8 keys
     const int c = 4 * db + 2 * (G & 1) + ((j16 & 3) >> 1);
-    vaddr[db] = TILEB + r * ROWB + 16 * (c ^ L::fv(r)) + 8 * (j16 & 1);
+    vbase[db] = (const lds_s16x4*)(vring + r * ROWB + 16 * (c ^ L::fv(r)) + 8 * (j16 & 1));
   }
 
   f32x16 oacc[QB][DB];
@@ -230,15 +228,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // S^T of 32-key block kb (0/1) of a stage, both query blocks.
-  auto qk = [&] __device__(const char* stage, int kb, f32x16 (&sacc)[QB]) {
+  auto qk = [&] __device__(int st, int kb, f32x16 (&sacc)[QB]) {
+    // The S MFMAs issue as one block of their own (no VALU interleaved) at raised wave
+    // priority: with two waves per SIMD, one wave's MFMA block then runs while the other
+    // wave does its softmax.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) sacc[qb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(stage + kaddr[s] + kb * 32 * ROWB));
+      const bf16x8 kf =
+          as_bf16x8(*reinterpret_cast<const uint4*>(kring + st * TILEB + kaddr[s] + kb * 32 * ROWB));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sacc[qb] = mfma32x32x16(kf, qf[qb][s], sacc[qb]);
     }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto mask = [&] __device__(f32x16 (&sacc)[QB], int kstart) {
 #pragma unroll
@@ -281,20 +287,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
     return any;
   };
-  // Ends a straight-line region [S MFMAs of the next block + softmax of this one]: asks the
-  // scheduler to alternate one MFMA with a run of VALU work, then pins P and the row sums
-  // in registers so the exponentials cannot sink below the rescale branch.
+  // Pins P and the row sums in registers at the end of the softmax, so the exponentials
+  // cannot sink below the rescale branch into the PV region.
   auto close_region = [&] __device__(const bf16x8 (&pf)[QB][2]) {
-#pragma unroll
-    for (int i = 0; i < KS; ++i) {  // per K fragment: one LDS read, QB MFMAs, VALU between
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-      if constexpr (QB == 2) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-      }
-    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -309,14 +304,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha[qb];
   };
   // O^T += V^T P^T for 32-key block kb of a stage.
-  auto pv = [&] __device__(const char* stage, int kb, const bf16x8 (&pf)[QB][2]) {
+  auto pv = [&] __device__(int st, int kb, const bf16x8 (&pf)[QB][2]) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const char* vr = stage + vaddr[db] + (32 * kb + 16 * half) * ROWB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr + 8 * ROWB));
+        const lds_s16x4* vr = vbase[db] + (st * TILEB + (32 * kb + 16 * half) * ROWB) / 8;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vr);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr + ROWB));
         const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
         const bf16x8 vf = as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
 #pragma unroll
@@ -326,19 +321,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   };
 
   // Prologue: stages 0..2 in flight, wait for stage 0, first S block.
-  issue(lds0, 0);
-  if (n_kt > 1) issue(lds1, 1);
-  if (n_kt > 2) issue(lds2, 2);
+  issue(0, 0);
+  if (n_kt > 1) issue(1, 1);
+  if (n_kt > 2) issue(2, 2);
   sync_stage(n_kt > 2 ? 2 : n_kt - 1);
 
   f32x16 s_cur[QB], s_nxt[QB];
   bf16x8 pf[QB][2];
   float alpha[QB];
-  qk(lds0, 0, s_cur);
+  qk(0, 0, s_cur);
 
   // Stage t: `cur` holds it, `nxt` holds stage t+1 (read ahead for its first block),
   // `refill` is the buffer of stage t-1, reloaded with stage t+3.
-  auto body = [&] __device__(int t, const char* cur, const char* nxt, char* refill) {
+  auto body = [&] __device__(int t, int cur, int nxt, int refill) {
     sync_stage(t + 2 < n_kt ? 1 : 0);  // stage t+1 landed; stage t+2 may be in flight
     if (t + 3 < n_kt) issue(refill, t + 3);
     const int k0 = t * BC;
@@ -366,14 +361,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       for (int qb = 0; qb < QB; ++qb) s_cur[qb] = s_nxt[qb];
     }
   };
+  // Unrolled by the ring depth so every stage buffer is named statically; guarded bodies
+  // (no early exits) keep the accumulators in one register set.
   for (int t = 0; t < n_kt; t += 4) {
-    body(t, lds0, lds1, lds3);
-    if (t + 1 >= n_kt) break;
-    body(t + 1, lds1, lds2, lds0);
-    if (t + 2 >= n_kt) break;
-    body(t + 2, lds2, lds3, lds1);
-    if (t + 3 >= n_kt) break;
-    body(t + 3, lds3, lds0, lds2);
+    body(t, 0, 1, 3);
+    if (t + 1 < n_kt) body(t + 1, 1, 2, 0);
+    if (t + 2 < n_kt) body(t + 2, 2, 3, 1);
+    if (t + 3 < n_kt) body(t + 3, 3, 0, 2);
   }
 
   float inv[QB];

@@ -49,6 +49,30 @@ __device__ __forceinline__ bf16_t to_bf16(float x) {
   return __builtin_bit_cast(bf16_t, v);
 }
 
+// 16-byte global -> LDS copies (global_load_lds_dwordx4): lane i's 16 bytes land at LDS
+// byte address `lds` + 16 i, where `lds` is the same for the whole wave (it goes to M0).
+// Issued from inline assembly on purpose: the compiler then neither tracks these writes
+// nor inserts its own conservative waits before LDS reads; callers order them with
+// explicit s_waitcnt vmcnt (loads retire in order) and s_barrier. Nothing else in these
+// kernels uses M0.
+//   dma16_sbase: address = uniform 64-bit base + per-lane 32-bit byte offset
+//   dma16_vaddr: address = per-lane 64-bit pointer
+__device__ __forceinline__ void dma16_sbase(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma16_vaddr(const void* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds) : "memory");
+}
+// LDS byte address of a pointer into a __shared__ array, made wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// s_waitcnt immediate that waits until at most `vm` vector-memory loads of this wave are
+// in flight, leaving the export and LDS counters unconstrained.
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // Global position of local row i of rank r, for chunk length C and fold D.
 // Rows 0..C-1 are chunk r, rows C..2C-1 are the mirror chunk 2D-1-r.
 __host__ __device__ __forceinline__ int64_t zigzag_pos(int64_t i, int64_t C, int r, int D) {

@@ -255,6 +255,187 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(Operands op, Epi epi, int ti
   }
 }
 
+// ------------------------------------------------------------------- fast path (16-byte operands)
+// Same contraction and epilogues, with the operand tiles moved straight from global memory
+// into LDS (16-byte global_load_lds per lane, no register staging, no bounds predicates):
+//   * k advances in stages of 32 through a 3-deep ring of separate LDS buffers, loads
+//     issued two stages ahead, one barrier per stage;
+//   * a tile row holds 32 bf16 = four 16-byte chunks, chunk c of row r stored at
+//     c ^ ((r / 4) % 4), so the 16 rows read by 16 lanes at one chunk hit 16 distinct
+//     bank groups;
+//   * rows past M or N repeat the last row (their outputs are never stored); chunks past
+//     K (the last stage when K % 32 != 0) come from a block of zeros;
+//   * 8 waves per 256-wide tile (two per SIMD), each owning 128 x 64 outputs (128 x 32 per
+//     weight for the gated pair), so one wave's MFMAs cover the other's LDS latency.
+constexpr int FBK = 32;
+
+// Zeros read in place of chunks past K (16 bytes per lane). Never written.
+__device__ __attribute__((aligned(16))) uint4 kZeroChunks[64];
+
+template <int BM, int BN, int WM, int WN, bool DUAL, class Epi>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n) {
+  constexpr int NWN = BN / WN, NWAVE = (BM / WM) * NWN;
+  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int MI = WM / 32, NI = WN / 32;
+  constexpr int ATILE = BM * FBK * 2, BTILE = BN * FBK * 2;
+  constexpr int STAGE = ATILE + NB * BTILE;
+  constexpr int AINS = ATILE / 1024 / NWAVE;  // 1 KB DMA instructions per wave per stage
+  constexpr int BINS = BTILE / 1024 / NWAVE;
+  constexpr int LOADS = AINS + NB * BINS;     // per thread per stage
+  static_assert(AINS >= 1 && AINS * NWAVE * 1024 == ATILE, "A tile split");
+  static_assert(BINS >= 1 && BINS * NWAVE * 1024 == BTILE, "B tile split");
+  __shared__ __attribute__((aligned(1024))) char s0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char s1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char s2[STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int l32 = lane & 31, hl = lane >> 5;
+
+  const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+  const int span = kGroupM * tiles_n;
+  const int first_m = (t / span) * kGroupM;
+  const int gsz = min(tiles_m - first_m, kGroupM);
+  const int in_g = t - (t / span) * span;
+  const int m0 = (first_m + in_g % gsz) * BM;
+  const int n0 = (in_g / gsz) * BN;
+
+  // DMA instruction p of this wave covers tile rows 16 (p NWAVE + wave) + lane/4, physical
+  // chunk lane%4, i.e. logical chunk (lane%4) ^ ((row/4)%4).
+  uint32_t aoff[AINS], boff[BINS];
+  int akc[AINS], bkc[BINS];
+#pragma unroll
+  for (int p = 0; p < AINS; ++p) {
+    const int row = 16 * (p * NWAVE + wave) + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    aoff[p] = (uint32_t)min(m0 + row, op.M - 1) * (uint32_t)(op.lda * 2) + 16 * c;
+    akc[p] = 8 * c;
+  }
+#pragma unroll
+  for (int p = 0; p < BINS; ++p) {
+    const int row = 16 * (p * NWAVE + wave) + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    boff[p] = (uint32_t)min(n0 + row, op.N - 1) * (uint32_t)(op.ldb * 2) + 16 * c;
+    bkc[p] = 8 * c;
+  }
+  const char* abase = reinterpret_cast<const char*>(op.a);
+  const char* bbase = reinterpret_cast<const char*>(op.b);
+  const char* b2base = reinterpret_cast<const char*>(DUAL ? op.b2 : op.b);
+  auto issue = [&] __device__(char* st, int kt) {
+    const int k0 = kt * FBK;
+    const char* ab = abase + (size_t)k0 * 2;
+    const char* bb = bbase + (size_t)k0 * 2;
+    const char* b2 = b2base + (size_t)k0 * 2;
+    const uint32_t la = lds_addr(st) + wave * 1024;
+    if (k0 + FBK <= op.K) {
+#pragma unroll
+      for (int p = 0; p < AINS; ++p) dma16_sbase(ab, aoff[p], la + p * NWAVE * 1024);
+#pragma unroll
+      for (int p = 0; p < BINS; ++p) dma16_sbase(bb, boff[p], la + ATILE + p * NWAVE * 1024);
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int p = 0; p < BINS; ++p) dma16_sbase(b2, boff[p], la + ATILE + BTILE + p * NWAVE * 1024);
+      }
+    } else {  // last stage with K % 32 != 0: chunks past K read zeros
+      const void* z = &kZeroChunks[lane];
+#pragma unroll
+      for (int p = 0; p < AINS; ++p)
+        dma16_vaddr(k0 + akc[p] < op.K ? (const void*)(ab + aoff[p]) : z, la + p * NWAVE * 1024);
+#pragma unroll
+      for (int p = 0; p < BINS; ++p)
+        dma16_vaddr(k0 + bkc[p] < op.K ? (const void*)(bb + boff[p]) : z, la + ATILE + p * NWAVE * 1024);
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int p = 0; p < BINS; ++p)
+          dma16_vaddr(k0 + bkc[p] < op.K ? (const void*)(b2 + boff[p]) : z, la + ATILE + BTILE + p * NWAVE * 1024);
+      }
+    }
+  };
+
+  // Fragment byte offsets within a stage for k-steps 0 and 1 (row l32 of a 32-row block).
+  const int x = (l32 >> 2) & 3;
+  const int fo[2] = {l32 * 64 + 16 * (hl ^ x), l32 * 64 + 16 * ((2 + hl) ^ x)};
+
+  f32x16 acc[NB][MI][NI];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) acc[nb][mi][ni] = f32x16{};
+
+  auto compute = [&] __device__(const char* st) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[MI];
+      bf16x8 bfr[NB][NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        af[mi] = as_bf16x8(*reinterpret_cast<const uint4*>(st + (wm * WM + 32 * mi) * 64 + fo[ks]));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          bfr[nb][ni] = as_bf16x8(
+              *reinterpret_cast<const uint4*>(st + ATILE + nb * BTILE + (wn * WN + 32 * ni) * 64 + fo[ks]));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) acc[nb][mi][ni] = mfma32x32x16(bfr[nb][ni], af[mi], acc[nb][mi][ni]);
+    }
+  };
+
+  const int nk = (op.K + FBK - 1) / FBK;
+  issue(s0, 0);
+  if (nk > 1) issue(s1, 1);
+  // Stage kt: wait for its loads (stage kt+1 may stay in flight), barrier, refill the buffer
+  // of stage kt-1 with stage kt+2, then the MFMAs of stage kt.
+  auto body = [&] __device__(int kt, const char* cur, char* refill) {
+    if (kt + 1 < nk) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS read moves above the barrier
+    if (kt + 2 < nk) issue(refill, kt + 2);
+    compute(cur);
+  };
+  // Unrolled by the ring depth so every stage buffer is named statically; guarded bodies
+  // (no early exits) keep the accumulators in one register set.
+  for (int kt = 0; kt < nk; kt += 3) {
+    body(kt, s0, s2);
+    if (kt + 1 < nk) body(kt + 1, s1, s0);
+    if (kt + 2 < nk) body(kt + 2, s2, s1);
+  }
+
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int m = m0 + wm * WM + mi * 32 + l32;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WN + ni * 32 + 8 * g + 4 * hl;
+        const f32x4 v0 = {acc[0][mi][ni][4 * g], acc[0][mi][ni][4 * g + 1], acc[0][mi][ni][4 * g + 2],
+                          acc[0][mi][ni][4 * g + 3]};
+        if constexpr (DUAL) {
+          const f32x4 v1 = {acc[1][mi][ni][4 * g], acc[1][mi][ni][4 * g + 1], acc[1][mi][ni][4 * g + 2],
+                            acc[1][mi][ni][4 * g + 3]};
+          epi(m, n, v0, v1, op.M, op.N);
+        } else {
+          epi(m, n, v0, op.M, op.N);
+        }
+      }
+    }
+  }
+}
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <int BM, int BN, bool DUAL, bool VEC, class Epi>
@@ -265,29 +446,52 @@ hipError_t run_tiles(const Operands& op, const Epi& epi, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Large problems take the 256 x 256 tile (256 x 128 for the gated pair, which carries
-// two accumulators); when that leaves fewer tiles than CUs the 128 x 128 (128 x 64)
-// tile keeps the chip busy. Operands that are not 16-byte vectorisable (odd K or
-// strides, only in tiny shapes) take the element-wise loader with the small tile.
+template <int BM, int BN, int WM, int WN, bool DUAL, class Epi>
+hipError_t run_fast(const Operands& op, const Epi& epi, hipStream_t s) {
+  const int tm = (op.M + BM - 1) / BM;
+  const int tn = (op.N + BN - 1) / BN;
+  constexpr int threads = (BM / WM) * (BN / WN) * 64;
+  hipLaunchKernelGGL((gemm_fast<BM, BN, WM, WN, DUAL, Epi>), dim3(tm * tn), dim3(threads), 0, s, op, epi, tm, tn);
+  return hipGetLastError();
+}
+
+// Operand requirements of the fast path: 16-byte chunks (K, strides multiples of 8
+// elements, 16-byte aligned bases) and byte offsets of every row within 32 bits.
+bool fast_ok(const Operands& op, bool dual) {
+  const bool vec = (op.K % 8 == 0) && (op.lda % 8 == 0) && (op.ldb % 8 == 0) && aligned16(op.a) && aligned16(op.b) &&
+                   (!dual || aligned16(op.b2));
+  const uint64_t a_span = (uint64_t)(op.M - 1) * (uint64_t)op.lda * 2 + (uint64_t)op.K * 2;
+  const uint64_t b_span = (uint64_t)(op.N - 1) * (uint64_t)op.ldb * 2 + (uint64_t)op.K * 2;
+  return vec && a_span < (1ull << 32) && b_span < (1ull << 32);
+}
+
+// Large problems take the 256 x 256 tile (256 x 128 for the gated pair, which carries two
+// accumulators); when that leaves fewer tiles than CUs the 128 x 128 (128 x 64) tile keeps
+// the chip busy. Operands that cannot take 16-byte chunks (odd K or strides: only tiny
+// shapes) use the register-staged kernel with element-wise loads.
 constexpr int64_t kBigTileMin = 256;
 
 template <class Epi>
 hipError_t run_single(const Operands& op, const Epi& epi, hipStream_t s) {
-  const bool vec = (op.K % 8 == 0) && (op.lda % 8 == 0) && (op.ldb % 8 == 0) && aligned16(op.a) && aligned16(op.b);
-  if (!vec) return run_tiles<128, 128, false, false>(op, epi, s);
+  if (!fast_ok(op, false)) {
+    const bool vec = (op.K % 8 == 0) && (op.lda % 8 == 0) && (op.ldb % 8 == 0) && aligned16(op.a) && aligned16(op.b);
+    return vec ? run_tiles<128, 128, false, true>(op, epi, s) : run_tiles<128, 128, false, false>(op, epi, s);
+  }
   const int64_t big = (int64_t)((op.M + 255) / 256) * ((op.N + 255) / 256);
-  if (big >= kBigTileMin) return run_tiles<256, 256, false, true>(op, epi, s);
-  return run_tiles<128, 128, false, true>(op, epi, s);
+  if (big >= kBigTileMin) return run_fast<256, 256, 128, 64, false>(op, epi, s);
+  return run_fast<128, 128, 64, 64, false>(op, epi, s);
 }
 
 template <class Epi>
 hipError_t run_dual(const Operands& op, const Epi& epi, hipStream_t s) {
-  const bool vec = (op.K % 8 == 0) && (op.lda % 8 == 0) && (op.ldb % 8 == 0) && aligned16(op.a) &&
-                   aligned16(op.b) && aligned16(op.b2);
-  if (!vec) return run_tiles<128, 64, true, false>(op, epi, s);
+  if (!fast_ok(op, true)) {
+    const bool vec = (op.K % 8 == 0) && (op.lda % 8 == 0) && (op.ldb % 8 == 0) && aligned16(op.a) &&
+                     aligned16(op.b) && aligned16(op.b2);
+    return vec ? run_tiles<128, 64, true, true>(op, epi, s) : run_tiles<128, 64, true, false>(op, epi, s);
+  }
   const int64_t big = (int64_t)((op.M + 255) / 256) * ((op.N + 127) / 128);
-  if (big >= kBigTileMin) return run_tiles<256, 128, true, true>(op, epi, s);
-  return run_tiles<128, 64, true, true>(op, epi, s);
+  if (big >= kBigTileMin) return run_fast<256, 128, 128, 32, true>(op, epi, s);
+  return run_fast<128, 64, 64, 32, true>(op, epi, s);
 }
 
 }  // namespace
