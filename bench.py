@@ -1,7 +1,7 @@
 """Benchmark of one TSP rank's layer forward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rank R]
-                [--no-cpu-baseline] [--sweep PATH]
+                [--no-cpu-baseline] [--cpu-rows N] [--calib-copy] [--sweep PATH]
 
 A step is one tsp_layer_fwd call: QKV projection of the rank's zigzag shard, causal
 attention against the full-sequence K/V, W_O, and the D-shard SwiGLU ring accumulated in
@@ -10,14 +10,24 @@ synthetic tensors already resident in HBM; the peers' K/V rows (what the all-gat
 delivers) are filled before timing by the peers' own QKV projections.
 
 Prints ONE JSON line: whole-step throughput in TFLOP/s of algorithmic work (exact
-causal pairs), the attention kernel's roofline (its own launches timed with HIP events
-on the stream it runs on), and the CPU oracle timed on a bounded sample of the same
-workload.
+causal pairs), the attention kernel's roofline, and the CPU oracle timed on a bounded
+sample of the same workload. The attention time is the average over the K timed steps
+of the library's own phase events, recorded on the launch stream around the attention
+launch inside each tsp_layer_fwd call (tsp_timing_start / tsp_timing_read). The
+roofline's HBM traffic comes from the committed FETCH_SIZE / WRITE_SIZE counter summary
+of the attention kernel, and is reported only while the kernel's sources still hash to
+the value recorded there.
+
+--calib-copy runs, before the timed steps, one plain device copy of 256 MiB (fp32
+negation: 256 MiB read, 256 MiB written) whose counter readings calibrate FETCH_SIZE and
+WRITE_SIZE into bytes.
 """
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,6 +39,12 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 F
 PEAK_HBM_GBS = 8000.0
 METRIC = "TSP rank-shard layer fwd TFLOP/s (% bf16 MFMA peak), 7B layer, S=16K-128K"
 DEFAULT_WORKLOAD = "7b_s128k_d8"
+PKG = os.path.join(ROOT, "long_context_transformer_amd")
+# Sources that determine the attention kernel's code; the counter summary records their hash.
+ATTN_SOURCES = [os.path.join(PKG, "csrc", "tsp_attn.hip"), os.path.join(PKG, "csrc", "tsp_device.h"),
+                os.path.join(PKG, "build.py")]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_7b_s128k_d8_hbm_traffic.md")
+CALIB_MIB = 256
 
 
 def layer_flops(B, S, D, d, H, hd, F):
@@ -65,12 +81,8 @@ def setup(w, rank):
         "desc": tsp.make_desc(B, S, D, rank, d, H, hd, F),
         "attn_out": torch.empty((B, S // D, d), dtype=torch.bfloat16, device="cuda"),
         "mlp_out": torch.empty((B, S // D, d), dtype=torch.float32, device="cuda"),
-        "q": torch.empty((B, S // D, d), dtype=torch.bfloat16, device="cuda"),
-        "o": torch.empty((B, S // D, d), dtype=torch.bfloat16, device="cuda"),
     }
     st["ws"] = torch.empty(tsp.layer_workspace_size(st["desc"]), dtype=torch.uint8, device="cuda")
-    # Q of the rank for the attention-only timing
-    tsp.qkv_fwd(xs, dev["w_qkv"], st["q"], kf, vf, B, S, D, rank, H, hd)
     torch.cuda.synchronize()
     st["setup_s"] = time.time() - t0
     return st
@@ -83,10 +95,14 @@ def step(st):
 
 
 def time_layer(st, steps, warmup):
+    """Average step time (ms) over `steps` timed steps, and the per-phase averages from the
+    library's events recorded inside those same steps."""
     import torch
+    from long_context_transformer_amd import tsp
     for _ in range(warmup):
         step(st)
     torch.cuda.synchronize()
+    tsp.timing_start(steps)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     ev0.record()
@@ -95,23 +111,42 @@ def time_layer(st, steps, warmup):
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    return ev0.elapsed_time(ev1) / steps, wall
+    calls = tsp.timing_read(steps)
+    phases = {p: sum(c[p] for c in calls) / len(calls) for p in tsp.PHASES}
+    return ev0.elapsed_time(ev1) / steps, wall, phases
 
 
-def time_attention(st, w, rank, launches):
-    """Average duration of the attention kernel alone, HIP events on its own stream."""
+def calib_copy():
+    """One plain copy kernel of known size (CALIB_MIB read, CALIB_MIB written)."""
     import torch
-    from long_context_transformer_amd import tsp
-    args = (st["q"], st["kf"], st["vf"], st["o"], None, w.B, w.S, w.D, rank, w.n_heads, w.head_dim)
-    tsp.attn_fwd(*args)
+    n = CALIB_MIB * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(launches):
-        tsp.attn_fwd(*args)
-    ev1.record()
+    torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / launches
+    del src, dst
+
+
+def attn_sources_hash():
+    h = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def attn_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary, or None when the
+    summary is absent, covers another workload, or the kernel's sources have changed."""
+    if workload != DEFAULT_WORKLOAD or not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    src = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not src or not val or src.group(1) != attn_sources_hash():
+        return None
+    return float(val.group(1))
 
 
 def blas_threads():
@@ -126,14 +161,15 @@ def blas_threads():
 
 
 def cpu_baseline(w, inputs, rank, rows_sample):
-    """The fp64 oracle on a bounded sample of the same workload: the last `rows_sample`
-    local rows of the rank's early chunk, with the K/V projection of every position
-    those rows see. Returns TFLOP/s of the algorithmic work of that sample."""
+    """The fp64 oracle on a bounded sample of the same workload: the rank's last
+    `rows_sample` local rows (the end of its mirror chunk, the rows with the longest key
+    prefix), through QKV, causal attention, W_O and the SwiGLU, with the K/V projection of
+    every position those rows see. Returns TFLOP/s of the work the oracle does for it."""
     import numpy as np
     from long_context_transformer_amd import synth
     from oracle import tsp_oracle as O
-    C = w.C
-    rows = np.arange(C - rows_sample, C)
+    R2 = w.rows
+    rows = np.arange(R2 - rows_sample, R2)
     idx = O.zigzag_index(w.S, w.D, rank)
     kmax = int(idx[rows].max()) + 1
     b_sel = slice(0, 1)
@@ -152,7 +188,7 @@ def cpu_baseline(w, inputs, rank, rows_sample):
              + 6 * R * d * F)
     threads, api = blas_threads()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": (f"{w.name} rank {rank}, batch 0: local rows {C - R}..{C - 1} (positions "
+            "sample": (f"{w.name} rank {rank}, batch 0: local rows {R2 - R}..{R2 - 1} (positions "
                        f"{int(idx[rows].min())}..{int(idx[rows].max())}) through QKV, causal "
                        f"attention, W_O and SwiGLU, plus K/V projections of positions 0..{kmax - 1}; "
                        f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64 numpy ({api})"),
@@ -166,9 +202,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--rank", type=int, default=0)
-    ap.add_argument("--attn-launches", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 256 MiB plain copy kernel first (counter calibration)")
     ap.add_argument("--sweep", default=None, help="also time every workload (and every rank of the "
                     "S=32K one) and write one JSON line each to this file")
     args = ap.parse_args()
@@ -189,13 +226,17 @@ def main():
     w = synth.WORKLOADS[args.workload].with_rank(args.rank)
     st = setup(w, args.rank)
     print(f"# setup {st['setup_s']:.1f}s", file=sys.stderr, flush=True)
-    ms, wall = time_layer(st, args.steps, args.warmup)
+    if args.calib_copy:
+        calib_copy()
+    ms, wall, phases = time_layer(st, args.steps, args.warmup)
     flops, attn_flops = layer_flops(w.B, w.S, w.D, w.d_model, w.n_heads, w.head_dim, w.ffn)
     tflops = flops / (ms * 1e-3) / 1e12
-    attn_ms = time_attention(st, w, args.rank, args.attn_launches)
+    attn_ms = phases["attention"]
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
     print(f"# layer {ms:.3f} ms  {tflops:.1f} TFLOP/s  attention {attn_ms:.3f} ms "
-          f"{attn_tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+          f"{attn_tflops:.1f} TFLOP/s  phases " + " ".join(f"{k}={v:.3f}" for k, v in phases.items()),
+          file=sys.stderr, flush=True)
+    traffic = attn_traffic(w.name)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -220,10 +261,11 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "seq_len": w.S, "fold": w.D, "rank": args.rank,
                    "d_model": w.d_model, "n_heads": w.n_heads, "head_dim": w.head_dim,
                    "ffn": w.ffn, "flops_per_step": flops},
+        "phases_ms": {k: round(v, 4) for k, v in phases.items()},
         "roofline": {"kernel": "attention (attn_fwd<128>)", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "avg_launch_ms": round(attn_ms, 4),
+                     "traffic": traffic, "avg_launch_ms": round(attn_ms, 4),
                      "flops_per_launch": attn_flops},
         "cpu_baseline": cpu,
     }
@@ -236,13 +278,14 @@ def main():
                 for r in ranks:
                     ww = base.with_rank(r)
                     s2 = setup(ww, r)
-                    ms2, _ = time_layer(s2, 10 if ww.S >= 65536 else 20, 3)
+                    ms2, _, ph2 = time_layer(s2, 10 if ww.S >= 65536 else 20, 3)
                     fl, afl = layer_flops(ww.B, ww.S, ww.D, ww.d_model, ww.n_heads, ww.head_dim, ww.ffn)
-                    ams = time_attention(s2, ww, r, 5)
+                    ams = ph2["attention"]
                     line = {"workload": name, "rank": r, "ms": round(ms2, 4),
                             "tflops": round(fl / ms2 / 1e9, 2),
                             "pct_peak": round(100 * fl / ms2 / 1e9 / PEAK_BF16_TFLOPS, 2),
-                            "attn_ms": round(ams, 4), "attn_tflops": round(afl / ams / 1e9, 2)}
+                            "attn_ms": round(ams, 4), "attn_tflops": round(afl / ams / 1e9, 2),
+                            "phases_ms": {k: round(v, 4) for k, v in ph2.items()}}
                     f.write(json.dumps(line) + "\n")
                     f.flush()
                     print("# sweep " + json.dumps(line), file=sys.stderr, flush=True)

@@ -29,10 +29,14 @@
  *     r*C .. r*C+C-1) then chunk 2D-1-r, both ascending; C = S/(2D).
  *   - Device pointers are allocated and owned by the caller, must be 16-byte aligned,
  *     and outputs must not alias inputs. The library never allocates or frees memory,
- *     never synchronises, and keeps no state between calls.
+ *     never synchronises, and keeps no state between calls (the opt-in timing hook at
+ *     the end of this header aside).
  *   - `stream` is a hipStream_t (NULL = the default stream). Kernels are enqueued on it
  *     and run asynchronously; errors raised while they run surface at the caller's
  *     next synchronisation of that stream.
+ *   - Empty problems (B = 0, S = 0, or M = 0 for the MLP step) are valid: after the
+ *     shape checks the call returns TSP_OK without reading any pointer or launching
+ *     anything (torch hands out NULL data pointers for empty tensors).
  *   - Every entry point returns a tsp_status. Argument errors are decided on the host
  *     before any HIP call, so they are deterministic and safe without a GPU. The
  *     message of the last error on the calling thread is tsp_last_error().
@@ -96,8 +100,8 @@ TSP_API const char* tsp_last_error(void);
  * idx_out: idx[i] = r*C + i for i < C, and (2D-1-r)*C + (i-C) for C <= i < 2C, with
  * C = S/(2D). Pairing chunk r with its mirror 2D-1-r gives every rank C*(S+1) causal
  * (query, key) pairs per sequence and head. Exact integer arithmetic.
- * Errors: TSP_ERR_NULL (idx_out), TSP_ERR_SHAPE (S <= 0, D <= 0, S % 2D != 0,
- * idx_len != S/D), TSP_ERR_RANK.
+ * Errors: TSP_ERR_NULL (idx_out, when S > 0), TSP_ERR_SHAPE (S < 0, D <= 0,
+ * S % 2D != 0, idx_len != S/D), TSP_ERR_RANK.
  */
 TSP_API int tsp_zigzag_index(int64_t S, int32_t D, int32_t rank, int64_t* idx_out, int64_t idx_len);
 
@@ -153,7 +157,9 @@ TSP_API int tsp_mlp_shard_accum(const void* x, const void* w1_j, const void* w3_
                         int64_t ld_w2, float* acc, int64_t M, int32_t d, int32_t Fs,
                         int32_t accumulate, void* ws, size_t ws_bytes, tsp_stream_t stream);
 
-/* Workspace bytes tsp_layer_fwd needs for `desc` (0 if desc is invalid). */
+/* Workspace bytes tsp_layer_fwd needs for `desc` (0 if desc is invalid): Q and O of the
+ * rank, bf16 [B, 2C, d] each, and the gated hidden of all D shards, bf16
+ * [B*2C, D * round_up(F/D, 8)]. */
 TSP_API size_t tsp_layer_workspace_size(const tsp_layer_desc* desc);
 
 /*
@@ -169,12 +175,32 @@ TSP_API size_t tsp_layer_workspace_size(const tsp_layer_desc* desc);
  *   mlp_out  f32  [B, 2C, d]  sum over the D shards, taken in ring order
  *            j = (r - t) mod D for t = 0 .. D-1
  *   ws       device workspace, at least tsp_layer_workspace_size(desc) bytes
- * The pointer arrays w1/w3/w2 live in HOST memory.
+ * The pointer arrays w1/w3/w2 live in HOST memory. With every shard on the device, the
+ * MLP runs as two launches (gated hidden of all shards; one down projection whose
+ * reduction takes the shards in the ring order above, fp32 in registers) when D <= 32,
+ * F/D and d are multiples of 8 and every shard is 16-byte aligned; otherwise as D
+ * tsp_mlp_shard_accum-style steps. Both give the same sum order over the shards.
  */
 TSP_API int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const void* w_qkv,
                   const void* w_o, const void* const* w1, const void* const* w3,
                   const void* const* w2, void* k_full, void* v_full, void* attn_out,
                   float* mlp_out, void* ws, size_t ws_bytes, tsp_stream_t stream);
+
+/*
+ * Measurement hook (outside the method): phase timing of tsp_layer_fwd with HIP events
+ * recorded on the call's own stream, between its launches.
+ *   tsp_timing_start(max_calls)  creates (4 + 1) * max_calls events and arms the hook:
+ *       the next max_calls tsp_layer_fwd calls record an event before the QKV launch and
+ *       after the QKV, attention, W_O and MLP launches. max_calls = 0 disarms and
+ *       destroys the events. These events are the only objects the library creates.
+ *   tsp_timing_read(ms, max_calls, n_calls)  waits for the last recorded event, writes
+ *       ms[4 i + p] = milliseconds of phase p (0 QKV, 1 attention, 2 W_O, 3 MLP) of
+ *       recorded call i for i < *n_calls = min(calls recorded, max_calls), then disarms.
+ * Process-wide state behind a mutex; arm it only around calls that do not overlap.
+ * Errors: TSP_ERR_SHAPE (max_calls < 0), TSP_ERR_NULL, TSP_ERR_HIP.
+ */
+TSP_API int tsp_timing_start(int32_t max_calls);
+TSP_API int tsp_timing_read(float* ms, int32_t max_calls, int32_t* n_calls);
 
 #ifdef __cplusplus
 }

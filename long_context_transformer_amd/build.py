@@ -54,6 +54,45 @@ def _run(cmd, verbose):
     return out
 
 
+def _llvm_tool(name):
+    for cand in (os.path.join("/opt/rocm/llvm/bin", name), shutil.which(name)):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError(f"{name} not found")
+
+
+def check_kernel_names(obj):
+    """Every kernel the host code of `obj` launches must exist under the same mangled name
+    in its gfx950 code object (otherwise the launch fails at run time). The host side has a
+    handle symbol per kernel, next to its __device_stub__; the device side lists kernels in
+    the code object's metadata notes."""
+    import tempfile
+    with tempfile.TemporaryDirectory() as td:
+        fatbin = os.path.join(td, "fatbin")
+        code = os.path.join(td, "code")
+        subprocess.run(["objcopy", f"--dump-section=.hip_fatbin={fatbin}", obj, os.path.join(td, "o")],
+                       check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        subprocess.run([_llvm_tool("clang-offload-bundler"), "--unbundle", "--type=o", f"--input={fatbin}",
+                        f"--targets=hipv4-amdgcn-amd-amdhsa--{ARCH}", f"--output={code}"], check=True,
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        notes = subprocess.run([_llvm_tool("llvm-readelf"), "--notes", code], check=True, text=True,
+                               stdout=subprocess.PIPE).stdout
+    device = {line.split()[1].strip("'\"") for line in notes.splitlines()
+              if line.strip().startswith(".name:") and "_Z" in line}
+    mangled = subprocess.run(["nm", "--defined-only", obj], check=True, text=True,
+                             stdout=subprocess.PIPE).stdout.splitlines()
+    demangled = subprocess.run(["nm", "-C", "--defined-only", obj], check=True, text=True,
+                               stdout=subprocess.PIPE).stdout.splitlines()
+    stubs = {l.split(" ", 2)[2].replace("__device_stub__", "") for l in demangled if "__device_stub__" in l}
+    handles = [m.split(" ", 2)[2] for m, dm in zip(mangled, demangled)
+               if dm.split(" ", 2)[1] in "dDbB" and dm.split(" ", 2)[2] in stubs]
+    missing = [h for h in handles if h not in device]
+    if missing or not handles:
+        raise RuntimeError(f"{os.path.basename(obj)}: host kernels without a device kernel of the same "
+                           f"name: {missing or 'no kernels found'}")
+    return len(handles)
+
+
 def build(verbose=False, resource_usage=False):
     """Compile every HIP source for gfx950 and link libtsp.so. Returns the library path."""
     hipcc = _hipcc()
@@ -71,6 +110,9 @@ def build(verbose=False, resource_usage=False):
     for _, out in results:
         if out.strip() and (verbose or resource_usage):
             print(out)
+    for obj, _ in results:
+        if os.path.basename(obj) != "tsp_api.o":  # the API file launches no kernels itself
+            check_kernel_names(obj)
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]], verbose)
     os.replace(tmp, LIB)

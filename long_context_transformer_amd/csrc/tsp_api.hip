@@ -1,9 +1,13 @@
 // tsp_api.hip -- the C ABI declared in include/tsp.h: argument checks on the host,
 // workspace carving, and the launch sequence of one TSP rank's layer on the caller's
-// stream. The library allocates nothing and keeps no state between calls.
+// stream. The library allocates nothing and keeps no state between calls, except for the
+// opt-in phase timing hook (tsp_timing_start / tsp_timing_read) used by measurements.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+
+#include <mutex>
+#include <vector>
 
 #include "tsp.h"
 #include "tsp_device.h"
@@ -38,12 +42,13 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 constexpr int64_t kMaxI32 = 2147483647;
 
 // Checks shared by every entry point that knows (B, S, D, rank): S % 2D == 0, rank
-// in range, and local-row counts that fit the kernels' 32-bit row indices.
+// in range, and local-row counts that fit the kernels' 32-bit row indices. B = 0 or S = 0
+// is a valid empty problem (callers return before touching any pointer).
 int check_fold(int64_t B, int64_t S, int64_t D, int64_t rank) {
-  if (B < 1) return fail(TSP_ERR_SHAPE, "batch must be >= 1 (got %lld)", (long long)B);
+  if (B < 0) return fail(TSP_ERR_SHAPE, "batch must be >= 0 (got %lld)", (long long)B);
   if (D < 1) return fail(TSP_ERR_SHAPE, "fold D must be >= 1 (got %lld)", (long long)D);
-  if (S < 1 || S % (2 * D) != 0)
-    return fail(TSP_ERR_SHAPE, "seq_len S=%lld must be a positive multiple of 2D=%lld", (long long)S,
+  if (S < 0 || S % (2 * D) != 0)
+    return fail(TSP_ERR_SHAPE, "seq_len S=%lld must be a non-negative multiple of 2D=%lld", (long long)S,
                 (long long)(2 * D));
   if (rank < 0 || rank >= D) return fail(TSP_ERR_RANK, "rank %lld outside [0, %lld)", (long long)rank, (long long)D);
   if (B * (S / D) > kMaxI32 / 4) return fail(TSP_ERR_UNSUPPORTED, "B*S/D too large for 32-bit row indices");
@@ -57,6 +62,25 @@ int check_heads(int64_t H, int64_t hd) {
   return TSP_OK;
 }
 
+// Phase timing hook: events of armed tsp_layer_fwd calls, kPhases + 1 per call.
+constexpr int kPhases = 4;  // QKV, attention, W_O, MLP
+std::mutex g_tm_mu;
+std::vector<hipEvent_t> g_tm_ev;
+int g_tm_cap = 0, g_tm_used = 0;
+
+void timing_destroy() {
+  for (hipEvent_t e : g_tm_ev) (void)hipEventDestroy(e);
+  g_tm_ev.clear();
+  g_tm_cap = g_tm_used = 0;
+}
+
+// Events for the next armed call (kPhases + 1 of them), or nullptr when not armed.
+hipEvent_t* timing_slot() {
+  std::lock_guard<std::mutex> lk(g_tm_mu);
+  if (g_tm_used >= g_tm_cap) return nullptr;
+  return &g_tm_ev[(size_t)(g_tm_used++) * (kPhases + 1)];
+}
+
 size_t mlp_ws_bytes(int64_t M, int64_t Fs) { return round_up((size_t)M * (size_t)round_up((size_t)Fs, 8) * 2, kAlign); }
 
 }  // namespace
@@ -65,13 +89,50 @@ extern "C" {
 
 int tsp_version(void) { return (1 << 16) | 0; }
 
+int tsp_timing_start(int32_t max_calls) {
+  std::lock_guard<std::mutex> lk(g_tm_mu);
+  timing_destroy();
+  if (max_calls < 0) return fail(TSP_ERR_SHAPE, "max_calls must be >= 0");
+  if (max_calls == 0) return ok();
+  g_tm_ev.resize((size_t)max_calls * (kPhases + 1));
+  for (size_t i = 0; i < g_tm_ev.size(); ++i) {
+    hipError_t e = hipEventCreate(&g_tm_ev[i]);
+    if (e != hipSuccess) {
+      g_tm_ev.resize(i);
+      timing_destroy();
+      return hip_status(e, "hipEventCreate");
+    }
+  }
+  g_tm_cap = max_calls;
+  return ok();
+}
+
+int tsp_timing_read(float* ms, int32_t max_calls, int32_t* n_calls) {
+  if (!n_calls || (max_calls > 0 && !ms)) return fail(TSP_ERR_NULL, "ms and n_calls must be non-NULL");
+  std::lock_guard<std::mutex> lk(g_tm_mu);
+  const int n = g_tm_used < max_calls ? g_tm_used : (max_calls > 0 ? max_calls : 0);
+  *n_calls = n;
+  int rc = TSP_OK;
+  if (g_tm_used > 0) {
+    rc = hip_status(hipEventSynchronize(g_tm_ev[(size_t)g_tm_used * (kPhases + 1) - 1]), "hipEventSynchronize");
+  }
+  for (int i = 0; i < n && rc == TSP_OK; ++i)
+    for (int p = 0; p < kPhases && rc == TSP_OK; ++p)
+      rc = hip_status(hipEventElapsedTime(&ms[i * kPhases + p], g_tm_ev[(size_t)i * (kPhases + 1) + p],
+                                          g_tm_ev[(size_t)i * (kPhases + 1) + p + 1]),
+                      "hipEventElapsedTime");
+  timing_destroy();
+  return rc == TSP_OK ? ok() : rc;
+}
+
 const char* tsp_last_error(void) { return g_err; }
 
 int tsp_zigzag_index(int64_t S, int32_t D, int32_t rank, int64_t* idx_out, int64_t idx_len) {
-  if (!idx_out) return fail(TSP_ERR_NULL, "idx_out is NULL");
   if (int rc = check_fold(1, S, D, rank)) return rc;
   if (idx_len != S / D)
     return fail(TSP_ERR_SHAPE, "idx_len %lld != S/D = %lld", (long long)idx_len, (long long)(S / D));
+  if (S == 0) return ok();
+  if (!idx_out) return fail(TSP_ERR_NULL, "idx_out is NULL");
   const int64_t C = S / (2 * (int64_t)D);
   for (int64_t i = 0; i < 2 * C; ++i) idx_out[i] = tsp::zigzag_pos(i, C, rank, D);
   return ok();
@@ -79,9 +140,10 @@ int tsp_zigzag_index(int64_t S, int32_t D, int32_t rank, int64_t* idx_out, int64
 
 int tsp_qkv_fwd(const void* x, const void* w_qkv, void* q_out, void* k_full, void* v_full, int32_t B, int64_t S,
                 int32_t D, int32_t rank, int32_t n_heads, int32_t head_dim, tsp_stream_t stream) {
-  if (!x || !w_qkv || !k_full || !v_full) return fail(TSP_ERR_NULL, "x, w_qkv, k_full and v_full must be non-NULL");
   if (int rc = check_fold(B, S, D, rank)) return rc;
   if (int rc = check_heads(n_heads, head_dim)) return rc;
+  if (B == 0 || S == 0) return ok();
+  if (!x || !w_qkv || !k_full || !v_full) return fail(TSP_ERR_NULL, "x, w_qkv, k_full and v_full must be non-NULL");
   if (misaligned(x) || misaligned(w_qkv) || misaligned(k_full) || misaligned(v_full) || misaligned(q_out))
     return fail(TSP_ERR_ALIGN, "device pointers must be 16-byte aligned");
   const int d = n_heads * head_dim;
@@ -94,13 +156,14 @@ int tsp_qkv_fwd(const void* x, const void* w_qkv, void* q_out, void* k_full, voi
 
 int tsp_attn_fwd(const void* q, const void* k_full, const void* v_full, void* o, float* lse, int32_t B, int64_t S,
                  int32_t D, int32_t rank, int32_t n_heads, int32_t head_dim, float scale, tsp_stream_t stream) {
-  if (!q || !k_full || !v_full || !o) return fail(TSP_ERR_NULL, "q, k_full, v_full and o must be non-NULL");
   if (int rc = check_fold(B, S, D, rank)) return rc;
   if (int rc = check_heads(n_heads, head_dim)) return rc;
+  if (!(scale == scale) || isinf(scale)) return fail(TSP_ERR_SHAPE, "scale must be finite");
+  if (B == 0 || S == 0) return ok();
+  if (!q || !k_full || !v_full || !o) return fail(TSP_ERR_NULL, "q, k_full, v_full and o must be non-NULL");
   if (misaligned(q) || misaligned(k_full) || misaligned(v_full) || misaligned(o) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(TSP_ERR_ALIGN, "q/k/v/o must be 16-byte aligned and lse 4-byte aligned");
-  if (!(scale == scale) || isinf(scale)) return fail(TSP_ERR_SHAPE, "scale must be finite");
   if (int rc = hip_status(tsp::launch_attn(q, k_full, v_full, o, lse, B, S, D, rank, n_heads, head_dim, scale,
                                            static_cast<hipStream_t>(stream)),
                           "attention launch"))
@@ -109,18 +172,19 @@ int tsp_attn_fwd(const void* q, const void* k_full, const void* v_full, void* o,
 }
 
 size_t tsp_mlp_workspace_size(int64_t M, int32_t Fs) {
-  if (M < 1 || Fs < 1) return 0;
+  if (M < 0 || Fs < 1) return 0;
   return mlp_ws_bytes(M, Fs);
 }
 
 int tsp_mlp_shard_accum(const void* x, const void* w1_j, const void* w3_j, const void* w2_j, int64_t ld_w2, float* acc,
                         int64_t M, int32_t d, int32_t Fs, int32_t accumulate, void* ws, size_t ws_bytes,
                         tsp_stream_t stream) {
-  if (!x || !w1_j || !w3_j || !w2_j || !acc || !ws)
-    return fail(TSP_ERR_NULL, "x, w1_j, w3_j, w2_j, acc and ws must be non-NULL");
-  if (M < 1 || d < 1 || Fs < 1) return fail(TSP_ERR_SHAPE, "M, d and Fs must be >= 1");
+  if (M < 0 || d < 1 || Fs < 1) return fail(TSP_ERR_SHAPE, "M must be >= 0, d and Fs >= 1");
   if (M > kMaxI32 / 4) return fail(TSP_ERR_UNSUPPORTED, "M too large for 32-bit row indices");
   if (ld_w2 < Fs) return fail(TSP_ERR_SHAPE, "ld_w2 %lld < Fs %d", (long long)ld_w2, Fs);
+  if (M == 0) return ok();
+  if (!x || !w1_j || !w3_j || !w2_j || !acc || !ws)
+    return fail(TSP_ERR_NULL, "x, w1_j, w3_j, w2_j, acc and ws must be non-NULL");
   if (misaligned(x) || misaligned(w1_j) || misaligned(w3_j) || misaligned(w2_j) || misaligned(acc) || misaligned(ws))
     return fail(TSP_ERR_ALIGN, "device pointers must be 16-byte aligned");
   if (ws_bytes < mlp_ws_bytes(M, Fs))
@@ -164,7 +228,8 @@ LayerCarve carve(const tsp_layer_desc* d) {
   c.q_off = 0;
   c.o_off = act;
   c.h_off = 2 * act;
-  c.total = 2 * act + mlp_ws_bytes((int64_t)M, d->ffn / d->fold);
+  // Gated hidden of all D shards: [M, D * round_up(F/D, 8)] bf16.
+  c.total = 2 * act + mlp_ws_bytes((int64_t)M, (int64_t)d->fold * round_up((size_t)(d->ffn / d->fold), 8));
   return c;
 }
 
@@ -179,6 +244,7 @@ int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const void* w
                   const void* const* w1, const void* const* w3, const void* const* w2, void* k_full, void* v_full,
                   void* attn_out, float* mlp_out, void* ws, size_t ws_bytes, tsp_stream_t stream) {
   if (int rc = check_desc(desc)) return rc;
+  if (desc->batch == 0 || desc->seq_len == 0) return ok();
   if (!x_shard || !w_qkv || !w_o || !w1 || !w3 || !w2 || !k_full || !v_full || !attn_out || !mlp_out || !ws)
     return fail(TSP_ERR_NULL, "a required pointer is NULL");
   const int D = desc->fold;
@@ -199,26 +265,48 @@ int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const void* w
   const int M = (int)(B * (S / D));
   const int Fs = desc->ffn / D;
   const int64_t ldw2 = desc->w2_ld ? desc->w2_ld : Fs;
-  const int64_t ldh = (int64_t)round_up((size_t)Fs, 8);
+  const int64_t ldseg = (int64_t)round_up((size_t)Fs, 8);  // H columns per shard block
+  const int64_t ldh = ldseg * D;
   char* base = static_cast<char*>(ws);
   void* q = base + c.q_off;
   void* o = base + c.o_off;
   void* hbuf = base + c.h_off;
+  hipEvent_t* tm = timing_slot();
+  auto mark = [&](int p) -> int { return tm ? hip_status(hipEventRecord(tm[p], s), "hipEventRecord") : TSP_OK; };
 
+  if (int rc = mark(0)) return rc;
   if (int rc = hip_status(tsp::launch_qkv(x_shard, w_qkv, q, k_full, v_full, B, S, D, r, d, s), "qkv launch"))
     return rc;
+  if (int rc = mark(1)) return rc;
   if (int rc = hip_status(tsp::launch_attn(q, k_full, v_full, o, nullptr, B, S, D, r, H, hd, desc->scale, s),
                           "attention launch"))
     return rc;
+  if (int rc = mark(2)) return rc;
   if (int rc = hip_status(tsp::launch_proj_bf16(o, d, w_o, d, attn_out, d, M, d, d, s), "W_O launch")) return rc;
+  if (int rc = mark(3)) return rc;
+  // All D shards are resident here, so the ring runs as two launches: the gated hidden of
+  // every shard, then one down projection whose reduction visits the shards in ring order
+  // with the fp32 sums held in registers (stored once, no read-modify-write per shard).
+  if (tsp::mlp_ring_fusable(w1, w3, w2, ldw2, D, M, d, Fs, ldh)) {
+    if (int rc = hip_status(tsp::launch_gate_up_ring(attn_out, w1, w3, D, hbuf, ldh, ldseg, M, Fs, d, s),
+                            "gate/up launch"))
+      return rc;
+    if (int rc = hip_status(tsp::launch_down_ring(hbuf, ldh, ldseg, w2, ldw2, D, r, mlp_out, d, M, d, Fs, s),
+                            "down projection launch"))
+      return rc;
+    if (int rc = mark(4)) return rc;
+    return ok();
+  }
   for (int t = 0; t < D; ++t) {
     const int j = ((r - t) % D + D) % D;  // shard held at ring step t
-    if (int rc = hip_status(tsp::launch_gate_up(attn_out, d, w1[j], w3[j], d, hbuf, ldh, M, Fs, d, s), "gate/up launch"))
+    if (int rc = hip_status(tsp::launch_gate_up(attn_out, d, w1[j], w3[j], d, hbuf, ldseg, M, Fs, d, s),
+                            "gate/up launch"))
       return rc;
-    if (int rc = hip_status(tsp::launch_down_acc(hbuf, ldh, w2[j], ldw2, mlp_out, d, M, d, Fs, t > 0 ? 1 : 0, s),
+    if (int rc = hip_status(tsp::launch_down_acc(hbuf, ldseg, w2[j], ldw2, mlp_out, d, M, d, Fs, t > 0 ? 1 : 0, s),
                             "down projection launch"))
       return rc;
   }
+  if (int rc = mark(4)) return rc;
   return ok();
 }
 

@@ -109,6 +109,7 @@ struct EpiQKV {
 struct EpiSwiGLU {
   bf16_t* h;
   int64_t ldh;
+  __device__ __forceinline__ void shift_cols(int64_t c) { h += c; }
   __device__ __forceinline__ static float silu(float g) { return g / (1.0f + __expf(-g)); }
   __device__ __forceinline__ void operator()(int m, int n, const f32x4& g, const f32x4& u, int M,
                                              int N) const {
@@ -272,9 +273,41 @@ constexpr int FBK = 32;
 // Zeros read in place of chunks past K (16 bytes per lane). Never written.
 __device__ __attribute__((aligned(16))) uint4 kZeroChunks[64];
 
-template <int BM, int BN, int WM, int WN, bool DUAL, class Epi>
+// Shard tables of the fused MLP launches, which cover all D weight shards a rank sees in
+// one launch each (passed by value in the kernel arguments).
+//   SEG_N (gate/up): the column tiles are grouped by shard; a tile of shard j multiplies by
+//     W1_j / W3_j (b[j], b2[j]; N = rows of one shard) and stores into column block j of H.
+//   SEG_K (down): the reduction runs over the shards one after another in ring order, the
+//     fp32 accumulators staying in registers; at ring step t the A columns start at a_col[t]
+//     and the weight is b[t] (K = columns of one shard, zero-filled past K per shard).
+// (Plain int constants and a named trait: an unnamed enum or std::conditional in a kernel's
+// signature can mangle differently in the host and device compilations.)
+constexpr int SEG_NONE = 0, SEG_N = 1, SEG_K = 2;
+constexpr int kMaxShards = 32;
+struct NoShards {};
+struct Shards {
+  const bf16_t* b[kMaxShards];
+  const bf16_t* b2[kMaxShards];
+  int64_t a_col[kMaxShards];
+  int64_t out_col;  // SEG_N: columns between the output blocks of consecutive shards
+  int tn;           // SEG_N: column tiles per shard
+  int nks;          // SEG_K: 32-wide k stages per shard
+  int count;        // number of shards
+};
+template <int SEG>
+struct SegArgOf {
+  typedef Shards type;
+};
+template <>
+struct SegArgOf<SEG_NONE> {
+  typedef NoShards type;
+};
+template <int SEG>
+using SegArg = typename SegArgOf<SEG>::type;
+
+template <int BM, int BN, int WM, int WN, bool DUAL, int SEG, class Epi>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n) {
+void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
   constexpr int NWN = BN / WN, NWAVE = (BM / WM) * NWN;
   constexpr int NB = DUAL ? 2 : 1;
   constexpr int MI = WM / 32, NI = WN / 32;
@@ -301,7 +334,18 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n) {
   const int gsz = min(tiles_m - first_m, kGroupM);
   const int in_g = t - (t / span) * span;
   const int m0 = (first_m + in_g % gsz) * BM;
-  const int n0 = (in_g / gsz) * BN;
+  int n0 = (in_g / gsz) * BN;
+  const char* abase = reinterpret_cast<const char*>(op.a);
+  const char* bbase = reinterpret_cast<const char*>(op.b);
+  const char* b2base = reinterpret_cast<const char*>(DUAL ? op.b2 : op.b);
+  if constexpr (SEG == SEG_N) {
+    const int nt = in_g / gsz;
+    const int j = nt / sg.tn;
+    n0 = (nt - j * sg.tn) * BN;
+    bbase = reinterpret_cast<const char*>(sg.b[j]);
+    b2base = reinterpret_cast<const char*>(sg.b2[j]);
+    epi.shift_cols(j * sg.out_col);
+  }
 
   // DMA instruction p of this wave covers tile rows 16 (p NWAVE + wave) + lane/4, physical
   // chunk lane%4, i.e. logical chunk (lane%4) ^ ((row/4)%4).
@@ -321,13 +365,24 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n) {
     boff[p] = (uint32_t)min(n0 + row, op.N - 1) * (uint32_t)(op.ldb * 2) + 16 * c;
     bkc[p] = 8 * c;
   }
-  const char* abase = reinterpret_cast<const char*>(op.a);
-  const char* bbase = reinterpret_cast<const char*>(op.b);
-  const char* b2base = reinterpret_cast<const char*>(DUAL ? op.b2 : op.b);
+  // Stages are issued strictly in order; under SEG_K (seg, kk) is the shard step and the
+  // stage within it of the next one.
+  int seg = 0, kk = 0;
   auto issue = [&] __device__(char* st, int kt) {
+    const char* ab = abase;
+    const char* bb = bbase;
+    if constexpr (SEG == SEG_K) {
+      ab += sg.a_col[seg] * 2;
+      bb = reinterpret_cast<const char*>(sg.b[seg]);
+      kt = kk;
+      if (++kk == sg.nks) {
+        kk = 0;
+        ++seg;
+      }
+    }
     const int k0 = kt * FBK;
-    const char* ab = abase + (size_t)k0 * 2;
-    const char* bb = bbase + (size_t)k0 * 2;
+    ab += (size_t)k0 * 2;
+    bb += (size_t)k0 * 2;
     const char* b2 = b2base + (size_t)k0 * 2;
     const uint32_t la = lds_addr(st) + wave * 1024;
     if (k0 + FBK <= op.K) {
@@ -390,7 +445,8 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n) {
     }
   };
 
-  const int nk = (op.K + FBK - 1) / FBK;
+  int nk = (op.K + FBK - 1) / FBK;
+  if constexpr (SEG == SEG_K) nk = sg.count * sg.nks;
   issue(s0, 0);
   if (nk > 1) issue(s1, 1);
   // Stage kt: wait for its loads (stage kt+1 may stay in flight), barrier, refill the buffer
@@ -446,12 +502,18 @@ hipError_t run_tiles(const Operands& op, const Epi& epi, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, bool DUAL, class Epi>
-hipError_t run_fast(const Operands& op, const Epi& epi, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, bool DUAL, int SEG = SEG_NONE, class Epi>
+hipError_t run_fast(const Operands& op, const Epi& epi, hipStream_t s, SegArg<SEG> sg = {}) {
   const int tm = (op.M + BM - 1) / BM;
-  const int tn = (op.N + BN - 1) / BN;
+  int tn = (op.N + BN - 1) / BN;
+  if constexpr (SEG == SEG_N) {
+    sg.tn = tn;
+    tn *= sg.count;
+  }
+  if constexpr (SEG == SEG_K) sg.nks = (op.K + FBK - 1) / FBK;
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  hipLaunchKernelGGL((gemm_fast<BM, BN, WM, WN, DUAL, Epi>), dim3(tm * tn), dim3(threads), 0, s, op, epi, tm, tn);
+  hipLaunchKernelGGL((gemm_fast<BM, BN, WM, WN, DUAL, SEG, Epi>), dim3(tm * tn), dim3(threads), 0, s, op, epi, tm,
+                     tn, sg);
   return hipGetLastError();
 }
 
@@ -526,6 +588,53 @@ hipError_t launch_down_acc(const void* h, int64_t ldh, const void* w2, int64_t l
   Operands op{static_cast<const bf16_t*>(h), ldh, static_cast<const bf16_t*>(w2), nullptr, ldw2, M, N, K};
   EpiAcc epi{acc, ldacc, accumulate};
   return run_single(op, epi, stream);
+}
+
+bool mlp_ring_fusable(const void* const* w1, const void* const* w3, const void* const* w2, int64_t ldw2, int D, int M,
+                      int d, int Fs, int64_t ldh) {
+  if (D < 1 || D > kMaxShards || Fs % 8 != 0 || d % 8 != 0 || ldw2 % 8 != 0 || ldh % 8 != 0) return false;
+  for (int j = 0; j < D; ++j)
+    if (!aligned16(w1[j]) || !aligned16(w3[j]) || !aligned16(w2[j])) return false;
+  const uint64_t h_span = (uint64_t)(M - 1) * (uint64_t)ldh * 2 + (uint64_t)ldh * 2;
+  const uint64_t w13_span = (uint64_t)Fs * (uint64_t)d * 2;
+  const uint64_t w2_span = (uint64_t)(d - 1) * (uint64_t)ldw2 * 2 + (uint64_t)Fs * 2;
+  const uint64_t x_span = (uint64_t)M * (uint64_t)d * 2;
+  return h_span < (1ull << 32) && w13_span < (1ull << 32) && w2_span < (1ull << 32) && x_span < (1ull << 32);
+}
+
+hipError_t launch_gate_up_ring(const void* x, const void* const* w1, const void* const* w3, int D, void* h,
+                               int64_t ldh, int64_t ldseg, int M, int Fs, int d, hipStream_t stream) {
+  Operands op{static_cast<const bf16_t*>(x), d, nullptr, nullptr, d, M, Fs, d};
+  EpiSwiGLU epi{static_cast<bf16_t*>(h), ldh};
+  Shards sg{};
+  for (int j = 0; j < D; ++j) {
+    sg.b[j] = static_cast<const bf16_t*>(w1[j]);
+    sg.b2[j] = static_cast<const bf16_t*>(w3[j]);
+  }
+  sg.out_col = ldseg;
+  sg.count = D;
+  op.b = sg.b[0];
+  op.b2 = sg.b2[0];
+  const int64_t big = (int64_t)((M + 255) / 256) * D * ((Fs + 127) / 128);
+  if (big >= kBigTileMin) return run_fast<256, 128, 128, 32, true, SEG_N>(op, epi, stream, sg);
+  return run_fast<128, 64, 64, 32, true, SEG_N>(op, epi, stream, sg);
+}
+
+hipError_t launch_down_ring(const void* h, int64_t ldh, int64_t ldseg, const void* const* w2, int64_t ldw2, int D,
+                            int rank, float* out, int64_t ldout, int M, int N, int Fs, hipStream_t stream) {
+  Operands op{static_cast<const bf16_t*>(h), ldh, nullptr, nullptr, ldw2, M, N, Fs};
+  EpiAcc epi{out, ldout, 0};
+  Shards sg{};
+  for (int t = 0; t < D; ++t) {
+    const int j = ((rank - t) % D + D) % D;  // shard held at ring step t
+    sg.b[t] = static_cast<const bf16_t*>(w2[j]);
+    sg.a_col[t] = (int64_t)j * ldseg;
+  }
+  sg.count = D;
+  op.b = sg.b[0];
+  const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  if (big >= kBigTileMin) return run_fast<256, 256, 128, 64, false, SEG_K>(op, epi, stream, sg);
+  return run_fast<128, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
 }
 
 }  // namespace tsp

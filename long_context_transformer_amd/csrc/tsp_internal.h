@@ -25,6 +25,19 @@ hipError_t launch_gate_up(const void* x, int64_t ldx, const void* w1, const void
 hipError_t launch_down_acc(const void* h, int64_t ldh, const void* w2, int64_t ldw2, float* acc,
                            int64_t ldacc, int M, int N, int K, int accumulate, hipStream_t stream);
 
+// The D-shard MLP ring of one rank in two launches (all shards resident on the device).
+// mlp_ring_fusable: whether the shard operands suit them (at most 32 shards, 16-byte chunks,
+// 32-bit row offsets); otherwise the caller loops over launch_gate_up / launch_down_acc.
+bool mlp_ring_fusable(const void* const* w1, const void* const* w3, const void* const* w2, int64_t ldw2, int D,
+                      int M, int d, int Fs, int64_t ldh);
+// H[:, j*ldseg + n] = silu(X W1_j^T) * (X W3_j^T) for every shard j and n < Fs.
+hipError_t launch_gate_up_ring(const void* x, const void* const* w1, const void* const* w3, int D, void* h,
+                               int64_t ldh, int64_t ldseg, int M, int Fs, int d, hipStream_t stream);
+// out[M, N] = sum over ring steps t = 0..D-1 (shard j = (rank - t) mod D, in that order) of
+// H[:, j*ldseg : j*ldseg + Fs] W2_j^T, the fp32 sum held in registers and stored once.
+hipError_t launch_down_ring(const void* h, int64_t ldh, int64_t ldseg, const void* const* w2, int64_t ldw2, int D,
+                            int rank, float* out, int64_t ldout, int M, int N, int Fs, hipStream_t stream);
+
 // Causal attention of the rank's queries against full-sequence K/V (step a3).
 hipError_t launch_attn(const void* q, const void* k_full, const void* v_full, void* o, float* lse,
                        int B, int64_t S, int D, int rank, int H, int hd, float scale,

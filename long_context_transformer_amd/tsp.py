@@ -52,6 +52,8 @@ _SIGS = {
     "tsp_layer_fwd": (_I32, [ctypes.POINTER(LayerDesc), _VP, _VP, _VP, ctypes.POINTER(_VP),
                              ctypes.POINTER(_VP), ctypes.POINTER(_VP), _VP, _VP, _VP, _VP, _VP,
                              ctypes.c_size_t, _VP]),
+    "tsp_timing_start": (_I32, [_I32]),
+    "tsp_timing_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32, ctypes.POINTER(_I32)]),
 }
 
 _lib = None
@@ -158,3 +160,19 @@ def layer_fwd(desc, x_shard, w_qkv, w_o, w1, w3, w2, k_full, v_full, attn_out, m
     _check(load().tsp_layer_fwd(ctypes.byref(desc), _ptr(x_shard), _ptr(w_qkv), _ptr(w_o), a1, a3, a2,
                                 _ptr(k_full), _ptr(v_full), _ptr(attn_out), _ptr(mlp_out), _ptr(ws),
                                 ws_bytes, _stream(stream, x_shard)))
+
+
+PHASES = ("qkv", "attention", "w_o", "mlp")
+
+
+def timing_start(max_calls):
+    """Arm the library's phase timing for the next `max_calls` layer_fwd calls."""
+    _check(load().tsp_timing_start(int(max_calls)))
+
+
+def timing_read(max_calls):
+    """Per-call phase durations (ms) of the armed calls: list of dicts keyed by PHASES."""
+    buf = (ctypes.c_float * (4 * max(int(max_calls), 1)))()
+    n = _I32(0)
+    _check(load().tsp_timing_read(buf, int(max_calls), ctypes.byref(n)))
+    return [{p: float(buf[4 * i + k]) for k, p in enumerate(PHASES)} for i in range(n.value)]

@@ -77,7 +77,7 @@ def test_attn_errors():
     f = tsp.attn_fwd
     assert _code(f, None, A, A, A, None, 1, 256, 4, 0, 4, 64, 0.0, 0) == 1
     assert _code(f, A, A, A, A, None, 1, 250, 4, 0, 4, 64, 0.0, 0) == 2
-    assert _code(f, A, A, A, A, None, 0, 256, 4, 0, 4, 64, 0.0, 0) == 2
+    assert _code(f, A, A, A, A, None, -1, 256, 4, 0, 4, 64, 0.0, 0) == 2
     assert _code(f, A, A, A, A, None, 1, 256, 4, 5, 4, 64, 0.0, 0) == 3
     assert _code(f, A, A, A, A, None, 1, 256, 4, 0, 4, 96, 0.0, 0) == 4
     assert _code(f, A, MIS, A, A, None, 1, 256, 4, 0, 4, 64, 0.0, 0) == 6
@@ -99,7 +99,8 @@ def test_mlp_errors():
     assert need >= 64 * 176 * 2
     assert _code(f, A, A, A, None, 172, A, 64, 256, 172, 0, A, need, 0) == 1
     assert _code(f, A, A, A, A, 171, A, 64, 256, 172, 0, A, need, 0) == 2
-    assert _code(f, A, A, A, A, 172, A, 0, 256, 172, 0, A, need, 0) == 2
+    assert _code(f, A, A, A, A, 172, A, -1, 256, 172, 0, A, need, 0) == 2
+    assert _code(f, A, A, A, A, 172, A, 64, 256, 0, 0, A, need, 0) == 2
     assert _code(f, A, A, A, A, 172, MIS, 64, 256, 172, 0, A, need, 0) == 6
     assert _code(f, A, A, A, A, 172, A, 64, 256, 172, 0, A, need - 1, 0) == 5
     assert tsp.mlp_workspace_size(0, 172) == 0
@@ -138,6 +139,38 @@ def test_layer_errors():
     bad = _desc()
     bad.reserved = 1
     assert _code(f, bad, A, A, A, sh, sh, sh, A, A, A, A, A, ws, 0) == 2
+
+
+def test_empty_problems_are_noops():
+    """B = 0, S = 0 or M = 0: shape checks still apply, then TSP_OK with no pointer read
+    (NULL pointers, as torch gives for empty tensors) and no launch (none can happen here:
+    there is no GPU)."""
+    lib = tsp.load()
+    assert lib.tsp_zigzag_index(0, 4, 1, None, 0) == 0
+    assert lib.tsp_zigzag_index(0, 4, 4, None, 0) == 3
+    assert tsp.zigzag_index(0, 4, 1).shape == (0,)
+    tsp.attn_fwd(None, None, None, None, None, 0, 256, 4, 0, 4, 64)
+    tsp.attn_fwd(None, None, None, None, None, 2, 0, 4, 3, 4, 64)
+    assert _code(tsp.attn_fwd, None, None, None, None, None, 0, 250, 4, 0, 4, 64, 0.0, 0) == 2
+    assert _code(tsp.attn_fwd, None, None, None, None, None, 0, 256, 4, 0, 4, 80, 0.0, 0) == 4
+    tsp.qkv_fwd(None, None, None, None, None, 0, 256, 4, 0, 4, 64)
+    tsp.mlp_shard_accum(None, None, None, None, 172, None, 0, 256, 172, 0, None, 0)
+    empty = _desc(B=0)
+    assert tsp.layer_workspace_size(empty) == 0
+    tsp.layer_fwd(empty, None, None, None, [None] * 4, [None] * 4, [None] * 4, None, None, None,
+                  None, None, 0)
+    assert _code(tsp.layer_fwd, _desc(B=0, rank=4), None, None, None, [None] * 4, [None] * 4,
+                 [None] * 4, None, None, None, None, None, 0, 0) == 3
+
+
+def test_timing_hook_errors():
+    lib = tsp.load()
+    n = ctypes.c_int32(5)
+    assert lib.tsp_timing_start(-1) == 2
+    assert lib.tsp_timing_start(0) == 0
+    assert lib.tsp_timing_read(None, 4, ctypes.byref(n)) == 1
+    assert lib.tsp_timing_read(None, 0, None) == 1
+    assert lib.tsp_timing_read(None, 0, ctypes.byref(n)) == 0 and n.value == 0
 
 
 def test_binding_rejects_host_tensors():

@@ -190,7 +190,11 @@ def test_mlp_ring_sum_equals_unsharded():
 
 # ---------------------------------------------------------------------------- the layer
 def run_layer(w, inputs, rank, w2_view=False):
-    """Upload inputs, emulate the K/V all-gather for the peers, run tsp_layer_fwd."""
+    """Upload inputs, emulate the K/V all-gather for the peers, run tsp_layer_fwd.
+
+    w2_view: False (W1/W3 shards are row blocks of one tensor, W2 shards contiguous
+    copies), True (W2 shards are column views of the full W2, row stride F), or
+    "separate" (every shard of W1/W3/W2 its own allocation, made in reverse shard order)."""
     B, S, D, H, hd, d, F = w.B, w.S, w.D, w.n_heads, w.head_dim, w.d_model, w.ffn
     Fs = F // D
     x_full = dev_bf16(inputs["x_full"])
@@ -198,7 +202,14 @@ def run_layer(w, inputs, rank, w2_view=False):
     w1, w3, w2 = dev_bf16(inputs["w1"]), dev_bf16(inputs["w3"]), dev_bf16(inputs["w2"])
     w1s = [w1[j * Fs:(j + 1) * Fs] for j in range(D)]
     w3s = [w3[j * Fs:(j + 1) * Fs] for j in range(D)]
-    if w2_view:
+    if w2_view == "separate":
+        order = list(range(D))[::-1]
+        sep = {j: (w1s[j].clone(), w3s[j].clone(), w2[:, j * Fs:(j + 1) * Fs].contiguous()) for j in order}
+        w1s = [sep[j][0] for j in range(D)]
+        w3s = [sep[j][1] for j in range(D)]
+        w2s = [sep[j][2] for j in range(D)]
+        w2_view = False
+    elif w2_view:
         w2s = [w2.view(-1)[j * Fs:].data_ptr() for j in range(D)]
     else:
         w2s = [w2[:, j * Fs:(j + 1) * Fs].contiguous() for j in range(D)]
@@ -239,9 +250,15 @@ def test_layer_tiny_all_ranks():
     check_close("glued mlp_out", glued_y, full["mlp_out"])
 
 
+# Fs % 8 == 0 takes the two-launch MLP ring (gated hidden of all shards, then one down
+# projection over the shards in ring order); the tiny workload (Fs = 172) takes the
+# per-shard steps.
 LAYER_MID = [  # B, S, D, rank, H, hd, F, w2_view
-    (2, 2048, 4, 1, 4, 128, 1376, False),
-    (1, 1200, 3, 2, 4, 64, 1032, True),   # C = 200, Fs = 344, W2 shards as views
+    (2, 2048, 4, 1, 4, 128, 1376, False),     # Fs = 344: 24-column k tail in every shard
+    (1, 1200, 3, 2, 4, 64, 1032, True),       # C = 200, Fs = 344, W2 shards as views
+    (1, 512, 8, 5, 8, 64, 2304, False),       # D = 8, ring wraps at rank 5, Fs = 288
+    (1, 768, 2, 1, 4, 64, 1040, "separate"),  # Fs = 520, shards in separate allocations
+    (1, 256, 4, 2, 4, 64, 696, False),        # Fs = 174: per-shard steps (Fs % 8 != 0)
 ]
 
 
@@ -256,6 +273,36 @@ def test_layer_mid(B, S, D, rank, H, hd, F, w2_view):
                        S, D, rank, H)
     check_close("attn_out", host_f64(a), ref["attn_out"])
     check_close("mlp_out", host_f64(y), ref["mlp_out"])
+
+
+def test_empty_problems_on_device():
+    """B = 0 with empty device tensors: every entry point returns OK and writes nothing."""
+    e = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    tsp.attn_fwd(e, e, e, e, None, 0, 256, 4, 1, 4, 64)
+    tsp.qkv_fwd(e, e, None, e, e, 0, 256, 4, 1, 4, 64)
+    sentinel = torch.full((4, 8), 7.0, device="cuda")
+    tsp.mlp_shard_accum(e, e, e, e, 172, sentinel, 0, 256, 172, 0, torch.empty(0, device="cuda"))
+    desc = tsp.make_desc(0, 256, 4, 1, 256, 4, 64, 688)
+    assert tsp.layer_workspace_size(desc) == 0
+    tsp.layer_fwd(desc, e, e, e, [e] * 4, [e] * 4, [e] * 4, e, e, e,
+                  torch.empty(0, device="cuda"), torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == 7.0)
+
+
+def test_phase_timing_hook():
+    """The library's phase events: armed for 2 calls, 3 calls made, 2 read back, every
+    phase positive; disarmed afterwards (a further read returns nothing)."""
+    w = synth.WORKLOADS["tiny_s256_d4"]
+    inputs = synth.layer_inputs(w)
+    run_layer(w, inputs, 1)
+    tsp.timing_start(2)
+    for _ in range(3):
+        run_layer(w, inputs, 1)
+    calls = tsp.timing_read(2)
+    assert len(calls) == 2
+    assert all(c[p] > 0 for c in calls for p in tsp.PHASES), calls
+    assert tsp.timing_read(2) == []
 
 
 def test_layer_deterministic():
