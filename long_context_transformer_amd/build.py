@@ -20,8 +20,10 @@ LIB = os.path.join(PKG, "libtsp.so")
 SOURCES = ["tsp_api.hip", "tsp_gemm.hip", "tsp_attn.hip"]
 # Per-source code generation flags. The attention kernel keeps its O accumulator and
 # scores in VGPRs (MFMA "VGPR form"); the rescale of O then stays a plain VALU multiply
-# instead of AGPR<->VGPR copies on every key block.
-SOURCE_FLAGS = {"tsp_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# instead of AGPR<->VGPR copies on every key block. It also runs with the IEEE mode bit
+# off and no NaN operands assumed (its scores are finite or -inf), so max/min need no
+# canonicalising moves.
+SOURCE_FLAGS = {"tsp_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]}
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

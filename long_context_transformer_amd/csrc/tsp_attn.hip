@@ -54,30 +54,31 @@ namespace tsp {
 namespace {
 
 // Tile shape. Each wave owns QB 32-row query blocks; a workgroup owns BR rows (NW = BR /
-// (32 QB) waves) and streams keys through LDS in stages of BC (one or two 32-key softmax
+// (32 QB) waves) and streams keys through LDS in stages of BC = 64 (two 32-key softmax
 // blocks), with a 4-stage ring.
-//   BR 256, BC 64, QB 1: 8 waves sharing one ring; two waves per SIMD, so one wave's
-//                        softmax can overlap the other's MFMAs (the default, fastest
-//                        measured at 7B S=128K).
-//   BR 128, BC 32, QB 1: 4 waves and a 64 KB ring per workgroup, two workgroups per CU.
-//   BR 256, BC 64, QB 2: one wave per SIMD; each K/V fragment feeds two query blocks.
+//   BR 256, QB 1: 8 waves sharing one ring; two waves per SIMD, so one wave's softmax can
+//                 overlap the other's MFMAs (the default, fastest measured at 7B S=128K).
+//   BR 256, QB 2: one wave per SIMD; each K/V fragment feeds two query blocks.
 #ifndef TSP_ATTN_BR
 #define TSP_ATTN_BR 256
-#endif
-#ifndef TSP_ATTN_BC
-#define TSP_ATTN_BC 64
 #endif
 #ifndef TSP_ATTN_QB
 #define TSP_ATTN_QB 1
 #endif
+// CINIT 1: Q is pre-multiplied by scale*log2(e) (rounded to bf16) and every S MFMA chain
+// starts from -m, so the MFMAs produce s*c - m directly and the softmax needs no FMA per
+// score. CINIT 0: S = K Q^T, then one FMA per score.
+#ifndef TSP_ATTN_CINIT
+#define TSP_ATTN_CINIT 1
+#endif
 constexpr int BR = TSP_ATTN_BR;
-constexpr int BC = TSP_ATTN_BC;
+constexpr int BC = 64;
 constexpr int QB = TSP_ATTN_QB;
+constexpr int RING = 4;
 constexpr int NW = BR / (32 * QB);
 constexpr int kThreads = 64 * NW;
 constexpr int kWavesPerSimd = (QB == 1) ? 2 : 1;
 constexpr float kLazy = 8.0f;     // rescale O only when the max grows by more than this (log2)
-static_assert(BC == 32 || BC == 64, "one or two 32-key blocks per stage");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -121,8 +122,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // K and V rings: stage st of K at kring + st * TILEB, of V at vring + st * TILEB. With
   // 4 stages each ring spans 64 KB, so every fragment address is a per-lane base plus an
   // immediate offset.
-  __shared__ __attribute__((aligned(1024))) char kring[4 * TILEB];
-  __shared__ __attribute__((aligned(1024))) char vring[4 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char kring[RING * TILEB];
+  __shared__ __attribute__((aligned(1024))) char vring[RING * TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -155,6 +156,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     for (int s = 0; s < KS; ++s)
       qf[qb][s] = valid ? as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s)) : bf16x8{};
   }
+#if TSP_ATTN_CINIT
+  // Q * scale * log2(e), rounded to bf16 (round to nearest even): S comes out in log2 units.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[qb][s][e] = (__bf16)((float)qf[qb][s][e] * a.scale_log2);
+#endif
 
   // ---- stage loads: global -> LDS, 16 bytes per lane, lane-linear within the 1 KB a wave
   // instruction writes. Load p of this wave covers linear chunks (NW p + wave) * 64 + lane.
@@ -224,25 +234,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     m_s[qb] = -INFINITY;
     l_run[qb] = 0.0f;
   }
+  // Every S MFMA chain starts from -m_cm (m_cm = the reference max when the chain is
+  // issued; 0 before the first block). m_at_*: m_cm of the two S buffers.
+  float m_cm[QB], m_at_cur[QB], m_at_nxt[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) m_cm[qb] = m_at_cur[qb] = m_at_nxt[qb] = 0.0f;
+  auto note = [&] __device__(float (&m_at)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_at[qb] = m_cm[qb];
+  };
   const float c2 = a.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // S^T of 32-key block kb (0/1) of a stage, both query blocks.
-  auto qk = [&] __device__(int st, int kb, f32x16 (&sacc)[QB]) {
+  // K fragments of 32-key block kb (0/1) of a stage: 16 keys per lane group, dims of step s.
+  auto load_k = [&] __device__(int st, int kb, bf16x8 (&kf)[KS]) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(kring + st * TILEB + kaddr[s] + kb * 32 * ROWB));
+  };
+  // S^T of one 32-key block from its K fragments, both query blocks.
+  auto qk = [&] __device__(const bf16x8 (&kf)[KS], f32x16 (&sacc)[QB]) {
     // The S MFMAs issue as one block of their own (no VALU interleaved) at raised wave
     // priority: with two waves per SIMD, one wave's MFMA block then runs while the other
     // wave does its softmax.
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sacc[qb] = f32x16{};
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 kf =
-          as_bf16x8(*reinterpret_cast<const uint4*>(kring + st * TILEB + kaddr[s] + kb * 32 * ROWB));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[qb] = mfma32x32x16(kf, qf[qb][s], sacc[qb]);
+      for (int r = 0; r < 16; ++r) sacc[qb][r] = TSP_ATTN_CINIT ? -m_cm[qb] : 0.0f;
+      sacc[qb] = mfma32x32x16(kf[0], qf[qb][0], sacc[qb]);
     }
+#pragma unroll
+    for (int s = 1; s < KS; ++s)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb] = mfma32x32x16(kf[s], qf[qb][s], sacc[qb]);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -253,16 +279,73 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       for (int r = 0; r < 16; ++r)
         if (kstart + 8 * (r >> 2) + 4 * hl + (r & 3) > qpos[qb]) sacc[qb][r] = -INFINITY;
   };
+#if TSP_ATTN_CINIT
+  // sacc = s*c - m_at (m_at: the reference max the block was computed against). Row max;
+  // in the rare case that the max grew by more than kLazy or the block was computed
+  // against an older reference, shift it to the current reference (and move the reference
+  // and the chain start value); then exponentials, bf16 P and their sum. Returns whether
+  // this lane needs the O rescale (then by the factors in alpha).
+  auto softmax = [&] __device__(f32x16 (&sacc)[QB], const float (&m_at)[QB], bf16x8 (&pf)[QB][2],
+                                float (&alpha)[QB]) {
+    bool any = false, need = false;
+    float mx[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float v = sacc[qb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) v = fmaxf(v, sacc[qb][r]);
+      mx[qb] = max_swap32(v);
+      const float d = m_s[qb] - m_at[qb];  // 0 unless the reference moved since the MFMAs
+      need |= (mx[qb] - d > kLazy) | (d != 0.0f);
+      alpha[qb] = 1.0f;
+    }
+    if (__ballot(need)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float d = m_s[qb] - m_at[qb];
+        const bool upd = mx[qb] - d > kLazy;
+        const float m_new = upd ? m_at[qb] + mx[qb] : m_s[qb];
+        alpha[qb] = upd ? __builtin_amdgcn_exp2f(m_s[qb] - m_new) : 1.0f;  // 0 on the first block
+        const float shift = m_new - m_at[qb];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[qb][r] -= shift;
+        l_run[qb] *= alpha[qb];
+        m_s[qb] = m_new;
+        if (upd) m_cm[qb] = m_new;
+        any |= upd;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float lsum = 0.0f;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(sacc[qb][8 * half + 2 * e]);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[qb][8 * half + 2 * e + 1]);
+          w[e] = pack_bf16x2(p0, p1);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, lsum, false);
+        }
+        pf[qb][half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+      }
+      l_run[qb] += lsum;
+    }
+    return any;
+  };
+#else
   // Row max, reference max, exponentials, bf16 P and their sum. Returns whether this lane
   // needs the O rescale (then by the factors in alpha).
-  auto softmax = [&] __device__(f32x16 (&sacc)[QB], bf16x8 (&pf)[QB][2], float (&alpha)[QB]) {
+  auto softmax = [&] __device__(f32x16 (&sacc)[QB], const float (&)[QB], bf16x8 (&pf)[QB][2],
+                                float (&alpha)[QB]) {
     bool any = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = sacc[qb][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_swap32(mx);
       const float mxs = mx * c2;
       const bool upd = mxs > m_s[qb] + kLazy;
       const float m_new = upd ? mxs : m_s[qb];
@@ -287,6 +370,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
     return any;
   };
+#endif
   // Pins P and the row sums in registers at the end of the softmax, so the exponentials
   // cannot sink below the rescale branch into the PV region.
   auto close_region = [&] __device__(const bf16x8 (&pf)[QB][2]) {
@@ -303,8 +387,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha[qb];
   };
-  // O^T += V^T P^T for 32-key block kb of a stage.
-  auto pv = [&] __device__(int st, int kb, const bf16x8 (&pf)[QB][2]) {
+  // V^T fragments of 32-key block kb of a stage (two 16-key halves x DB dim blocks), from
+  // transpose reads.
+  auto load_v = [&] __device__(int st, int kb, bf16x8 (&vf)[2][DB]) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -313,11 +398,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vr);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr + ROWB));
         const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
-        const bf16x8 vf = as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32x32x16(vf, pf[qb][half], oacc[qb][db]);
+        vf[half][db] = as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
       }
     }
+  };
+  // O^T += V^T P^T for one 32-key block.
+  auto pv = [&] __device__(const bf16x8 (&vf)[2][DB], const bf16x8 (&pf)[QB][2]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32x32x16(vf[half][db], pf[qb][half], oacc[qb][db]);
   };
 
   // Prologue: stages 0..2 in flight, wait for stage 0, first S block.
@@ -328,38 +420,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
   f32x16 s_cur[QB], s_nxt[QB];
   bf16x8 pf[QB][2];
+  bf16x8 kf[KS];     // K fragments of the next S block, read one softmax ahead
+  bf16x8 vf[2][DB];  // V^T fragments of the next PV block, read one softmax ahead
   float alpha[QB];
-  qk(0, 0, s_cur);
+  load_k(0, 0, kf);
+  qk(kf, s_cur);
+  note(m_at_cur);
+  load_k(0, 1, kf);
 
-  // Stage t: `cur` holds it, `nxt` holds stage t+1 (read ahead for its first block),
-  // `refill` is the buffer of stage t-1, reloaded with stage t+3.
+  // Stage t: `cur` holds it, `nxt` holds stage t+1 (its first block's S is computed here),
+  // `refill` is the buffer of stage t-1, reloaded with stage t+3. Every LDS read is issued
+  // one softmax before its MFMAs: the K of block 1 of stage t comes from the previous stage.
   auto body = [&] __device__(int t, int cur, int nxt, int refill) {
     sync_stage(t + 2 < n_kt ? 1 : 0);  // stage t+1 landed; stage t+2 may be in flight
     if (t + 3 < n_kt) issue(refill, t + 3);
     const int k0 = t * BC;
-    if constexpr (BC == 64) {
-      if (k0 + 31 > wmin_pos) mask(s_cur, k0);
-      qk(cur, 1, s_nxt);
-      bool any = softmax(s_cur, pf, alpha);
-      close_region(pf);
-      if (__ballot(any)) rescale(alpha);
-      pv(cur, 0, pf);
-      if (k0 + 63 > wmin_pos) mask(s_nxt, k0 + 32);
-      qk(nxt, 0, s_cur);  // after the last stage this reads a stale buffer; the result is unused
-      any = softmax(s_nxt, pf, alpha);
-      close_region(pf);
-      if (__ballot(any)) rescale(alpha);
-      pv(cur, 1, pf);
-    } else {
-      if (k0 + 31 > wmin_pos) mask(s_cur, k0);
-      qk(nxt, 0, s_nxt);  // after the last stage this reads a stale buffer; the result is unused
-      bool any = softmax(s_cur, pf, alpha);
-      close_region(pf);
-      if (__ballot(any)) rescale(alpha);
-      pv(cur, 0, pf);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s_cur[qb] = s_nxt[qb];
-    }
+    if (k0 + 31 > wmin_pos) mask(s_cur, k0);
+    qk(kf, s_nxt);  // block 1 of stage t
+    note(m_at_nxt);
+    load_v(cur, 0, vf);
+    load_k(nxt, 0, kf);  // after the last stage this reads a stale buffer; the result is unused
+    bool any = softmax(s_cur, m_at_cur, pf, alpha);
+    close_region(pf);
+    if (__ballot(any)) rescale(alpha);
+    pv(vf, pf);
+    if (k0 + 63 > wmin_pos) mask(s_nxt, k0 + 32);
+    qk(kf, s_cur);  // block 0 of stage t+1
+    note(m_at_cur);
+    load_v(cur, 1, vf);
+    load_k(nxt, 1, kf);
+    any = softmax(s_nxt, m_at_nxt, pf, alpha);
+    close_region(pf);
+    if (__ballot(any)) rescale(alpha);
+    pv(vf, pf);
   };
   // Unrolled by the ring depth so every stage buffer is named statically; guarded bodies
   // (no early exits) keep the accumulators in one register set.

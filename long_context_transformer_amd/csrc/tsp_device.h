@@ -58,7 +58,14 @@ __device__ __forceinline__ bf16_t to_bf16(float x) {
 //   dma16_sbase: address = uniform 64-bit base + per-lane 32-bit byte offset
 //   dma16_vaddr: address = per-lane 64-bit pointer
 __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds) : "memory");
+  // The base must sit in SGPRs: read it from the first lane (free when already scalar).
+  // readfirstlane returns int: each half is taken as uint32_t before widening, so the low
+  // half is zero-extended.
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  const uint64_t ps = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ps), "s"(lds) : "memory");
 }
 __device__ __forceinline__ void dma16_vaddr(const void* addr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds) : "memory");
@@ -67,6 +74,17 @@ __device__ __forceinline__ void dma16_vaddr(const void* addr, uint32_t lds) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// max(v of this lane, v of lane ^ 32) in registers (v_permlane32_swap exchanges the upper
+// half of the first operand with the lower half of the second; with both holding v, the
+// pair's max is the max across the two half-waves). Inline assembly: this compiler folds
+// a max of the intrinsic's two results to its first result. The s_nops give the wait
+// states around the permute. Inputs are finite or -inf.
+__device__ __forceinline__ float max_swap32(float v) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1" : "+v"(x), "+v"(y));
+  return __builtin_bit_cast(float, x);
 }
 
 // s_waitcnt immediate that waits until at most `vm` vector-memory loads of this wave are

@@ -12,6 +12,14 @@ from long_context_transformer_amd import synth, tsp
 MAX_REL = 2e-2
 MEAN_REL = 2e-3
 
+# The log-sum-exp output has no tolerance in the contract. The kernel forms scores from
+# Q * scale * log2(e) rounded to bf16 (relative error <= 2^-9 per element), which moves a
+# score by about 3e-3 (log2 units) at the spreads of the 7B workloads; the LSE, a smooth
+# max of the scores, carries errors of that size (about 2e-3 in natural-log units). Bounds
+# of 2e-3 (max) and 3e-4 (mean) of max|lse| (about 11 at S=128K) leave a margin of 2-3x.
+LSE_MAX_REL = 2e-3
+LSE_MEAN_REL = 3e-4
+
 BF16_NAN = 0x7FC0
 
 
