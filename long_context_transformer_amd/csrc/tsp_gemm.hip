@@ -306,7 +306,8 @@ template <int SEG>
 using SegArg = typename SegArgOf<SEG>::type;
 
 template <int BM, int BN, int WM, int WN, bool DUAL, int SEG, class Epi>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN) / 4, (BM / WM) * (BN / WN) / 4)))
 void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
   constexpr int NWN = BN / WN, NWAVE = (BM / WM) * NWN;
   constexpr int NB = DUAL ? 2 : 1;
@@ -367,17 +368,37 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
   }
   // Stages are issued strictly in order; under SEG_K (seg, kk) is the shard step and the
   // stage within it of the next one.
+  // Under SEG_K the bases of the current shard step and of the next one are kept in
+  // registers; the table is read once per shard step, a whole step before it is needed.
   int seg = 0, kk = 0;
+  const char* seg_a = abase;
+  const char* seg_b = bbase;
+  const char* nxt_a = abase;
+  const char* nxt_b = bbase;
+  if constexpr (SEG == SEG_K) {
+    seg_a = abase + sg.a_col[0] * 2;
+    seg_b = reinterpret_cast<const char*>(sg.b[0]);
+    if (sg.count > 1) {
+      nxt_a = abase + sg.a_col[1] * 2;
+      nxt_b = reinterpret_cast<const char*>(sg.b[1]);
+    }
+  }
   auto issue = [&] __device__(char* st, int kt) {
     const char* ab = abase;
     const char* bb = bbase;
     if constexpr (SEG == SEG_K) {
-      ab += sg.a_col[seg] * 2;
-      bb = reinterpret_cast<const char*>(sg.b[seg]);
+      ab = seg_a;
+      bb = seg_b;
       kt = kk;
       if (++kk == sg.nks) {
         kk = 0;
         ++seg;
+        seg_a = nxt_a;
+        seg_b = nxt_b;
+        if (seg + 1 < sg.count) {
+          nxt_a = abase + sg.a_col[seg + 1] * 2;
+          nxt_b = reinterpret_cast<const char*>(sg.b[seg + 1]);
+        }
       }
     }
     const int k0 = kt * FBK;
