@@ -46,6 +46,23 @@ def attention_row(q_row, pos, k_seq, v_seq, scale):
     return o, mx + math.log(z)
 
 
+def attention_row_range(q_row, pos, k_seq, v_seq, scale, key_lo, key_hi):
+    """One query row attending the keys j with key_lo <= j < key_hi and j <= pos.
+
+    Returns (o [hd], lse); a row that sees no key gives ([0]*hd, -inf).
+    """
+    keys = [j for j in range(key_lo, min(key_hi, pos + 1))]
+    hd = len(v_seq[0])
+    if not keys:
+        return [0.0] * hd, -math.inf
+    scores = [scale * sum(q_row[c] * k_seq[j][c] for c in range(len(q_row))) for j in keys]
+    mx = max(scores)
+    ex = [math.exp(s - mx) for s in scores]
+    z = sum(ex)
+    o = [sum(ex[t] * v_seq[j][c] for t, j in enumerate(keys)) / z for c in range(hd)]
+    return o, mx + math.log(z)
+
+
 def silu(g):
     return g / (1.0 + math.exp(-g))
 

@@ -62,6 +62,8 @@ __all__ = [
     "qkv_rows",
     "rank_layer",
     "layer_flops",
+    "attention_range",
+    "lse_merge",
 ]
 
 
@@ -142,6 +144,68 @@ def causal_attention(q, q_pos, k, v, scale=None, row_block=512):
                 o[b, r0:r1, h, :] = (e / z) @ vv
                 lse[b, h, r0:r1] = (m + np.log(z))[:, 0]
     return o, lse
+
+
+def attention_range(q, q_pos, k, v, key_lo, key_hi, scale=None, row_block=512):
+    """Causal attention restricted to the keys at positions [key_lo, key_hi).
+
+    [TSP §2, attention layers] The all-gather delivers the K/V of the sequence chunk by
+    chunk; attention over each arrived chunk, merged by log-sum-exp (lse_merge), equals
+    attention over the whole sequence. For a query at position p the visible keys are j
+    with key_lo <= j < key_hi and j <= p.
+    Returns (o [B, n, H, hd], lse [B, H, n]): the softmax-weighted mean of V over the
+    visible keys and the natural log of sum_j exp(scale * q.k_j) over them. A row that
+    sees no key gets o = 0 and lse = -inf (the neutral element of lse_merge).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    B, n, H, hd = q.shape
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(hd)
+    key_lo, key_hi = int(key_lo), int(key_hi)
+    o = np.zeros((B, n, H, hd), dtype=np.float64)
+    lse = np.full((B, H, n), -np.inf, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, n, row_block):
+                r1 = min(n, r0 + row_block)
+                pos = q_pos[r0:r1]
+                hi = min(key_hi, int(pos.max()) + 1)
+                if hi <= key_lo:
+                    continue
+                keys = np.arange(key_lo, hi, dtype=np.int64)
+                s = (q[b, r0:r1, h, :] @ k[b, key_lo:hi, h, :].T) * scale
+                visible = keys[None, :] <= pos[:, None]
+                s = np.where(visible, s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                seen = np.isfinite(m[:, 0])
+                m_safe = np.where(np.isfinite(m), m, 0.0)
+                e = np.exp(s - m_safe)
+                z = e.sum(axis=1, keepdims=True)
+                z_safe = np.where(z > 0, z, 1.0)
+                o[b, r0:r1, h, :] = np.where(seen[:, None], (e / z_safe) @ v[b, key_lo:hi, h, :], 0.0)
+                lse[b, h, r0:r1] = np.where(seen, (m_safe + np.log(z_safe))[:, 0], -np.inf)
+    return o, lse
+
+
+def lse_merge(o_a, lse_a, o_b, lse_b):
+    """Attention over the union of two disjoint key sets, from the attention over each.
+
+    With lse = log(exp(lse_a) + exp(lse_b)), the merged output is
+    exp(lse_a - lse) o_a + exp(lse_b - lse) o_b (each o a softmax-weighted mean over its
+    own keys). o: [B, n, H, hd], lse: [B, H, n]. (0, -inf) is the neutral element.
+    """
+    o_a, o_b = np.asarray(o_a, dtype=np.float64), np.asarray(o_b, dtype=np.float64)
+    lse_a, lse_b = np.asarray(lse_a, dtype=np.float64), np.asarray(lse_b, dtype=np.float64)
+    lse = np.logaddexp(lse_a, lse_b)
+    fin = np.isfinite(lse)
+    ref = np.where(fin, lse, 0.0)
+    w_a = np.where(fin, np.exp(lse_a - ref), 0.0)  # [B, H, n]
+    w_b = np.where(fin, np.exp(lse_b - ref), 0.0)
+    to_rows = lambda w: np.transpose(w, (0, 2, 1))[..., None]  # [B, n, H, 1]
+    return to_rows(w_a) * o_a + to_rows(w_b) * o_b, lse
 
 
 def silu(g):

@@ -255,11 +255,85 @@ def pin_layer_flops():
     assert O.layer_flops(1, 256, 4, 256, 4, 64, 688) == 109_608_960
 
 
+def pin_range_vs_brute():
+    """Attention over a key range equals the scalar-loop brute force: ranges that start and
+    end inside a block, cut through the query rows, or leave rows with no key at all."""
+    rng = _rng(21)
+    B, S, H, hd, D, r = 1, 40, 2, 8, 2, 1
+    idx = O.zigzag_index(S, D, r)
+    q = rng.standard_normal((B, len(idx), H, hd))
+    k = rng.standard_normal((B, S, H, hd))
+    v = rng.standard_normal((B, S, H, hd))
+    scale = 1.0 / math.sqrt(hd)
+    for lo, hi in [(0, S), (3, 17), (11, 12), (25, 40), (35, 36), (0, 0), (38, 60)]:
+        o, lse = O.attention_range(q, idx, k, v, lo, hi, row_block=7)
+        for i, p in enumerate(idx):
+            for h in range(H):
+                ob, lb = brute.attention_row_range(q[0, i, h].tolist(), int(p), k[0, :, h].tolist(),
+                                                   v[0, :, h].tolist(), scale, lo, hi)
+                np.testing.assert_allclose(o[0, i, h], ob, rtol=1e-12, atol=1e-13)
+                if math.isinf(lb):
+                    assert lse[0, h, i] == -np.inf
+                else:
+                    np.testing.assert_allclose(lse[0, h, i], lb, rtol=1e-12)
+
+
+def pin_range_merge_equals_full():
+    """Key chunks merged in all-gather arrival order (the rank's own chunks first, then the
+    others around the ring) give full causal attention; so does an unaligned split merged
+    in reverse order."""
+    rng = _rng(22)
+    B, S, H, hd, D, r = 2, 64, 2, 8, 4, 1
+    C = S // (2 * D)
+    idx = O.zigzag_index(S, D, r)
+    q = rng.standard_normal((B, len(idx), H, hd))
+    k = rng.standard_normal((B, S, H, hd))
+    v = rng.standard_normal((B, S, H, hd))
+    full_o, full_lse = O.causal_attention(q, idx, k, v)
+    own = [r, 2 * D - 1 - r]
+    order = own + [c for t in range(1, D) for c in ((r - t) % D, 2 * D - 1 - (r - t) % D)]
+    assert sorted(order) == list(range(2 * D))
+    for bounds in ([(c * C, (c + 1) * C) for c in order], [(23, 64), (5, 23), (0, 5)]):
+        acc_o = np.zeros_like(full_o)
+        acc_lse = np.full_like(full_lse, -np.inf)
+        for lo, hi in bounds:
+            po, pl = O.attention_range(q, idx, k, v, lo, hi)
+            acc_o, acc_lse = O.lse_merge(acc_o, acc_lse, po, pl)
+        np.testing.assert_allclose(acc_o, full_o, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(acc_lse, full_lse, rtol=1e-12)
+
+
+def pin_merge_identity():
+    """(0, -inf) is neutral for lse_merge, the merge is symmetric, and the range [0, S)
+    is causal attention itself."""
+    rng = _rng(23)
+    B, S, H, hd = 1, 24, 2, 4
+    pos = np.arange(S)
+    q, k, v = (rng.standard_normal((B, S, H, hd)) for _ in range(3))
+    o, lse = O.attention_range(q, pos, k, v, 0, S)
+    fo, fl = O.causal_attention(q, pos, k, v)
+    np.testing.assert_allclose(o, fo, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, fl, rtol=1e-13)
+    zo, zl = np.zeros_like(o), np.full_like(lse, -np.inf)
+    mo, ml = O.lse_merge(zo, zl, o, lse)
+    np.testing.assert_array_equal(mo, o)
+    np.testing.assert_array_equal(ml, lse)
+    o1, l1 = O.attention_range(q, pos, k, v, 0, 9)
+    o2, l2 = O.attention_range(q, pos, k, v, 9, S)
+    a = O.lse_merge(o1, l1, o2, l2)
+    b = O.lse_merge(o2, l2, o1, l1)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(a[0], fo, rtol=1e-10, atol=1e-12)
+    eo, el = O.lse_merge(zo, zl, zo, zl)
+    assert np.all(eo == 0) and np.all(el == -np.inf)
+
+
 PINS = [pin_zigzag_golden, pin_zigzag_partition, pin_zigzag_balance, pin_zigzag_identity,
         pin_attention_vs_brute, pin_attention_vs_library, pin_attention_concat_ranks,
         pin_attention_special_cases, pin_attention_scale, pin_silu_closed_form,
         pin_mlp_vs_brute, pin_mlp_shards_sum, pin_layer_vs_brute, pin_layer_concat_ranks,
-        pin_layer_rows_subset, pin_layer_flops]
+        pin_layer_rows_subset, pin_layer_flops, pin_range_vs_brute, pin_range_merge_equals_full,
+        pin_merge_identity]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -307,7 +381,22 @@ def _bad_split_heads(t, n_heads):
     return t.reshape(*t.shape[:-1], t.shape[-1] // n_heads, n_heads).swapaxes(-1, -2)
 
 
+_good_range = O.attention_range
+_good_merge = O.lse_merge
+
+
+def _bad_range(q, q_pos, k, v, key_lo, key_hi, scale=None, row_block=512):
+    return _good_range(q, q_pos, k, v, key_lo + 1, key_hi, scale, row_block)  # lower bound one key late
+
+
+def _bad_merge(o_a, lse_a, o_b, lse_b):
+    o, lse = _good_merge(o_b, lse_a, o_a, lse_b)  # outputs paired with the other side's weight
+    return o, lse
+
+
 MUTANTS = {
+    "range_lower_bound_late": ("attention_range", _bad_range),
+    "merge_weights_swapped": ("lse_merge", _bad_merge),
     "zigzag_mirror_off_by_one": ("zigzag_index", _bad_zigzag),
     "mask_drops_diagonal": ("causal_scores_mask", _bad_mask),
     "mask_one_key_late": ("causal_scores_mask", _bad_mask_off),
