@@ -149,6 +149,92 @@ def attn_traffic(workload):
     return float(val.group(1))
 
 
+def arrival_order(D, r):
+    """All-gather arrival order of the 2D zigzag chunks: the rank's own two, then the chunk
+    pairs of ranks r-1, r-2, ... around the ring."""
+    order = [r, 2 * D - 1 - r]
+    for t in range(1, D):
+        p = (r - t) % D
+        order += [p, 2 * D - 1 - p]
+    return order
+
+
+def time_chunked(st, w, rank, reps=3, fused=True):
+    """Chunked-arrival attention: tsp_attn_fwd_range per zigzag chunk in arrival order,
+    merged into an fp32 accumulator (fused: by the range launch itself; otherwise by a
+    tsp_attn_merge launch after each), bf16 O after the last chunk. Times the whole
+    pipeline, the range launches and the merges (HIP events on the launch stream), and the
+    single-launch attention on the same Q/K/V for comparison."""
+    import torch
+    from long_context_transformer_amd import tsp
+    B, S, D, H, hd, C = w.B, w.S, w.D, w.n_heads, w.head_dim, w.C
+    R = S // D
+    q = torch.empty((B, R, H * hd), dtype=torch.bfloat16, device="cuda")
+    tsp.qkv_fwd(st["xs"], st["dev"]["w_qkv"], q, st["kf"], st["vf"], B, S, D, rank, H, hd)
+    acc_o = torch.empty((B, R, H, hd), dtype=torch.float32, device="cuda")
+    acc_l = torch.empty((B, H, R), dtype=torch.float32, device="cuda")
+    po, pl = torch.empty_like(acc_o), torch.empty_like(acc_l)
+    out = torch.empty((B, R, H, hd), dtype=torch.bfloat16, device="cuda")
+    bounds = [(c * C, (c + 1) * C) for c in arrival_order(D, rank)]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    t_range = t_merge = t_total = 0.0
+    for rep in range(reps + 1):
+        acc_o.zero_()
+        acc_l.fill_(float("-inf"))
+        torch.cuda.synchronize()
+        e_all0, e_all1 = ev(), ev()
+        marks = []
+        e_all0.record()
+        for n, (lo, hi) in enumerate(bounds):
+            e0, e1, e2 = ev(), ev(), ev()
+            last = out if n == len(bounds) - 1 else None
+            e0.record()
+            if fused:
+                tsp.attn_fwd_range(q, st["kf"], st["vf"], acc_o, acc_l, B, S, D, rank, H, hd, lo, hi,
+                                   accumulate=True, o_out=last)
+                e1.record()
+            else:
+                tsp.attn_fwd_range(q, st["kf"], st["vf"], po, pl, B, S, D, rank, H, hd, lo, hi)
+                e1.record()
+                tsp.attn_merge(acc_o, acc_l, po, pl, last, B, S, D, H, hd)
+            e2.record()
+            marks.append((e0, e1, e2))
+        e_all1.record()
+        torch.cuda.synchronize()
+        if rep == 0:
+            continue  # warm-up pass
+        t_total += e_all0.elapsed_time(e_all1)
+        t_range += sum(a.elapsed_time(b) for a, b, _ in marks)
+        t_merge += sum(b.elapsed_time(c) for _, b, c in marks)
+    t_total, t_range, t_merge = t_total / reps, t_range / reps, t_merge / reps
+    mono = torch.empty_like(out)
+    tsp.attn_fwd(q, st["kf"], st["vf"], mono, None, B, S, D, rank, H, hd)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(reps):
+        tsp.attn_fwd(q, st["kf"], st["vf"], mono, None, B, S, D, rank, H, hd)
+    e1.record()
+    torch.cuda.synchronize()
+    t_mono = e0.elapsed_time(e1) / reps
+    diff = float((out.float() - mono.float()).abs().max())
+    res = {"chunks": len(bounds), "order": "own chunks, then ring", "fused_merge": fused,
+           "ms": round(t_total, 4), "range_launches_ms": round(t_range, 4),
+           "single_launch_ms": round(t_mono, 4), "overhead_pct": round(100 * (t_total / t_mono - 1), 2),
+           "max_abs_diff_vs_single_launch": diff}
+    if not fused:
+        # merge traffic per launch: fp32 O read twice and written once, lse read twice and
+        # written once; the last merge also writes the bf16 O (counted once)
+        n_el = B * R * H * hd
+        merge_bytes = len(bounds) * (12 * n_el + 12 * B * H * R) + 2 * n_el
+        merge_gbs = merge_bytes / (t_merge * 1e-3) / 1e9
+        res["merges_ms"] = round(t_merge, 4)
+        res["merge_roofline"] = {"bound": "hbm", "achieved": round(merge_gbs, 1), "peak": PEAK_HBM_GBS,
+                                 "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
+                                 "bytes_per_merge": 12 * n_el + 12 * B * H * R}
+    return res
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -204,6 +290,8 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--chunked", action="store_true",
+                    help="also time chunked-arrival attention (range launches + log-sum-exp merges)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB plain copy kernel first (counter calibration)")
     ap.add_argument("--sweep", default=None, help="also time every workload (and every rank of the "
@@ -237,6 +325,11 @@ def main():
           f"{attn_tflops:.1f} TFLOP/s  phases " + " ".join(f"{k}={v:.3f}" for k, v in phases.items()),
           file=sys.stderr, flush=True)
     traffic = attn_traffic(w.name)
+    chunked = None
+    if args.chunked:
+        chunked = time_chunked(st, w, args.rank, fused=True)
+        chunked["with_merge_launches"] = time_chunked(st, w, args.rank, fused=False)
+        print("# chunked " + json.dumps(chunked), file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -269,6 +362,8 @@ def main():
                      "flops_per_launch": attn_flops},
         "cpu_baseline": cpu,
     }
+    if chunked:
+        out["chunked_attention"] = chunked
     print(json.dumps(out), flush=True)
 
     if args.sweep:

@@ -137,6 +137,45 @@ TSP_API int tsp_attn_fwd(const void* q, const void* k_full, const void* v_full, 
                  int32_t B, int64_t S, int32_t D, int32_t rank, int32_t n_heads,
                  int32_t head_dim, float scale, tsp_stream_t stream);
 
+/*
+ * Chunked-arrival attention: the consumer side of overlapping the K/V all-gather with
+ * attention. [TSP §2, attention layers: the all-gather of K/V feeds FlashAttention;
+ * §3, implementation and overlap: transfers hidden behind compute]
+ *
+ * tsp_attn_fwd_range: the rank's queries against the keys at positions [key_lo, key_hi)
+ * only, e.g. one zigzag chunk of the sequence as soon as the all-gather has delivered it.
+ *   q        bf16 [B, 2C, H, hd]  local row order
+ *   k_full, v_full bf16 [B, S, H, hd]  natural order; only rows [key_lo, min(key_hi,
+ *            last position of the rank + 1)) are read
+ *   o_part   f32 [B, 2C, H, hd]  softmax-weighted mean of V over the keys j of the range
+ *            with j <= the query's position; 0 for a row that sees no such key
+ *   lse_part f32 [B, H, 2C]  natural log of the sum of exp(scale q.k_j) over those keys;
+ *            -inf for a row that sees none
+ *   0 <= key_lo <= key_hi <= S; scale as for tsp_attn_fwd.
+ *   accumulate != 0: (o_part, lse_part) hold a running accumulator (start: 0, -inf) and
+ *            the range's result is merged into it by log-sum-exp (as tsp_attn_merge does)
+ *            instead of overwriting it; rows that see no key of the range, and whole row
+ *            tiles without one, are left untouched.
+ *   o_out    bf16 [B, 2C, H, hd] or NULL: receives the resulting O of every row (with
+ *            accumulate, after the last range it is the output of tsp_attn_fwd).
+ * tsp_attn_merge: (o_acc, lse_acc) <- their log-sum-exp merge with (o_part, lse_part):
+ *   lse = log(exp(lse_acc) + exp(lse_part)),
+ *   o_acc = exp(lse_acc - lse) o_acc + exp(lse_part - lse) o_part.
+ *   Same layouts as above; start from o_acc = 0, lse_acc = -inf (or from the first
+ *   range's outputs). o_out (bf16 [B, 2C, H, hd], may be NULL) receives the merged O;
+ *   after every key range of [0, S) has been merged, in any order, it is the output of
+ *   tsp_attn_fwd. o_part and lse_part must not alias the accumulators.
+ * Errors: TSP_ERR_NULL, TSP_ERR_SHAPE (key range, fold), TSP_ERR_RANK,
+ * TSP_ERR_UNSUPPORTED (head_dim), TSP_ERR_ALIGN (16 bytes; lse 4 bytes).
+ */
+TSP_API int tsp_attn_fwd_range(const void* q, const void* k_full, const void* v_full, float* o_part,
+                               float* lse_part, int32_t B, int64_t S, int32_t D, int32_t rank,
+                               int32_t n_heads, int32_t head_dim, float scale, int64_t key_lo,
+                               int64_t key_hi, int32_t accumulate, void* o_out, tsp_stream_t stream);
+TSP_API int tsp_attn_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                           void* o_out, int32_t B, int64_t S, int32_t D, int32_t n_heads,
+                           int32_t head_dim, tsp_stream_t stream);
+
 /* Workspace bytes tsp_mlp_shard_accum needs for M rows and shard width Fs. */
 TSP_API size_t tsp_mlp_workspace_size(int64_t M, int32_t Fs);
 

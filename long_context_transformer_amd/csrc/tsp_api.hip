@@ -171,6 +171,47 @@ int tsp_attn_fwd(const void* q, const void* k_full, const void* v_full, void* o,
   return ok();
 }
 
+int tsp_attn_fwd_range(const void* q, const void* k_full, const void* v_full, float* o_part, float* lse_part,
+                       int32_t B, int64_t S, int32_t D, int32_t rank, int32_t n_heads, int32_t head_dim, float scale,
+                       int64_t key_lo, int64_t key_hi, int32_t accumulate, void* o_out, tsp_stream_t stream) {
+  if (int rc = check_fold(B, S, D, rank)) return rc;
+  if (int rc = check_heads(n_heads, head_dim)) return rc;
+  if (!(scale == scale) || isinf(scale)) return fail(TSP_ERR_SHAPE, "scale must be finite");
+  if (key_lo < 0 || key_lo > key_hi || key_hi > S)
+    return fail(TSP_ERR_SHAPE, "key range [%lld, %lld) not within [0, S=%lld]", (long long)key_lo,
+                (long long)key_hi, (long long)S);
+  if (B == 0 || S == 0) return ok();
+  if (!q || !k_full || !v_full || !o_part || !lse_part)
+    return fail(TSP_ERR_NULL, "q, k_full, v_full, o_part and lse_part must be non-NULL");
+  if (misaligned(q) || misaligned(k_full) || misaligned(v_full) || misaligned(o_part) || misaligned(o_out) ||
+      (reinterpret_cast<uintptr_t>(lse_part) & 3u))
+    return fail(TSP_ERR_ALIGN, "q/k/v/o_part/o_out must be 16-byte aligned and lse_part 4-byte aligned");
+  return hip_status(tsp::launch_attn_range(q, k_full, v_full, o_part, lse_part, B, S, D, rank, n_heads, head_dim,
+                                           scale, key_lo, key_hi, accumulate ? 1 : 0, o_out,
+                                           static_cast<hipStream_t>(stream)),
+                    "range attention launch") == TSP_OK
+             ? ok()
+             : TSP_ERR_HIP;
+}
+
+int tsp_attn_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part, void* o_out, int32_t B,
+                   int64_t S, int32_t D, int32_t n_heads, int32_t head_dim, tsp_stream_t stream) {
+  if (int rc = check_fold(B, S, D, 0)) return rc;
+  if (int rc = check_heads(n_heads, head_dim)) return rc;
+  if (B == 0 || S == 0) return ok();
+  if (!o_acc || !lse_acc || !o_part || !lse_part)
+    return fail(TSP_ERR_NULL, "o_acc, lse_acc, o_part and lse_part must be non-NULL");
+  if (misaligned(o_acc) || misaligned(o_part) || misaligned(o_out) || (reinterpret_cast<uintptr_t>(lse_acc) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse_part) & 3u))
+    return fail(TSP_ERR_ALIGN, "o_acc/o_part/o_out must be 16-byte aligned and lse 4-byte aligned");
+  if (o_acc == o_part || lse_acc == lse_part) return fail(TSP_ERR_SHAPE, "the partial must not alias the accumulator");
+  return hip_status(tsp::launch_attn_merge(o_acc, lse_acc, o_part, lse_part, o_out, B, (int)(S / D), n_heads,
+                                           head_dim, static_cast<hipStream_t>(stream)),
+                    "merge launch") == TSP_OK
+             ? ok()
+             : TSP_ERR_HIP;
+}
+
 size_t tsp_mlp_workspace_size(int64_t M, int32_t Fs) {
   if (M < 0 || Fs < 1) return 0;
   return mlp_ws_bytes(M, Fs);

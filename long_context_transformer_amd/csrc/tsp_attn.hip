@@ -89,8 +89,11 @@ struct AttnArgs {
   const bf16_t* q;
   const bf16_t* k;
   const bf16_t* v;
-  bf16_t* o;
+  bf16_t* o;     // full attention: bf16 O
+  float* o32;    // key-range attention: fp32 O (normalised over the range's keys)
   float* lse;
+  int key_lo, key_hi;  // key-range attention: key positions [key_lo, key_hi)
+  int accumulate;      // key-range attention: merge into (o32, lse) instead of overwriting
   int64_t S;
   int64_t C;
   int rows;  // 2C local rows per sequence
@@ -115,7 +118,10 @@ struct Lay {
   __device__ static int fv(int r) { return HD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-template <int HD>
+// PART = false: every key up to the query's position, bf16 O. PART = true: only keys in
+// [key_lo, key_hi) (a chunk of the sequence as the all-gather delivers it), fp32 O and the
+// log-sum-exp for the merge; rows that see no key get O = 0 and lse = -inf.
+template <int HD, bool PART>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void attn_fwd(AttnArgs a) {
   using L = Lay<HD>;
   constexpr int KS = L::KS, DB = L::DB, ROWB = L::ROWB, CPR = L::CPR, TILEB = L::TILEB, NDMA = L::NDMA;
@@ -135,8 +141,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int qt = a.n_qt - 1 - (item - bh * a.n_qt);  // heaviest tile of the (b, h) first
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
   const int row0 = qt * BR;
-  const int kv_end = (int)zigzag_pos(min(row0 + BR, a.rows) - 1, a.C, a.rank, a.D) + 1;
-  const int n_kt = (kv_end + BC - 1) / BC;
+  int kv_end = (int)zigzag_pos(min(row0 + BR, a.rows) - 1, a.C, a.rank, a.D) + 1;
+  int k_base = 0;  // position of the first key of stage 0
+  if constexpr (PART) {
+    kv_end = min(kv_end, a.key_hi);
+    k_base = (a.key_lo / BC) * BC;
+  }
+  const int n_kt = (kv_end - k_base + BC - 1) / BC;
 
   const int wrow0 = row0 + wave * (32 * QB);
   const int wmin_pos = wrow0 < a.rows ? (int)zigzag_pos(wrow0, a.C, a.rank, a.D) : 0;
@@ -166,6 +177,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       for (int e = 0; e < 8; ++e) qf[qb][s][e] = (__bf16)((float)qf[qb][s][e] * a.scale_log2);
 #endif
 
+  // A tile whose keys all lie outside the range: O = 0, lse = -inf, no LDS work (the whole
+  // workgroup returns here, before any barrier).
+  if constexpr (PART) {
+    if (kv_end <= a.key_lo) {
+      // accumulate: the range adds nothing to these rows; only the bf16 O is written if asked
+      if (a.accumulate && a.o == nullptr) return;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (qi[qb] >= a.rows) continue;
+        const int64_t ro = ((int64_t)b * a.rows + qi[qb]) * tok + (int64_t)h * HD;
+        float* op = a.o32 + ro;
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int dim = db * 32 + 8 * g + 4 * hl;
+            if (a.accumulate) {
+              const f32x4 v = *reinterpret_cast<const f32x4*>(op + dim);
+              *reinterpret_cast<uint2*>(a.o + ro + dim) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+            } else {
+              *reinterpret_cast<f32x4*>(op + dim) = f32x4{};
+              if (a.o != nullptr) *reinterpret_cast<uint2*>(a.o + ro + dim) = make_uint2(0u, 0u);
+            }
+          }
+        if (!a.accumulate && hl == 0) a.lse[((int64_t)b * a.H + h) * a.rows + qi[qb]] = -INFINITY;
+      }
+      return;
+    }
+  }
+
   // ---- stage loads: global -> LDS, 16 bytes per lane, lane-linear within the 1 KB a wave
   // instruction writes. Load p of this wave covers linear chunks (NW p + wave) * 64 + lane.
   const char* kseq = reinterpret_cast<const char*>(a.k + (int64_t)b * a.S * tok + (int64_t)h * HD);
@@ -181,7 +222,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   }
   const uint32_t tokb = (uint32_t)(tok * 2);
   auto issue = [&] __device__(int st, int t) {
-    const int key0 = t * BC;
+    const int key0 = k_base + t * BC;
     const int lim = kv_end - 1 - key0;  // rows past the tile's last key repeat it (masked)
     const char* kb = kseq + (int64_t)key0 * tok * 2;
     const char* vb = vseq + (int64_t)key0 * tok * 2;
@@ -277,7 +318,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (kstart + 8 * (r >> 2) + 4 * hl + (r & 3) > qpos[qb]) sacc[qb][r] = -INFINITY;
+        if (kstart + 8 * (r >> 2) + 4 * hl + (r & 3) > qpos[qb] ||
+            (PART && (kstart + 8 * (r >> 2) + 4 * hl + (r & 3) < a.key_lo ||
+                      kstart + 8 * (r >> 2) + 4 * hl + (r & 3) >= a.key_hi)))
+          sacc[qb][r] = -INFINITY;
   };
 #if TSP_ATTN_CINIT
   // sacc = s*c - m_at (m_at: the reference max the block was computed against). Row max;
@@ -306,7 +350,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         const bool upd = mx[qb] - d > kLazy;
         const float m_new = upd ? m_at[qb] + mx[qb] : m_s[qb];
         alpha[qb] = upd ? __builtin_amdgcn_exp2f(m_s[qb] - m_new) : 1.0f;  // 0 on the first block
-        const float shift = m_new - m_at[qb];
+        // a row with no visible key so far keeps its scores (-inf) and reference
+        const float shift = m_new == -INFINITY ? 0.0f : m_new - m_at[qb];
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[qb][r] -= shift;
         l_run[qb] *= alpha[qb];
@@ -434,8 +479,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   auto body = [&] __device__(int t, int cur, int nxt, int refill) {
     sync_stage(t + 2 < n_kt ? 1 : 0);  // stage t+1 landed; stage t+2 may be in flight
     if (t + 3 < n_kt) issue(refill, t + 3);
-    const int k0 = t * BC;
-    if (k0 + 31 > wmin_pos) mask(s_cur, k0);
+    const int k0 = k_base + t * BC;
+    // causal mask where a key may follow a row; in a key range also at its two ends
+    if (k0 + 31 > wmin_pos || (PART && (k0 < a.key_lo || k0 + 32 > a.key_hi))) mask(s_cur, k0);
     qk(kf, s_nxt);  // block 1 of stage t
     note(m_at_nxt);
     load_v(cur, 0, vf);
@@ -444,7 +490,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     close_region(pf);
     if (__ballot(any)) rescale(alpha);
     pv(vf, pf);
-    if (k0 + 63 > wmin_pos) mask(s_nxt, k0 + 32);
+    if (k0 + 63 > wmin_pos || (PART && (k0 + 32 < a.key_lo || k0 + 64 > a.key_hi))) mask(s_nxt, k0 + 32);
     qk(kf, s_cur);  // block 0 of stage t+1
     note(m_at_cur);
     load_v(cur, 1, vf);
@@ -467,8 +513,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    inv[qb] = 1.0f / l_tot;
+    inv[qb] = PART ? (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) : 1.0f / l_tot;
     l_run[qb] = l_tot;
+  }
+  if constexpr (PART) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (qi[qb] >= a.rows) continue;
+      const int64_t ro = ((int64_t)b * a.rows + qi[qb]) * tok + (int64_t)h * HD;
+      float* op = a.o32 + ro;
+      float* lp = a.lse + ((int64_t)b * a.H + h) * a.rows + qi[qb];
+      const float lse_b = l_run[qb] > 0.0f ? (m_s[qb] + __log2f(l_run[qb])) * 0.69314718055994531f : -INFINITY;
+      // Overwrite: weights (0, 1). Accumulate: the log-sum-exp merge with what the
+      // accumulator holds (both lanes of the row read it before lane hl == 0 writes).
+      float wa = 0.0f, wb = 1.0f, lse_new = lse_b;
+      if (a.accumulate) {
+        const float lse_a = *lp;
+        const float mm = fmaxf(lse_a, lse_b);
+        wb = 0.0f;
+        if (mm != -INFINITY) {
+          wa = __expf(lse_a - mm);
+          wb = __expf(lse_b - mm);
+          const float z = wa + wb;
+          lse_new = mm + __logf(z);
+          wa /= z;
+          wb /= z;
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dim = db * 32 + 8 * g + 4 * hl;
+          const f32x16& o = oacc[qb][db];
+          const float s = wb * inv[qb];
+          f32x4 val = {o[4 * g] * s, o[4 * g + 1] * s, o[4 * g + 2] * s, o[4 * g + 3] * s};
+          if (a.accumulate) val += wa * *reinterpret_cast<const f32x4*>(op + dim);
+          *reinterpret_cast<f32x4*>(op + dim) = val;
+          if (a.o != nullptr) *reinterpret_cast<uint2*>(a.o + ro + dim) = pack_bf16x4(val[0], val[1], val[2], val[3]);
+        }
+      }
+      if (hl == 0) *lp = lse_new;
+    }
+    return;
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -509,10 +596,100 @@ hipError_t launch_attn(const void* q, const void* k_full, const void* v_full, vo
   a.items = B * H * a.n_qt;
   const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)hd);
   a.scale_log2 = sc * 1.4426950408889634f;
+  a.o32 = nullptr;
+  a.key_lo = 0;
+  a.key_hi = (int)S;
+  a.accumulate = 0;
   if (hd == 128) {
-    hipLaunchKernelGGL(attn_fwd<128>, dim3(a.items), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd<128, false>), dim3(a.items), dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(attn_fwd<64>, dim3(a.items), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd<64, false>), dim3(a.items), dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_range(const void* q, const void* k_full, const void* v_full, float* o32, float* lse, int B,
+                             int64_t S, int D, int rank, int H, int hd, float scale, int64_t key_lo, int64_t key_hi,
+                             int accumulate, void* o_out, hipStream_t stream) {
+  AttnArgs a;
+  a.q = static_cast<const bf16_t*>(q);
+  a.k = static_cast<const bf16_t*>(k_full);
+  a.v = static_cast<const bf16_t*>(v_full);
+  a.o = static_cast<bf16_t*>(o_out);
+  a.accumulate = accumulate;
+  a.o32 = o32;
+  a.lse = lse;
+  a.S = S;
+  a.C = S / (2 * D);
+  a.rows = (int)(2 * a.C);
+  a.D = D;
+  a.rank = rank;
+  a.H = H;
+  a.n_qt = (a.rows + BR - 1) / BR;
+  a.items = B * H * a.n_qt;
+  a.key_lo = (int)key_lo;
+  a.key_hi = (int)key_hi;
+  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)hd);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  if (hd == 128) {
+    hipLaunchKernelGGL((attn_fwd<128, true>), dim3(a.items), dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_fwd<64, true>), dim3(a.items), dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+// Log-sum-exp merge of a partial attention into a running one, one wave per (sequence,
+// row, head): lanes own hd / 64 consecutive dims; every lane reads the two lse values
+// before lane 0 writes the merged one (one wave, in program order).
+template <int HD>
+__global__ __launch_bounds__(256) void attn_merge(float* o_acc, float* lse_acc, const float* o_part,
+                                                  const float* lse_part, bf16_t* o_out, int64_t units, int rows, int H) {
+  constexpr int PER = HD / 64;
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * rows + row) * H + h
+  if (u >= units) return;
+  const int lane = threadIdx.x & 63;
+  const int h = (int)(u % H);
+  const int64_t br = u / H;
+  const int row = (int)(br % rows);
+  const int64_t b = br / rows;
+  const int64_t li = (b * H + h) * rows + row;
+  const float la = lse_acc[li], lb = lse_part[li];
+  const float m = fmaxf(la, lb);
+  float wa = 0.0f, wb = 0.0f, lnew = -INFINITY;
+  if (m != -INFINITY) {
+    wa = __expf(la - m);
+    wb = __expf(lb - m);
+    const float z = wa + wb;
+    lnew = m + __logf(z);
+    wa /= z;
+    wb /= z;
+  }
+  float* pa = o_acc + u * HD + lane * PER;
+  const float* pb = o_part + u * HD + lane * PER;
+  float r[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) r[e] = wa * pa[e] + wb * pb[e];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) pa[e] = r[e];
+  if (o_out != nullptr) {
+    bf16_t* po = o_out + u * HD + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) po[e] = to_bf16(r[e]);
+  }
+  if (lane == 0) lse_acc[li] = lnew;
+}
+
+hipError_t launch_attn_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part, void* o_out,
+                             int B, int rows, int H, int hd, hipStream_t stream) {
+  const int64_t units = (int64_t)B * rows * H;
+  const dim3 grid((unsigned)((units + 3) / 4));
+  if (hd == 128) {
+    hipLaunchKernelGGL(attn_merge<128>, grid, dim3(256), 0, stream, o_acc, lse_acc, o_part, lse_part,
+                       static_cast<bf16_t*>(o_out), units, rows, H);
+  } else {
+    hipLaunchKernelGGL(attn_merge<64>, grid, dim3(256), 0, stream, o_acc, lse_acc, o_part, lse_part,
+                       static_cast<bf16_t*>(o_out), units, rows, H);
   }
   return hipGetLastError();
 }

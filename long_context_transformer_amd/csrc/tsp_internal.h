@@ -43,4 +43,17 @@ hipError_t launch_attn(const void* q, const void* k_full, const void* v_full, vo
                        int B, int64_t S, int D, int rank, int H, int hd, float scale,
                        hipStream_t stream);
 
+// Causal attention restricted to key positions [key_lo, key_hi): fp32 O (normalised over
+// those keys) [B, 2C, H, hd] and lse [B, H, 2C]; rows with no such key get 0 and -inf.
+// accumulate != 0: log-sum-exp merge into (o32, lse) instead (rows without such keys
+// untouched); o_out (bf16, may be null) receives the resulting O of every row.
+hipError_t launch_attn_range(const void* q, const void* k_full, const void* v_full, float* o32, float* lse, int B,
+                             int64_t S, int D, int rank, int H, int hd, float scale, int64_t key_lo, int64_t key_hi,
+                             int accumulate, void* o_out, hipStream_t stream);
+
+// o_acc, lse_acc <- log-sum-exp merge with (o_part, lse_part); o_out (bf16, may be null)
+// receives the merged O.
+hipError_t launch_attn_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part, void* o_out,
+                             int B, int rows, int H, int hd, hipStream_t stream);
+
 }  // namespace tsp

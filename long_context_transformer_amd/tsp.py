@@ -52,6 +52,9 @@ _SIGS = {
     "tsp_layer_fwd": (_I32, [ctypes.POINTER(LayerDesc), _VP, _VP, _VP, ctypes.POINTER(_VP),
                              ctypes.POINTER(_VP), ctypes.POINTER(_VP), _VP, _VP, _VP, _VP, _VP,
                              ctypes.c_size_t, _VP]),
+    "tsp_attn_fwd_range": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32, _I32,
+                                  ctypes.c_float, _I64, _I64, _I32, _VP, _VP]),
+    "tsp_attn_merge": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32, _VP]),
     "tsp_timing_start": (_I32, [_I32]),
     "tsp_timing_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32, ctypes.POINTER(_I32)]),
 }
@@ -124,6 +127,23 @@ def qkv_fwd(x, w_qkv, q_out, k_full, v_full, B, S, D, rank, n_heads, head_dim, s
 def attn_fwd(q, k_full, v_full, o, lse, B, S, D, rank, n_heads, head_dim, scale=0.0, stream=None):
     _check(load().tsp_attn_fwd(_ptr(q), _ptr(k_full), _ptr(v_full), _ptr(o), _ptr(lse), B, S, D, rank,
                                n_heads, head_dim, scale, _stream(stream, q)))
+
+
+def attn_fwd_range(q, k_full, v_full, o_part, lse_part, B, S, D, rank, n_heads, head_dim, key_lo,
+                   key_hi, scale=0.0, accumulate=False, o_out=None, stream=None):
+    """Attention of the rank's queries against key positions [key_lo, key_hi): fp32 o_part
+    [B, 2C, H, hd] and lse_part [B, H, 2C] (0 and -inf for rows with no visible key), or
+    merged into them when accumulate; o_out (bf16 or None) receives the resulting O."""
+    _check(load().tsp_attn_fwd_range(_ptr(q), _ptr(k_full), _ptr(v_full), _ptr(o_part), _ptr(lse_part), B, S,
+                                     D, rank, n_heads, head_dim, scale, key_lo, key_hi, 1 if accumulate else 0,
+                                     _ptr(o_out), _stream(stream, q)))
+
+
+def attn_merge(o_acc, lse_acc, o_part, lse_part, o_out, B, S, D, n_heads, head_dim, stream=None):
+    """(o_acc, lse_acc) <- log-sum-exp merge with (o_part, lse_part); o_out (bf16 or None)
+    receives the merged O."""
+    _check(load().tsp_attn_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part), _ptr(o_out), B, S, D,
+                                 n_heads, head_dim, _stream(stream, o_acc)))
 
 
 def mlp_workspace_size(M, Fs):

@@ -12,13 +12,14 @@ from long_context_transformer_amd import synth, tsp
 MAX_REL = 2e-2
 MEAN_REL = 2e-3
 
-# The log-sum-exp output has no tolerance in the contract. The kernel forms scores from
-# Q * scale * log2(e) rounded to bf16 (relative error <= 2^-9 per element), which moves a
-# score by about 3e-3 (log2 units) at the spreads of the 7B workloads; the LSE, a smooth
-# max of the scores, carries errors of that size (about 2e-3 in natural-log units). Bounds
-# of 2e-3 (max) and 3e-4 (mean) of max|lse| (about 11 at S=128K) leave a margin of 2-3x.
-LSE_MAX_REL = 2e-3
-LSE_MEAN_REL = 3e-4
+# The log-sum-exp output has no tolerance in the contract; its error is an absolute error
+# in log space. The kernel forms scores from Q * scale * log2(e) rounded to bf16 (relative
+# error <= 2^-9 per element), which moves a score by at most 2^-9 * scale * sum_d |q_d k_d|
+# (<= about 0.015 in natural-log units for unit-to-1.3 spreads and head_dim <= 128, about
+# 0.002 on average); the LSE, a smooth max of the scores, inherits errors of that size
+# (exactly that size for a row that sees a single key).
+LSE_MAX_ABS = 0.02
+LSE_MEAN_ABS = 3e-3
 
 BF16_NAN = 0x7FC0
 
@@ -56,6 +57,20 @@ def check_close(name, got, ref, max_rel=MAX_REL, mean_rel=MEAN_REL):
     assert mx <= max_rel * scale, f"{name}: max-abs {mx:.4g} > {max_rel} * {scale:.4g}"
     assert mean <= mean_rel * scale, f"{name}: mean-abs {mean:.4g} > {mean_rel} * {scale:.4g}"
     return mx / scale, mean / scale
+
+
+def check_lse(name, got, ref):
+    """Absolute log-space bounds for the log-sum-exp output; -inf entries must match."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin), f"{name}: -inf pattern differs"
+    err = np.abs(got[fin] - ref[fin])
+    mx, mean = float(err.max()), float(err.mean())
+    print(f"  {name}: max_err={mx:.3g} mean_err={mean:.3g} (absolute, natural log)", flush=True)
+    assert mx <= LSE_MAX_ABS, f"{name}: max-abs {mx:.4g} > {LSE_MAX_ABS}"
+    assert mean <= LSE_MEAN_ABS, f"{name}: mean-abs {mean:.4g} > {LSE_MEAN_ABS}"
 
 
 def shard_rows(x_full_dev, S, D, rank):

@@ -85,6 +85,25 @@ def test_attn_errors():
     assert _code(f, A, A, A, A, None, 1, 256, 4, 0, 4, 64, float("nan"), 0) == 2
 
 
+def test_attn_range_and_merge_errors():
+    f = tsp.attn_fwd_range
+    args = (A, A, A, A, A + 16)
+    assert _code(f, *args, 1, 256, 4, 0, 4, 64, -1, 10, 0.0, 0) == 2     # key_lo < 0
+    assert _code(f, *args, 1, 256, 4, 0, 4, 64, 20, 10, 0.0, 0) == 2     # key_lo > key_hi
+    assert _code(f, *args, 1, 256, 4, 0, 4, 64, 0, 257, 0.0, 0) == 2     # key_hi > S
+    assert _code(f, *args, 1, 256, 4, 9, 4, 64, 0, 256, 0.0, 0) == 3
+    assert _code(f, None, A, A, A, A, 1, 256, 4, 0, 4, 64, 0, 256, 0.0, 0) == 1
+    assert _code(f, A, A, A, MIS, A, 1, 256, 4, 0, 4, 64, 0, 256, 0.0, 0) == 6
+    assert _code(f, A, A, A, A, A + 2, 1, 256, 4, 0, 4, 64, 0, 256, 0.0, 0) == 6
+    f(None, None, None, None, None, 0, 256, 4, 0, 4, 64, 0, 256)          # empty batch: no-op
+    m = tsp.attn_merge
+    assert _code(m, A, A + 16, A + 32, A + 48, None, 1, 250, 4, 4, 64) == 2
+    assert _code(m, None, A, A, A, None, 1, 256, 4, 4, 64) == 1
+    assert _code(m, A, A + 16, A, A + 48, None, 1, 256, 4, 4, 64) == 2   # partial aliases accumulator
+    assert _code(m, A, A + 16, A + 32, A + 48, MIS, 1, 256, 4, 4, 64) == 6
+    m(None, None, None, None, None, 0, 256, 4, 4, 64)
+
+
 def test_qkv_errors():
     f = tsp.qkv_fwd
     assert _code(f, A, None, None, A, A, 1, 256, 4, 0, 4, 64, 0) == 1

@@ -1,0 +1,204 @@
+"""GPU parity of chunked-arrival attention: attention over a key range (tsp_attn_fwd_range)
+and the log-sum-exp merge of partial attentions (tsp_attn_merge), against the fp64 oracle.
+
+The all-gather of K/V delivers the sequence chunk by chunk; attention over each arrived
+chunk, merged by log-sum-exp, must equal attention over the whole sequence (summary of
+"Folding Tensor and Sequence Parallelism for Memory-Efficient Transformer Training &
+Inference", gist.science 2604.26294, §2 attention layers, §3 implementation and overlap).
+Tolerance: the contract's max-abs <= 2e-2 max|ref|, mean-abs <= 2e-3 max|ref| per tensor
+(per (chunk, head) at full size); rows that see no key of a range must be exactly
+(0, -inf).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_transformer_amd import synth, tsp
+from oracle import tsp_oracle as O
+
+from _gpu_helpers import check_close, check_lse, dev_bf16, host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tsp.load()
+
+
+def qkv_inputs(B, S, D, H, hd, seed):
+    R = S // D
+    q = synth.normal_bf16((B, R, H, hd), seed, std=1.0)
+    k = synth.normal_bf16((B, S, H, hd), seed + 1, std=1.0)
+    v = synth.normal_bf16((B, S, H, hd), seed + 2, std=1.0)
+    return q, k, v
+
+
+def arrival_order(D, r):
+    """All-gather arrival order of the 2D chunks: the rank's own two chunks, then the
+    chunk pairs of ranks r-1, r-2, ... around the ring."""
+    order = [r, 2 * D - 1 - r]
+    for t in range(1, D):
+        p = (r - t) % D
+        order += [p, 2 * D - 1 - p]
+    return order
+
+
+def run_range(qd, kd, vd, B, S, D, r, H, hd, lo, hi):
+    R = S // D
+    o = torch.full((B, R, H, hd), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, H, R), float("nan"), dtype=torch.float32, device="cuda")
+    tsp.attn_fwd_range(qd, kd, vd, o, lse, B, S, D, r, H, hd, lo, hi)
+    return o, lse
+
+
+def check_range(name, o, lse, ref_o, ref_lse):
+    o_h = o.cpu().numpy().astype(np.float64)
+    l_h = lse.cpu().numpy().astype(np.float64)
+    empty = ~np.isfinite(ref_lse)  # [B, H, n]
+    assert np.array_equal(~np.isfinite(l_h), empty), f"{name}: rows without keys differ"
+    assert np.all(l_h[empty] == -np.inf)
+    rows_empty = np.transpose(empty, (0, 2, 1))  # [B, n, H]
+    assert np.all(o_h[rows_empty] == 0.0), f"{name}: O of rows without keys is not 0"
+    if np.any(~empty):
+        check_close(f"{name} O", o_h[~rows_empty], ref_o[~rows_empty])
+        check_lse(f"{name} lse", l_h[~empty], ref_lse[~empty])
+
+
+RANGE_CASES = [  # B, S, D, rank, H, hd, ranges
+    (1, 256, 4, 0, 4, 64, [(0, 256), (0, 32), (224, 256), (64, 128), (5, 71), (100, 101), (0, 0), (250, 256)]),
+    (2, 1200, 3, 1, 3, 128, [(0, 1200), (200, 400), (333, 777), (1000, 1200), (0, 64), (1199, 1200)]),
+    (1, 4096, 2, 1, 2, 128, [(1024, 2048), (0, 3000), (2047, 2049), (3072, 4096)]),
+]
+
+
+@pytest.mark.parametrize("B,S,D,rank,H,hd,ranges", RANGE_CASES)
+def test_attn_range_parity(B, S, D, rank, H, hd, ranges):
+    print(f"range attention B={B} S={S} D={D} rank={rank} H={H} hd={hd}", flush=True)
+    q, k, v = qkv_inputs(B, S, D, H, hd, 300 + S % 97)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    idx = O.zigzag_index(S, D, rank)
+    qf, kf, vf = synth.to_f64(q), synth.to_f64(k), synth.to_f64(v)
+    for lo, hi in ranges:
+        o, lse = run_range(qd, kd, vd, B, S, D, rank, H, hd, lo, hi)
+        torch.cuda.synchronize()
+        ref_o, ref_lse = O.attention_range(qf, idx, kf, vf, lo, hi)
+        check_range(f"[{lo},{hi})", o, lse, ref_o, ref_lse)
+    # o_out without accumulation: the bf16 of the range's own O, for every row
+    lo, hi = ranges[-1]
+    o2 = torch.empty((B, S // D, H, hd), dtype=torch.float32, device="cuda")
+    l2 = torch.empty((B, H, S // D), dtype=torch.float32, device="cuda")
+    ob = torch.full((B, S // D, H, hd), float("nan"), dtype=torch.bfloat16, device="cuda")
+    tsp.attn_fwd_range(qd, kd, vd, o2, l2, B, S, D, rank, H, hd, lo, hi, o_out=ob)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, o2.to(torch.bfloat16))
+
+
+def test_merge_parity():
+    """The merge kernel against the oracle's lse_merge, with rows of -inf on either side."""
+    B, S, D, H, hd = 2, 256, 4, 3, 128
+    R = S // D
+    rng = np.random.default_rng(41)
+    oa = rng.standard_normal((B, R, H, hd)).astype(np.float32)
+    ob = rng.standard_normal((B, R, H, hd)).astype(np.float32)
+    la = (rng.standard_normal((B, H, R)) * 3).astype(np.float32)
+    lb = (rng.standard_normal((B, H, R)) * 3).astype(np.float32)
+    la[0, 0, :5] = -np.inf
+    oa[0, :5, 0] = 0
+    lb[1, 2, 7:12] = -np.inf
+    ob[1, 7:12, 2] = 0
+    la[0, 1, 20:23] = lb[0, 1, 20:23] = -np.inf
+    oa[0, 20:23, 1] = ob[0, 20:23, 1] = 0
+    d = lambda x: torch.from_numpy(x).cuda()
+    o_acc, l_acc = d(oa.copy()), d(la.copy())
+    out = torch.empty((B, R, H, hd), dtype=torch.bfloat16, device="cuda")
+    tsp.attn_merge(o_acc, l_acc, d(ob), d(lb), out, B, S, D, H, hd)
+    torch.cuda.synchronize()
+    ref_o, ref_l = O.lse_merge(oa, la, ob, lb)
+    got_l = l_acc.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isfinite(got_l), np.isfinite(ref_l))
+    fin = np.isfinite(ref_l)
+    np.testing.assert_allclose(got_l[fin], ref_l[fin], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(o_acc.cpu().numpy(), ref_o, rtol=1e-5, atol=1e-5)
+    check_close("merged bf16 O", host_f64(out), ref_o)
+
+
+PIPE_CASES = [  # B, S, D, rank, H, hd
+    (1, 256, 4, 2, 4, 64),
+    (2, 2048, 4, 0, 2, 128),
+    (1, 1200, 3, 1, 3, 128),
+]
+
+
+def chunked_attention(qd, kd, vd, B, S, D, r, H, hd, bounds, fused=True):
+    """Attention per arrived chunk merged into an fp32 accumulator, bf16 O at the end:
+    fused (each range launch merges into the accumulator itself) or as range launches
+    followed by merge launches."""
+    R = S // D
+    acc_o = torch.zeros((B, R, H, hd), dtype=torch.float32, device="cuda")
+    acc_l = torch.full((B, H, R), float("-inf"), dtype=torch.float32, device="cuda")
+    out = torch.full((B, R, H, hd), float("nan"), dtype=torch.bfloat16, device="cuda")
+    po = torch.empty_like(acc_o)
+    pl = torch.empty_like(acc_l)
+    for n, (lo, hi) in enumerate(bounds):
+        last = out if n == len(bounds) - 1 else None
+        if fused:
+            tsp.attn_fwd_range(qd, kd, vd, acc_o, acc_l, B, S, D, r, H, hd, lo, hi, accumulate=True, o_out=last)
+        else:
+            tsp.attn_fwd_range(qd, kd, vd, po, pl, B, S, D, r, H, hd, lo, hi)
+            tsp.attn_merge(acc_o, acc_l, po, pl, last, B, S, D, H, hd)
+    return out, acc_l
+
+
+@pytest.mark.parametrize("B,S,D,rank,H,hd", PIPE_CASES)
+def test_chunked_pipeline(B, S, D, rank, H, hd):
+    """The 2D zigzag chunks in all-gather arrival order, merged, equal full causal attention
+    (oracle) and the single-launch kernel; so does an unaligned split in reverse order."""
+    print(f"chunked pipeline B={B} S={S} D={D} rank={rank} H={H} hd={hd}", flush=True)
+    q, k, v = qkv_inputs(B, S, D, H, hd, 500 + S % 89)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    idx = O.zigzag_index(S, D, rank)
+    ref_o, ref_lse = O.causal_attention(synth.to_f64(q), idx, synth.to_f64(k), synth.to_f64(v))
+    C = S // (2 * D)
+    splits = {"arrival": [(c * C, (c + 1) * C) for c in arrival_order(D, rank)],
+              "unaligned": [(S - S // 3, S), (37, S - S // 3), (0, 37)]}
+    mono = torch.empty((B, S // D, H, hd), dtype=torch.bfloat16, device="cuda")
+    tsp.attn_fwd(qd, kd, vd, mono, None, B, S, D, rank, H, hd)
+    for name, bounds in splits.items():
+        for fused in (True, False):
+            tag = f"{name} {'fused' if fused else 'range+merge'}"
+            out, lse = chunked_attention(qd, kd, vd, B, S, D, rank, H, hd, bounds, fused=fused)
+            torch.cuda.synchronize()
+            check_close(f"{tag} O vs oracle", host_f64(out), ref_o)
+            check_lse(f"{tag} lse vs oracle", lse.cpu().numpy().astype(np.float64), ref_lse)
+            check_close(f"{tag} O vs single launch", host_f64(out), host_f64(mono))
+
+
+@pytest.mark.parametrize("name,rank", [("7b_s128k_d8", 0), ("7b_s32k_d8", 5)])
+def test_chunked_pipeline_fullsize(name, rank):
+    """Full size: the 16 zigzag chunks in arrival order, sampled rows checked per (chunk, head)."""
+    w = synth.WORKLOADS[name].with_rank(rank)
+    B, S, D, H, hd, C = w.B, w.S, w.D, w.n_heads, w.head_dim, w.C
+    print(f"full-size chunked pipeline {name} rank {rank}", flush=True)
+    std = float(np.sqrt(4096) * 0.02)
+    q = synth.normal_bf16((B, S // D, H, hd), 8200 + rank, std=std)
+    k = synth.normal_bf16((B, S, H, hd), 8201, std=std)
+    v = synth.normal_bf16((B, S, H, hd), 8202, std=1.0)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    out, _ = chunked_attention(qd, kd, vd, B, S, D, rank, H, hd,
+                               [(c * C, (c + 1) * C) for c in arrival_order(D, rank)])
+    torch.cuda.synchronize()
+    o_h = host_f64(out)
+    del qd, kd, vd
+    idx = O.zigzag_index(S, D, rank)
+    rng = np.random.default_rng(8300 + rank)
+    rows = np.unique(np.concatenate([[0, C - 1, C, 2 * C - 1], rng.choice(2 * C, 12, replace=False)]))
+    kmax = int(idx[rows].max()) + 1
+    ref_o, _ = O.causal_attention(synth.to_f64(q[:, rows]), idx[rows], synth.to_f64(k[:, :kmax]),
+                                  synth.to_f64(v[:, :kmax]))
+    for chunk, sel in (("early", rows < C), ("mirror", rows >= C)):
+        for h in range(H):
+            check_close(f"{chunk} h{h}", o_h[0, rows[sel], h], ref_o[0, sel, h])
