@@ -259,16 +259,21 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(Operands op, Epi epi, int ti
 // ------------------------------------------------------------------- fast path (16-byte operands)
 // Same contraction and epilogues, with the operand tiles moved straight from global memory
 // into LDS (16-byte global_load_lds per lane, no register staging, no bounds predicates):
-//   * k advances in stages of 32 through a 3-deep ring of separate LDS buffers, loads
-//     issued two stages ahead, one barrier per stage;
-//   * a tile row holds 32 bf16 = four 16-byte chunks, chunk c of row r stored at
-//     c ^ ((r / 4) % 4), so the 16 rows read by 16 lanes at one chunk hit 16 distinct
+//   * k advances in stages of 64 through two LDS buffers: after the barrier of stage kt the
+//     loads of stage kt+1 go to the other buffer while the MFMAs of stage kt run;
+//   * a tile row holds 64 bf16 = eight 16-byte chunks, chunk c of row r stored at
+//     c ^ ((r / 2) % 8), so the 16 rows read by 16 lanes at one chunk hit 16 distinct
 //     bank groups;
 //   * rows past M or N repeat the last row (their outputs are never stored); chunks past
-//     K (the last stage when K % 32 != 0) come from a block of zeros;
+//     K (the last stage when K % 64 != 0) come from a block of zeros;
 //   * 8 waves per 256-wide tile (two per SIMD), each owning 128 x 64 outputs (128 x 32 per
 //     weight for the gated pair), so one wave's MFMAs cover the other's LDS latency.
-constexpr int FBK = 32;
+
+// Chunk swizzle of the stage tiles: rows of 4 chunks (k stage 32) rotate by (r / 4) % 4,
+// rows of 8 chunks (k stage 64) by (r / 2) % 8, so the 16 rows read by 16 lanes at one
+// chunk hit 16 distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz_chunk(int r) { return CPR == 4 ? (r >> 2) & 3 : (r >> 1) & 7; }
 
 // Zeros read in place of chunks past K (16 bytes per lane). Never written.
 __device__ __attribute__((aligned(16))) uint4 kZeroChunks[64];
@@ -305,14 +310,19 @@ struct SegArgOf<SEG_NONE> {
 template <int SEG>
 using SegArg = typename SegArgOf<SEG>::type;
 
-template <int BM, int BN, int WM, int WN, bool DUAL, int SEG, class Epi>
+template <int BM, int BN, int WM, int WN, bool DUAL, int SEG, int KB, class Epi>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN) / 4, (BM / WM) * (BN / WN) / 4)))
 void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
+  // KB: k extent of one LDS stage (2-stage ring). A tile row holds KB bf16 = CPR 16-byte
+  // chunks; chunk c of row r sits at c ^ sw(r).
+  constexpr int ROWB = KB * 2, CPR = KB / 8, RPI = 1024 / ROWB;  // rows per 1 KB DMA instruction
+  static_assert(KB == 32 || KB == 64, "stage depth");
+  auto sw = [](int r) { return swz_chunk<CPR>(r); };
   constexpr int NWN = BN / WN, NWAVE = (BM / WM) * NWN;
   constexpr int NB = DUAL ? 2 : 1;
   constexpr int MI = WM / 32, NI = WN / 32;
-  constexpr int ATILE = BM * FBK * 2, BTILE = BN * FBK * 2;
+  constexpr int ATILE = BM * KB * 2, BTILE = BN * KB * 2;
   constexpr int STAGE = ATILE + NB * BTILE;
   constexpr int AINS = ATILE / 1024 / NWAVE;  // 1 KB DMA instructions per wave per stage
   constexpr int BINS = BTILE / 1024 / NWAVE;
@@ -321,7 +331,6 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
   static_assert(BINS >= 1 && BINS * NWAVE * 1024 == BTILE, "B tile split");
   __shared__ __attribute__((aligned(1024))) char s0[STAGE];
   __shared__ __attribute__((aligned(1024))) char s1[STAGE];
-  __shared__ __attribute__((aligned(1024))) char s2[STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -354,15 +363,15 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
   int akc[AINS], bkc[BINS];
 #pragma unroll
   for (int p = 0; p < AINS; ++p) {
-    const int row = 16 * (p * NWAVE + wave) + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const int row = RPI * (p * NWAVE + wave) + lane / CPR;
+    const int c = (lane % CPR) ^ sw(row);
     aoff[p] = (uint32_t)min(m0 + row, op.M - 1) * (uint32_t)(op.lda * 2) + 16 * c;
     akc[p] = 8 * c;
   }
 #pragma unroll
   for (int p = 0; p < BINS; ++p) {
-    const int row = 16 * (p * NWAVE + wave) + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const int row = RPI * (p * NWAVE + wave) + lane / CPR;
+    const int c = (lane % CPR) ^ sw(row);
     boff[p] = (uint32_t)min(n0 + row, op.N - 1) * (uint32_t)(op.ldb * 2) + 16 * c;
     bkc[p] = 8 * c;
   }
@@ -401,12 +410,12 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
         }
       }
     }
-    const int k0 = kt * FBK;
+    const int k0 = kt * KB;
     ab += (size_t)k0 * 2;
     bb += (size_t)k0 * 2;
     const char* b2 = b2base + (size_t)k0 * 2;
     const uint32_t la = lds_addr(st) + wave * 1024;
-    if (k0 + FBK <= op.K) {
+    if (k0 + KB <= op.K) {
 #pragma unroll
       for (int p = 0; p < AINS; ++p) dma16_sbase(ab, aoff[p], la + p * NWAVE * 1024);
 #pragma unroll
@@ -415,7 +424,7 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
 #pragma unroll
         for (int p = 0; p < BINS; ++p) dma16_sbase(b2, boff[p], la + ATILE + BTILE + p * NWAVE * 1024);
       }
-    } else {  // last stage with K % 32 != 0: chunks past K read zeros
+    } else {  // last stage with K % 64 != 0: chunks past K read zeros
       const void* z = &kZeroChunks[lane];
 #pragma unroll
       for (int p = 0; p < AINS; ++p)
@@ -431,9 +440,12 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
     }
   };
 
-  // Fragment byte offsets within a stage for k-steps 0 and 1 (row l32 of a 32-row block).
-  const int x = (l32 >> 2) & 3;
-  const int fo[2] = {l32 * 64 + 16 * (hl ^ x), l32 * 64 + 16 * ((2 + hl) ^ x)};
+  // Fragment byte offsets within a stage for each 16-wide k step (row l32 of a 32-row
+  // block; the swizzle of a row depends only on its index within an aligned 32-row block).
+  constexpr int KSTEPS = KB / 16;
+  int fo[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) fo[ks] = l32 * ROWB + 16 * ((2 * ks + hl) ^ sw(l32));
 
   f32x16 acc[NB][MI][NI];
 #pragma unroll
@@ -445,18 +457,18 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
 
   auto compute = [&] __device__(const char* st) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KSTEPS; ++ks) {
       bf16x8 af[MI];
       bf16x8 bfr[NB][NI];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        af[mi] = as_bf16x8(*reinterpret_cast<const uint4*>(st + (wm * WM + 32 * mi) * 64 + fo[ks]));
+        af[mi] = as_bf16x8(*reinterpret_cast<const uint4*>(st + (wm * WM + 32 * mi) * ROWB + fo[ks]));
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
           bfr[nb][ni] = as_bf16x8(
-              *reinterpret_cast<const uint4*>(st + ATILE + nb * BTILE + (wn * WN + 32 * ni) * 64 + fo[ks]));
+              *reinterpret_cast<const uint4*>(st + ATILE + nb * BTILE + (wn * WN + 32 * ni) * ROWB + fo[ks]));
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -466,29 +478,23 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
     }
   };
 
-  int nk = (op.K + FBK - 1) / FBK;
+  int nk = (op.K + KB - 1) / KB;
   if constexpr (SEG == SEG_K) nk = sg.count * sg.nks;
   issue(s0, 0);
-  if (nk > 1) issue(s1, 1);
-  // Stage kt: wait for its loads (stage kt+1 may stay in flight), barrier, refill the buffer
-  // of stage kt-1 with stage kt+2, then the MFMAs of stage kt.
-  auto body = [&] __device__(int kt, const char* cur, char* refill) {
-    if (kt + 1 < nk) {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS));
-    } else {
+  {
+    // Stage kt: wait for its loads, barrier, load stage kt+1 into the buffer of stage kt-1,
+    // then the MFMAs of stage kt.
+    auto body2 = [&] __device__(int kt, const char* cur, char* other) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");  // no LDS read moves above the barrier
+      if (kt + 1 < nk) issue(other, kt + 1);
+      compute(cur);
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      body2(kt, s0, s1);
+      if (kt + 1 < nk) body2(kt + 1, s1, s0);
     }
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");  // no LDS read moves above the barrier
-    if (kt + 2 < nk) issue(refill, kt + 2);
-    compute(cur);
-  };
-  // Unrolled by the ring depth so every stage buffer is named statically; guarded bodies
-  // (no early exits) keep the accumulators in one register set.
-  for (int kt = 0; kt < nk; kt += 3) {
-    body(kt, s0, s2);
-    if (kt + 1 < nk) body(kt + 1, s1, s0);
-    if (kt + 2 < nk) body(kt + 2, s2, s1);
   }
 
 #pragma unroll
@@ -525,15 +531,16 @@ hipError_t run_tiles(const Operands& op, const Epi& epi, hipStream_t s) {
 
 template <int BM, int BN, int WM, int WN, bool DUAL, int SEG = SEG_NONE, class Epi>
 hipError_t run_fast(const Operands& op, const Epi& epi, hipStream_t s, SegArg<SEG> sg = {}) {
+  constexpr int KB = 64;
   const int tm = (op.M + BM - 1) / BM;
   int tn = (op.N + BN - 1) / BN;
   if constexpr (SEG == SEG_N) {
     sg.tn = tn;
     tn *= sg.count;
   }
-  if constexpr (SEG == SEG_K) sg.nks = (op.K + FBK - 1) / FBK;
+  if constexpr (SEG == SEG_K) sg.nks = (op.K + KB - 1) / KB;
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  hipLaunchKernelGGL((gemm_fast<BM, BN, WM, WN, DUAL, SEG, Epi>), dim3(tm * tn), dim3(threads), 0, s, op, epi, tm,
+  hipLaunchKernelGGL((gemm_fast<BM, BN, WM, WN, DUAL, SEG, KB, Epi>), dim3(tm * tn), dim3(threads), 0, s, op, epi, tm,
                      tn, sg);
   return hipGetLastError();
 }
