@@ -235,6 +235,54 @@ def time_chunked(st, w, rank, reps=3, fused=True):
     return res
 
 
+def time_streamed(st, w, steps, warmup):
+    """Weight-streamed layer (tsp_layer_fwd_streamed): two receive slots per weight kind,
+    shard copies on a copy stream, head groups alternating between two attention streams,
+    W_O partials on a fourth;
+    timed against the same call on one stream (no overlap) and against tsp_layer_fwd with
+    every shard resident. Also reports the resident weight bytes of both layouts."""
+    import torch
+    from long_context_transformer_amd import tsp
+    D = w.D
+    dev = st["dev"]
+    pa = tsp.pack_attn_shards(dev["w_qkv"], dev["w_o"], D)
+    pm = tsp.pack_mlp_shards(dev["w1"], dev["w3"], dev["w2"], D)
+    ws = torch.empty(tsp.layer_streamed_workspace_size(st["desc"]), dtype=torch.uint8, device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    a, y = st["attn_out"], st["mlp_out"]
+    a_ref, y_ref = a.clone(), y.clone()  # tsp_layer_fwd's outputs from the timed steps
+
+    def run(overlap):
+        tsp.layer_fwd_streamed(st["desc"], st["xs"], pa, pm, st["kf"], st["vf"], a, y, ws,
+                               streams=streams if overlap else None)
+
+    res = {}
+    for name, overlap in (("four_streams", True), ("one_stream", False)):
+        for _ in range(warmup):
+            run(overlap)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run(overlap)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_ms"] = round(e0.elapsed_time(e1) / steps, 4)
+    da = float((a.float() - a_ref.float()).abs().max() / a_ref.float().abs().max())
+    dy = float((y - y_ref).abs().max() / y_ref.abs().max())
+    slot_a = pa[0].numel() * 2
+    slot_m = pm[0].numel() * 2
+    res.update({
+        "copied_bytes_per_step": D * (slot_a + slot_m),
+        "resident_weight_bytes": 2 * (slot_a + slot_m),
+        "resident_weight_bytes_all_shards": sum(dev[k].numel() * 2 for k in ("w_qkv", "w_o", "w1", "w3", "w2")),
+        "workspace_bytes": ws.numel(),
+        "workspace_bytes_all_shards": st["ws"].numel(),
+        "max_rel_diff_vs_resident": {"attn_out": da, "mlp_out": dy},
+    })
+    return res
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -292,6 +340,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--chunked", action="store_true",
                     help="also time chunked-arrival attention (range launches + log-sum-exp merges)")
+    ap.add_argument("--streamed", action="store_true",
+                    help="also time the weight-streamed layer (two slots, copy stream) against this one")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB plain copy kernel first (counter calibration)")
     ap.add_argument("--sweep", default=None, help="also time every workload (and every rank of the "
@@ -331,6 +381,13 @@ def main():
         chunked["with_merge_launches"] = time_chunked(st, w, args.rank, fused=False)
         print("# chunked " + json.dumps(chunked), file=sys.stderr, flush=True)
 
+    streamed = None
+    if args.streamed:
+        streamed = time_streamed(st, w, max(args.steps // 2, 3), 2)
+        streamed["resident_ms"] = round(ms, 4)
+        streamed["overhead_pct"] = round(100 * (streamed["four_streams_ms"] / ms - 1), 2)
+        print("# streamed " + json.dumps(streamed), file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, st["inputs"], args.rank, args.cpu_rows)
@@ -364,6 +421,8 @@ def main():
     }
     if chunked:
         out["chunked_attention"] = chunked
+    if streamed:
+        out["weight_streamed_layer"] = streamed
     print(json.dumps(out), flush=True)
 
     if args.sweep:

@@ -226,6 +226,59 @@ TSP_API int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const
                   float* mlp_out, void* ws, size_t ws_bytes, tsp_stream_t stream);
 
 /*
+ * Weight-streamed layer: the rank holds two receive slots per weight kind instead of all
+ * D shards, and runs the layer as the pages' loops over packed shards.  [TSP §2 attention
+ * and MLP layers, §3 overlap of weight transfers with compute]
+ *
+ * Packed attention shard j (j = 0 .. D-1, heads [j H/D, (j+1) H/D), dg = d/D columns):
+ *   bf16, 4 dg d elements: [3 dg, d] = W_q rows, W_k rows, W_v rows of the group
+ *   (rows j dg .. (j+1) dg - 1 of each), then [d, dg] = W_o columns j dg .. (j+1) dg - 1,
+ *   row-major.
+ * Packed MLP shard j (Fs = F/D, Fp = round_up(Fs, 8)):
+ *   bf16, (2 Fs + Fp) d elements: [Fs, d] W1 rows of shard j, [Fs, d] W3 rows, then
+ *   [d, Fs] W2 columns of shard j with row stride Fp (the pad columns are never read).
+ *
+ * Per call, on the streams of `streams` (n_streams = 4: [0] the caller's stream, [1] the
+ * second attention stream, [2] the W_O stream, [3] the copy stream; a NULL entry means
+ * streams[0]. n_streams = 1: everything on streams[0], in one order, no overlap):
+ *   copy stream   copies the shards into the slots (hipMemcpyDeviceToDeviceNoCU: the copy
+ *                 engines), the one-GPU stand-in for receiving the broadcast. An attention
+ *                 slot is refilled in two parts: its QKV rows once the QKV launch that read
+ *                 them is done, its W_o columns once the W_O launch that read them is done.
+ *                 The MLP shards 0 and 1 are copied right after the attention shards 0, 1.
+ *   attention     head group t (t = j = 0 .. D-1) runs on streams[t % 2]: QKV of the
+ *                 group (its Q columns, its columns of the rank's K/V rows), then causal
+ *                 attention of its heads with every query tile's keys split at S/2 into
+ *                 two work items, merged by log-sum-exp into O. Two groups overlap.
+ *   W_O stream    O_group W_o,group^T added to an fp32 accumulator, in order of t; the
+ *                 last step stores the sum as bf16 attn_out.
+ *   streams[0]    the MLP ring after the last W_O step, t = 0 .. D-1 on shard
+ *                 j = (r - t) mod D: the gated hidden of shard j, then its down projection
+ *                 added to mlp_out.
+ * mlp_out doubles as the fp32 accumulator of the W_O partials before the MLP overwrites
+ * it. The other streams first wait for the work already queued on streams[0]; on return
+ * streams[0] waits for everything the call queued, so outputs are ready in its order.
+ * Requires H % D == 0 (whole heads per group).
+ *   w_attn, w_mlp  arrays (HOST memory) of D device pointers to packed shards, 16-byte
+ *                  aligned; the other arguments as in tsp_layer_fwd (desc->w2_ld is
+ *                  ignored: the packed layout fixes the W2 stride).
+ * The library keeps a few HIP events per host thread and device between calls (created
+ * on first use, never freed); calls that overlap on the same streams from different
+ * threads are not supported.
+ * Workspace (tsp_layer_streamed_workspace_size; 0 if desc is invalid): Q and O bf16
+ * [B 2C, d] each, the gated hidden of one shard bf16 [B 2C, Fp], two attention slots, two
+ * MLP slots, and per attention stream the fp32 O and log-sum-exp of a group's attention
+ * over keys [0, S/2) and [S/2, S) (merged into O after each group).
+ * Errors: as tsp_layer_fwd; TSP_ERR_SHAPE if H % D != 0 or n_streams is not 1 or 4.
+ */
+TSP_API size_t tsp_layer_streamed_workspace_size(const tsp_layer_desc* desc);
+TSP_API int tsp_layer_fwd_streamed(const tsp_layer_desc* desc, const void* x_shard,
+                                   const void* const* w_attn, const void* const* w_mlp,
+                                   void* k_full, void* v_full, void* attn_out, float* mlp_out,
+                                   void* ws, size_t ws_bytes, const tsp_stream_t* streams,
+                                   int32_t n_streams);
+
+/*
  * Measurement hook (outside the method): phase timing of tsp_layer_fwd with HIP events
  * recorded on the call's own stream, between its launches.
  *   tsp_timing_start(max_calls)  creates (4 + 1) * max_calls events and arms the hook:

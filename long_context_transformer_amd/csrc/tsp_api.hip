@@ -1,11 +1,13 @@
 // tsp_api.hip -- the C ABI declared in include/tsp.h: argument checks on the host,
 // workspace carving, and the launch sequence of one TSP rank's layer on the caller's
-// stream. The library allocates nothing and keeps no state between calls, except for the
-// opt-in phase timing hook (tsp_timing_start / tsp_timing_read) used by measurements.
+// stream(s). The library allocates no device memory. State kept between calls: the
+// opt-in phase timing hook (tsp_timing_start / tsp_timing_read) used by measurements,
+// and the per-thread, per-device HIP events of the weight-streamed layer.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -348,6 +350,235 @@ int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const void* w
       return rc;
   }
   if (int rc = mark(4)) return rc;
+  return ok();
+}
+
+
+}  // extern "C"
+
+namespace {
+
+// Events of the weight-streamed layer, per host thread and device, created on first use.
+// Re-recording an event is safe for waits already queued: a stream wait takes the
+// event's most recent record at the time the wait is queued.
+int stream_events(hipEvent_t** out, int n) {
+  thread_local std::map<int, std::vector<hipEvent_t>> pool;
+  int dev = 0;
+  if (int rc = hip_status(hipGetDevice(&dev), "hipGetDevice")) return rc;
+  std::vector<hipEvent_t>& ev = pool[dev];
+  while ((int)ev.size() < n) {
+    hipEvent_t e = nullptr;
+    if (int rc = hip_status(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreateWithFlags")) return rc;
+    ev.push_back(e);
+  }
+  *out = ev.data();
+  return TSP_OK;
+}
+
+struct StreamedCarve {
+  size_t q_off, o_off, h_off, slot_a[2], slot_m[2], part[2], total;
+  size_t attn_shard, mlp_shard;  // elements of one packed shard
+  int64_t fp;                    // W2 row stride / hidden row stride in a packed MLP shard
+};
+
+StreamedCarve carve_streamed(const tsp_layer_desc* d) {
+  const size_t M = (size_t)d->batch * (size_t)(d->seq_len / d->fold);
+  const size_t dm = (size_t)d->d_model;
+  const size_t dg = dm / (size_t)d->fold;
+  const size_t Fs = (size_t)(d->ffn / d->fold);
+  StreamedCarve c;
+  c.fp = (int64_t)round_up(Fs, 8);
+  c.attn_shard = 4 * dg * dm;
+  c.mlp_shard = (2 * Fs + (size_t)c.fp) * dm;
+  const size_t act = round_up(M * dm * 2, kAlign);
+  size_t at = 0;
+  c.q_off = at;
+  at += act;
+  c.o_off = at;
+  at += act;
+  c.h_off = at;
+  at += mlp_ws_bytes((int64_t)M, (int64_t)Fs);
+  for (int i = 0; i < 2; ++i) {
+    c.slot_a[i] = at;
+    at += round_up(c.attn_shard * 2, kAlign);
+  }
+  for (int i = 0; i < 2; ++i) {
+    c.slot_m[i] = at;
+    at += round_up(c.mlp_shard * 2, kAlign);
+  }
+  // Per attention stream: the two key halves of a head group's attention, fp32 O
+  // [2, M, dg] and log-sum-exp [2, M * heads per group].
+  const size_t hg = (size_t)(d->n_heads / d->fold);
+  for (int i = 0; i < 2; ++i) {
+    c.part[i] = at;
+    at += round_up(2 * M * dg * 4, kAlign) + round_up(2 * M * hg * 4, kAlign);
+  }
+  c.total = at;
+  return c;
+}
+
+int check_streamed_desc(const tsp_layer_desc* desc) {
+  if (int rc = check_desc(desc)) return rc;
+  if (desc->n_heads % desc->fold != 0)
+    return fail(TSP_ERR_SHAPE, "n_heads %d must be a multiple of D=%d for head groups", desc->n_heads, desc->fold);
+  return TSP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tsp_layer_streamed_workspace_size(const tsp_layer_desc* desc) {
+  if (check_streamed_desc(desc) != TSP_OK) return 0;
+  return carve_streamed(desc).total;
+}
+
+int tsp_layer_fwd_streamed(const tsp_layer_desc* desc, const void* x_shard, const void* const* w_attn,
+                           const void* const* w_mlp, void* k_full, void* v_full, void* attn_out, float* mlp_out,
+                           void* ws, size_t ws_bytes, const tsp_stream_t* streams, int32_t n_streams) {
+  if (int rc = check_streamed_desc(desc)) return rc;
+  if (n_streams != 1 && n_streams != 4) return fail(TSP_ERR_SHAPE, "n_streams must be 1 or 4 (got %d)", n_streams);
+  if (desc->batch == 0 || desc->seq_len == 0) return ok();
+  if (!x_shard || !w_attn || !w_mlp || !k_full || !v_full || !attn_out || !mlp_out || !ws || !streams)
+    return fail(TSP_ERR_NULL, "a required pointer is NULL");
+  const int D = desc->fold;
+  for (int j = 0; j < D; ++j) {
+    if (!w_attn[j] || !w_mlp[j]) return fail(TSP_ERR_NULL, "packed shard %d pointer is NULL", j);
+    if (misaligned(w_attn[j]) || misaligned(w_mlp[j]))
+      return fail(TSP_ERR_ALIGN, "packed shard %d pointer is not 16-byte aligned", j);
+  }
+  if (misaligned(x_shard) || misaligned(k_full) || misaligned(v_full) || misaligned(attn_out) ||
+      misaligned(mlp_out) || misaligned(ws))
+    return fail(TSP_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const StreamedCarve c = carve_streamed(desc);
+  if (ws_bytes < c.total) return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, c.total);
+
+  const int B = desc->batch, H = desc->n_heads, hd = desc->head_dim, d = desc->d_model, r = desc->rank;
+  const int64_t S = desc->seq_len;
+  const int M = (int)(B * (S / D));
+  const int Fs = desc->ffn / D;
+  const int hg = H / D;  // heads per group
+  const size_t dg = (size_t)(d / D);
+  const size_t qkv_part = 3 * dg * (size_t)d;  // elements of a shard's [3 dg, d] QKV rows
+  char* base = static_cast<char*>(ws);
+  void* q = base + c.q_off;
+  void* o = base + c.o_off;
+  void* hbuf = base + c.h_off;
+  tsp::bf16_t* slot_a[2] = {reinterpret_cast<tsp::bf16_t*>(base + c.slot_a[0]),
+                            reinterpret_cast<tsp::bf16_t*>(base + c.slot_a[1])};
+  tsp::bf16_t* slot_m[2] = {reinterpret_cast<tsp::bf16_t*>(base + c.slot_m[0]),
+                            reinterpret_cast<tsp::bf16_t*>(base + c.slot_m[1])};
+  float* part[2];
+  float* part_lse[2];
+  for (int i = 0; i < 2; ++i) {
+    part[i] = reinterpret_cast<float*>(base + c.part[i]);
+    part_lse[i] = reinterpret_cast<float*>(base + c.part[i] + round_up(2 * (size_t)M * dg * 4, kAlign));
+  }
+  hipStream_t s0 = static_cast<hipStream_t>(streams[0]);
+  auto pick = [&](int i) { return n_streams == 4 && streams[i] ? static_cast<hipStream_t>(streams[i]) : s0; };
+  hipStream_t comp[2] = {s0, pick(1)};
+  hipStream_t s_wo = pick(2);
+  hipStream_t cp = pick(3);
+
+  hipEvent_t* ev = nullptr;
+  if (int rc = stream_events(&ev, 16)) return rc;
+  hipEvent_t ev_start = ev[0], wo_last = ev[1];
+  hipEvent_t *q_full = ev + 2, *q_free = ev + 4;    // QKV part of an attention slot
+  hipEvent_t *o_full = ev + 6, *o_free = ev + 8;    // W_o part of an attention slot
+  hipEvent_t *m_full = ev + 10, *m_free = ev + 12;  // MLP slot
+  hipEvent_t* attn_done = ev + 14;                  // per attention stream
+  auto rec = [](hipEvent_t e, hipStream_t st) { return hip_status(hipEventRecord(e, st), "hipEventRecord"); };
+  auto wait = [](hipStream_t st, hipEvent_t e) {
+    return hip_status(hipStreamWaitEvent(st, e, 0), "hipStreamWaitEvent");
+  };
+  // Copy `elems` bf16 into a slot after `free_ev` (if any), then record `full_ev`.
+  auto fill = [&](void* dst, const void* src, size_t elems, hipEvent_t free_ev, hipEvent_t full_ev) -> int {
+    if (free_ev)
+      if (int rc = wait(cp, free_ev)) return rc;
+    if (int rc = hip_status(hipMemcpyAsync(dst, src, elems * 2, hipMemcpyDeviceToDeviceNoCU, cp), "shard copy"))
+      return rc;
+    return rec(full_ev, cp);
+  };
+  auto fill_qkv = [&](int t) {
+    return fill(slot_a[t & 1], w_attn[t], qkv_part, t >= 2 ? q_free[t & 1] : nullptr, q_full[t & 1]);
+  };
+  auto fill_wo = [&](int t) {
+    return fill(slot_a[t & 1] + qkv_part, static_cast<const tsp::bf16_t*>(w_attn[t]) + qkv_part, dg * d,
+                t >= 2 ? o_free[t & 1] : nullptr, o_full[t & 1]);
+  };
+  auto fill_mlp = [&](int t) {
+    const int j = ((r - t) % D + D) % D;  // ring order
+    return fill(slot_m[t & 1], w_mlp[j], c.mlp_shard, t >= 2 ? m_free[t & 1] : nullptr, m_full[t & 1]);
+  };
+
+  if (int rc = rec(ev_start, s0)) return rc;
+  for (hipStream_t st : {comp[1], s_wo, cp})
+    if (int rc = wait(st, ev_start)) return rc;
+  for (int t = 0; t < 2 && t < D; ++t) {
+    if (int rc = fill_qkv(t)) return rc;
+    if (int rc = fill_wo(t)) return rc;
+  }
+  for (int t = 0; t < 2 && t < D; ++t)
+    if (int rc = fill_mlp(t)) return rc;
+
+  // Head group t: QKV and attention on comp[t % 2], the W_O partial on s_wo (in order of t,
+  // so the fp32 sum takes the groups in order). A slot's QKV rows are refilled once its QKV
+  // launch is done, its W_o columns once its W_O launch is done.
+  for (int t = 0; t < D; ++t) {
+    const int sl = t & 1;
+    hipStream_t st = comp[sl];
+    if (int rc = wait(st, q_full[sl])) return rc;
+    if (int rc = hip_status(tsp::launch_qkv_group(x_shard, slot_a[sl], t, D, q, k_full, v_full, B, S, D, r, d, st),
+                            "group qkv launch"))
+      return rc;
+    if (t + 2 < D) {
+      if (int rc = rec(q_free[sl], st)) return rc;
+      if (int rc = fill_qkv(t + 2)) return rc;
+    }
+    // Causal attention of the group's heads, every query tile's keys split at S/2 into two
+    // work items (one group has about one tile per CU, and a tile of the later zigzag
+    // chunk sees up to S keys), then the halves merged by log-sum-exp into bf16 O.
+    if (int rc = hip_status(tsp::launch_attn_split(q, k_full, v_full, part[sl], part_lse[sl], B, S, D, r, H, hd,
+                                                   desc->scale, t * hg, hg, (int)(S / 2), st),
+                            "group attention launch"))
+      return rc;
+    if (int rc = hip_status(tsp::launch_attn_merge_halves(part[sl], part_lse[sl], o, B, (int)(S / D), H, hd, t * hg,
+                                                          hg, st),
+                            "group attention merge launch"))
+      return rc;
+    if (int rc = rec(attn_done[sl], st)) return rc;
+    if (int rc = wait(s_wo, attn_done[sl])) return rc;
+    if (int rc = wait(s_wo, o_full[sl])) return rc;
+    if (int rc = hip_status(tsp::launch_wo_group(o, slot_a[sl] + qkv_part, t, D, mlp_out, attn_out, M, d, t, D, s_wo),
+                            "group W_O launch"))
+      return rc;
+    if (t + 2 < D)
+      if (int rc = rec(o_free[sl], s_wo)) return rc;
+    // The W_o columns of group t+1 were released by W_O step t-1; queued here, behind the
+    // QKV rows of group t+2, so that no copy waits behind one that is needed later.
+    if (t + 1 >= 2 && t + 1 < D)
+      if (int rc = fill_wo(t + 1)) return rc;
+  }
+  if (int rc = rec(wo_last, s_wo)) return rc;
+  if (int rc = wait(s0, wo_last)) return rc;
+
+  // MLP ring on streams[0], shard j = (r - t) mod D at step t.
+  for (int t = 0; t < D; ++t) {
+    const int sl = t & 1;
+    const tsp::bf16_t* w1 = slot_m[sl];
+    const tsp::bf16_t* w3 = slot_m[sl] + (size_t)Fs * d;
+    const tsp::bf16_t* w2 = slot_m[sl] + 2 * (size_t)Fs * d;
+    if (int rc = wait(s0, m_full[sl])) return rc;
+    if (int rc = hip_status(tsp::launch_gate_up(attn_out, d, w1, w3, d, hbuf, c.fp, M, Fs, d, s0), "gate/up launch"))
+      return rc;
+    if (int rc = hip_status(tsp::launch_down_acc(hbuf, c.fp, w2, c.fp, mlp_out, d, M, d, Fs, t > 0 ? 1 : 0, s0),
+                            "down projection launch"))
+      return rc;
+    if (t + 2 < D) {
+      if (int rc = rec(m_free[sl], s0)) return rc;
+      if (int rc = fill_mlp(t + 2)) return rc;
+    }
+  }
   return ok();
 }
 

@@ -94,12 +94,21 @@ struct AttnArgs {
   float* lse;
   int key_lo, key_hi;  // key-range attention: key positions [key_lo, key_hi)
   int accumulate;      // key-range attention: merge into (o32, lse) instead of overwriting
+  // Key-range attention, layout of o32 and lse: heads [oh0, oh0 + oH) of a [B, rows, oH, HD]
+  // fp32 O and a [B, oH, rows] lse (oH = H, oh0 = 0 for the range entry point).
+  int oH, oh0;
+  // Split launch (key-range attention with split > 0): two items per tile, keys
+  // [0, split) and [split, S); the item of half 1 writes o32 + part_o and lse + part_l.
+  int split;
+  int64_t part_o, part_l;
   int64_t S;
   int64_t C;
   int rows;  // 2C local rows per sequence
   int D, rank, H;
   int n_qt;   // query tiles per (sequence, head)
-  int items;  // B * H * n_qt
+  int items;  // B * Hrun * n_qt
+  int h0, Hrun;  // heads [h0, h0 + Hrun) of the H in the layout
+  int strided;   // 1: item = block index (consecutive items on different XCDs)
   float scale_log2;
 };
 
@@ -136,22 +145,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
 
-  const int item = xcd_remap(blockIdx.x, a.items);
+  int item = a.strided ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.items);
+  int key_lo = a.key_lo, key_hi = a.key_hi;
+  float* o32 = a.o32;
+  float* lse32 = a.lse;
+  if constexpr (PART) {
+    if (a.split > 0) {  // both halves of a tile are consecutive items
+      const int half = item & 1;
+      item >>= 1;
+      key_lo = half ? a.split : 0;
+      key_hi = half ? (int)a.S : a.split;
+      o32 += half * a.part_o;
+      lse32 += half * a.part_l;
+    }
+  }
   const int bh = item / a.n_qt;
   const int qt = a.n_qt - 1 - (item - bh * a.n_qt);  // heaviest tile of the (b, h) first
-  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const int b = bh / a.Hrun, h = a.h0 + bh - (bh / a.Hrun) * a.Hrun;
   const int row0 = qt * BR;
   int kv_end = (int)zigzag_pos(min(row0 + BR, a.rows) - 1, a.C, a.rank, a.D) + 1;
   int k_base = 0;  // position of the first key of stage 0
   if constexpr (PART) {
-    kv_end = min(kv_end, a.key_hi);
-    k_base = (a.key_lo / BC) * BC;
+    kv_end = min(kv_end, key_hi);
+    k_base = (key_lo / BC) * BC;
   }
   const int n_kt = (kv_end - k_base + BC - 1) / BC;
 
   const int wrow0 = row0 + wave * (32 * QB);
   const int wmin_pos = wrow0 < a.rows ? (int)zigzag_pos(wrow0, a.C, a.rank, a.D) : 0;
   const int64_t tok = (int64_t)a.H * HD;  // elements between consecutive tokens
+  const int64_t otok = (int64_t)a.oH * HD;  // the same in o32
+  const int oh = h - a.oh0;
 
   // This lane's two query rows and their Q fragments (dims 16s + 8hl .. +7).
   int qi[QB], qpos[QB];
@@ -180,14 +204,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // A tile whose keys all lie outside the range: O = 0, lse = -inf, no LDS work (the whole
   // workgroup returns here, before any barrier).
   if constexpr (PART) {
-    if (kv_end <= a.key_lo) {
+    if (kv_end <= key_lo) {
       // accumulate: the range adds nothing to these rows; only the bf16 O is written if asked
       if (a.accumulate && a.o == nullptr) return;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (qi[qb] >= a.rows) continue;
         const int64_t ro = ((int64_t)b * a.rows + qi[qb]) * tok + (int64_t)h * HD;
-        float* op = a.o32 + ro;
+        float* op = o32 + ((int64_t)b * a.rows + qi[qb]) * otok + (int64_t)oh * HD;
 #pragma unroll
         for (int db = 0; db < HD / 32; ++db)
 #pragma unroll
@@ -201,7 +225,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
               if (a.o != nullptr) *reinterpret_cast<uint2*>(a.o + ro + dim) = make_uint2(0u, 0u);
             }
           }
-        if (!a.accumulate && hl == 0) a.lse[((int64_t)b * a.H + h) * a.rows + qi[qb]] = -INFINITY;
+        if (!a.accumulate && hl == 0) lse32[((int64_t)b * a.oH + oh) * a.rows + qi[qb]] = -INFINITY;
       }
       return;
     }
@@ -319,8 +343,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (kstart + 8 * (r >> 2) + 4 * hl + (r & 3) > qpos[qb] ||
-            (PART && (kstart + 8 * (r >> 2) + 4 * hl + (r & 3) < a.key_lo ||
-                      kstart + 8 * (r >> 2) + 4 * hl + (r & 3) >= a.key_hi)))
+            (PART && (kstart + 8 * (r >> 2) + 4 * hl + (r & 3) < key_lo ||
+                      kstart + 8 * (r >> 2) + 4 * hl + (r & 3) >= key_hi)))
           sacc[qb][r] = -INFINITY;
   };
 #if TSP_ATTN_CINIT
@@ -481,7 +505,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     if (t + 3 < n_kt) issue(refill, t + 3);
     const int k0 = k_base + t * BC;
     // causal mask where a key may follow a row; in a key range also at its two ends
-    if (k0 + 31 > wmin_pos || (PART && (k0 < a.key_lo || k0 + 32 > a.key_hi))) mask(s_cur, k0);
+    if (k0 + 31 > wmin_pos || (PART && (k0 < key_lo || k0 + 32 > key_hi))) mask(s_cur, k0);
     qk(kf, s_nxt);  // block 1 of stage t
     note(m_at_nxt);
     load_v(cur, 0, vf);
@@ -490,7 +514,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     close_region(pf);
     if (__ballot(any)) rescale(alpha);
     pv(vf, pf);
-    if (k0 + 63 > wmin_pos || (PART && (k0 + 32 < a.key_lo || k0 + 64 > a.key_hi))) mask(s_nxt, k0 + 32);
+    if (k0 + 63 > wmin_pos || (PART && (k0 + 32 < key_lo || k0 + 64 > key_hi))) mask(s_nxt, k0 + 32);
     qk(kf, s_cur);  // block 0 of stage t+1
     note(m_at_cur);
     load_v(cur, 1, vf);
@@ -521,8 +545,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     for (int qb = 0; qb < QB; ++qb) {
       if (qi[qb] >= a.rows) continue;
       const int64_t ro = ((int64_t)b * a.rows + qi[qb]) * tok + (int64_t)h * HD;
-      float* op = a.o32 + ro;
-      float* lp = a.lse + ((int64_t)b * a.H + h) * a.rows + qi[qb];
+      float* op = o32 + ((int64_t)b * a.rows + qi[qb]) * otok + (int64_t)oh * HD;
+      float* lp = lse32 + ((int64_t)b * a.oH + oh) * a.rows + qi[qb];
       const float lse_b = l_run[qb] > 0.0f ? (m_s[qb] + __log2f(l_run[qb])) * 0.69314718055994531f : -INFINITY;
       // Overwrite: weights (0, 1). Accumulate: the log-sum-exp merge with what the
       // accumulator holds (both lanes of the row read it before lane hl == 0 writes).
@@ -578,14 +602,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
 }  // namespace
 
-hipError_t launch_attn(const void* q, const void* k_full, const void* v_full, void* o, float* lse, int B, int64_t S,
-                       int D, int rank, int H, int hd, float scale, hipStream_t stream) {
+namespace {
+
+// Fields every launch sets the same way; the mode fields start as "full attention, all
+// heads, no key range".
+AttnArgs base_args(const void* q, const void* k_full, const void* v_full, int B, int64_t S, int D, int rank, int H,
+                   int hd, float scale) {
   AttnArgs a;
   a.q = static_cast<const bf16_t*>(q);
   a.k = static_cast<const bf16_t*>(k_full);
   a.v = static_cast<const bf16_t*>(v_full);
-  a.o = static_cast<bf16_t*>(o);
-  a.lse = lse;
+  a.o = nullptr;
+  a.o32 = nullptr;
+  a.lse = nullptr;
   a.S = S;
   a.C = S / (2 * D);
   a.rows = (int)(2 * a.C);
@@ -593,50 +622,83 @@ hipError_t launch_attn(const void* q, const void* k_full, const void* v_full, vo
   a.rank = rank;
   a.H = H;
   a.n_qt = (a.rows + BR - 1) / BR;
+  a.h0 = 0;
+  a.Hrun = H;
+  a.strided = 0;
   a.items = B * H * a.n_qt;
-  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)hd);
-  a.scale_log2 = sc * 1.4426950408889634f;
-  a.o32 = nullptr;
   a.key_lo = 0;
   a.key_hi = (int)S;
   a.accumulate = 0;
+  a.oH = H;
+  a.oh0 = 0;
+  a.split = 0;
+  a.part_o = 0;
+  a.part_l = 0;
+  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)hd);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  return a;
+}
+
+// Heads [h0, h0 + h_run) only.
+bool set_heads(AttnArgs& a, int B, int h0, int h_run) {
+  if (h0 < 0 || h_run <= 0 || h0 + h_run > a.H) return false;
+  a.h0 = h0;
+  a.Hrun = h_run;
+  a.items = B * h_run * a.n_qt;
+  return true;
+}
+
+template <bool PART>
+hipError_t launch(const AttnArgs& a, int hd, hipStream_t stream) {
   if (hd == 128) {
-    hipLaunchKernelGGL((attn_fwd<128, false>), dim3(a.items), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd<128, PART>), dim3(a.items), dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((attn_fwd<64, false>), dim3(a.items), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd<64, PART>), dim3(a.items), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn(const void* q, const void* k_full, const void* v_full, void* o, float* lse, int B, int64_t S,
+                       int D, int rank, int H, int hd, float scale, hipStream_t stream) {
+  AttnArgs a = base_args(q, k_full, v_full, B, S, D, rank, H, hd, scale);
+  a.o = static_cast<bf16_t*>(o);
+  a.lse = lse;
+  return launch<false>(a, hd, stream);
 }
 
 hipError_t launch_attn_range(const void* q, const void* k_full, const void* v_full, float* o32, float* lse, int B,
                              int64_t S, int D, int rank, int H, int hd, float scale, int64_t key_lo, int64_t key_hi,
                              int accumulate, void* o_out, hipStream_t stream) {
-  AttnArgs a;
-  a.q = static_cast<const bf16_t*>(q);
-  a.k = static_cast<const bf16_t*>(k_full);
-  a.v = static_cast<const bf16_t*>(v_full);
+  AttnArgs a = base_args(q, k_full, v_full, B, S, D, rank, H, hd, scale);
   a.o = static_cast<bf16_t*>(o_out);
   a.accumulate = accumulate;
   a.o32 = o32;
   a.lse = lse;
-  a.S = S;
-  a.C = S / (2 * D);
-  a.rows = (int)(2 * a.C);
-  a.D = D;
-  a.rank = rank;
-  a.H = H;
-  a.n_qt = (a.rows + BR - 1) / BR;
-  a.items = B * H * a.n_qt;
   a.key_lo = (int)key_lo;
   a.key_hi = (int)key_hi;
-  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)hd);
-  a.scale_log2 = sc * 1.4426950408889634f;
-  if (hd == 128) {
-    hipLaunchKernelGGL((attn_fwd<128, true>), dim3(a.items), dim3(kThreads), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((attn_fwd<64, true>), dim3(a.items), dim3(kThreads), 0, stream, a);
-  }
-  return hipGetLastError();
+  return launch<true>(a, hd, stream);
+}
+
+hipError_t launch_attn_split(const void* q, const void* k_full, const void* v_full, float* o32, float* lse, int B,
+                             int64_t S, int D, int rank, int H, int hd, float scale, int h0, int h_run, int split,
+                             hipStream_t stream) {
+  AttnArgs a = base_args(q, k_full, v_full, B, S, D, rank, H, hd, scale);
+  if (!set_heads(a, B, h0, h_run) || split <= 0 || split >= S) return hipErrorInvalidValue;
+  a.o32 = o32;
+  a.lse = lse;
+  a.oH = a.Hrun;
+  a.oh0 = a.h0;
+  a.split = split;
+  a.part_o = (int64_t)B * a.rows * a.Hrun * hd;
+  a.part_l = (int64_t)B * a.Hrun * a.rows;
+  a.items *= 2;
+  // Strided (consecutive items on different XCDs), heaviest tiles first: every XCD gets an
+  // even share of the heavy halves. (Measured faster than XCD-contiguous runs of a head's
+  // tiles with heavy and light tiles alternating.)
+  a.strided = 1;
+  return launch<true>(a, hd, stream);
 }
 
 // Log-sum-exp merge of a partial attention into a running one, one wave per (sequence,
@@ -678,6 +740,49 @@ __global__ __launch_bounds__(256) void attn_merge(float* o_acc, float* lse_acc, 
     for (int e = 0; e < PER; ++e) po[e] = to_bf16(r[e]);
   }
   if (lane == 0) lse_acc[li] = lnew;
+}
+
+// The two halves of a split launch merged into bf16 O: one wave per (sequence, row, head
+// of the group); partials in the group's [B, rows, h_run, HD] / [B, h_run, rows] layout,
+// O in the [B, rows, H, HD] layout at heads h0 .. h0 + h_run - 1.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_merge_halves(const float* o32, const float* lse, int64_t part_o,
+                                                         int64_t part_l, bf16_t* o_out, int64_t units, int rows,
+                                                         int h_run, int H, int h0) {
+  constexpr int PER = HD / 64;
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * rows + row) * h_run + h
+  if (u >= units) return;
+  const int lane = threadIdx.x & 63;
+  const int h = (int)(u % h_run);
+  const int64_t br = u / h_run;
+  const int row = (int)(br % rows);
+  const int64_t b = br / rows;
+  const int64_t li = (b * h_run + h) * rows + row;
+  const float la = lse[li], lb = lse[part_l + li];
+  const float m = fmaxf(la, lb);  // finite: half 0 holds key 0, which every row sees
+  const float ea = __expf(la - m), eb = __expf(lb - m);
+  const float wa = ea / (ea + eb), wb = eb / (ea + eb);
+  const float* pa = o32 + u * HD + lane * PER;
+  const float* pb = o32 + part_o + u * HD + lane * PER;
+  bf16_t* po = o_out + (br * H + h0 + h) * HD + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) po[e] = to_bf16(wa * pa[e] + wb * pb[e]);
+}
+
+hipError_t launch_attn_merge_halves(const float* o32, const float* lse, void* o_out, int B, int rows, int H, int hd,
+                                    int h0, int h_run, hipStream_t stream) {
+  if (h0 < 0 || h_run <= 0 || h0 + h_run > H) return hipErrorInvalidValue;
+  const int64_t units = (int64_t)B * rows * h_run;
+  const int64_t part_o = units * hd, part_l = units;
+  const dim3 grid((unsigned)((units + 3) / 4));
+  if (hd == 128) {
+    hipLaunchKernelGGL(attn_merge_halves<128>, grid, dim3(256), 0, stream, o32, lse, part_o, part_l,
+                       static_cast<bf16_t*>(o_out), units, rows, h_run, H, h0);
+  } else {
+    hipLaunchKernelGGL(attn_merge_halves<64>, grid, dim3(256), 0, stream, o32, lse, part_o, part_l,
+                       static_cast<bf16_t*>(o_out), units, rows, h_run, H, h0);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part, void* o_out,

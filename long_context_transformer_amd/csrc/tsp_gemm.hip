@@ -84,15 +84,17 @@ struct EpiQKV {
   bf16_t* q;  // may be null
   bf16_t* k;
   bf16_t* v;
-  int d;       // model width: columns [0,d) are Q, [d,2d) K, [2d,3d) V
+  int d;       // model width (row stride of q, k, v)
+  int dg;      // output columns [0,dg) are Q, [dg,2dg) K, [2dg,3dg) V (dg = d for all heads)
+  int col0;    // model column of output column 0 of each part (a head group's first column)
   int R;       // local rows per sequence (2C)
   int64_t C;   // zigzag chunk length
   int rank, D;
   int64_t S;
   __device__ __forceinline__ void operator()(int m, int n, const f32x4& val, int M, int N) const {
     if (m >= M || n >= N) return;
-    const int which = n / d;
-    const int col = n - which * d;
+    const int which = n / dg;
+    const int col = col0 + n - which * dg;
     const uint2 packed = pack_bf16x4(val[0], val[1], val[2], val[3]);
     if (which == 0) {
       if (q) *reinterpret_cast<uint2*>(q + (int64_t)m * d + col) = packed;
@@ -123,6 +125,21 @@ struct EpiSwiGLU {
     } else {
       for (int e = 0; e < 4 && n + e < N; ++e) p[e] = to_bf16(r[e]);
     }
+  }
+};
+
+// fp32 accumulator plus this partial, stored as bf16 (the last step of an fp32
+// accumulation; first: the partial alone).
+struct EpiAccBf16 {
+  const float* acc;
+  bf16_t* out;
+  int64_t ld;
+  int first;
+  __device__ __forceinline__ void operator()(int m, int n, const f32x4& v, int M, int N) const {
+    if (m >= M || n >= N) return;
+    f32x4 o = v;
+    if (!first) o += *reinterpret_cast<const f32x4*>(acc + (int64_t)m * ld + n);
+    *reinterpret_cast<uint2*>(out + (int64_t)m * ld + n) = pack_bf16x4(o[0], o[1], o[2], o[3]);
   }
 };
 
@@ -591,9 +608,29 @@ hipError_t launch_qkv(const void* x, const void* w_qkv, void* q_out, void* k_ful
   const int64_t C = S / (2 * D);
   const int R = (int)(2 * C);
   Operands op{static_cast<const bf16_t*>(x), d, static_cast<const bf16_t*>(w_qkv), nullptr, d, B * R, 3 * d, d};
-  EpiQKV epi{static_cast<bf16_t*>(q_out), static_cast<bf16_t*>(k_full), static_cast<bf16_t*>(v_full), d, R, C, rank, D,
-             S};
+  EpiQKV epi{static_cast<bf16_t*>(q_out), static_cast<bf16_t*>(k_full), static_cast<bf16_t*>(v_full), d, d, 0, R, C, rank,
+             D, S};
   return run_single(op, epi, stream);
+}
+
+hipError_t launch_qkv_group(const void* x, const void* w_qkv_g, int group, int groups, void* q_out, void* k_full,
+                            void* v_full, int B, int64_t S, int D, int rank, int d, hipStream_t stream) {
+  const int64_t C = S / (2 * D);
+  const int R = (int)(2 * C);
+  const int dg = d / groups;
+  Operands op{static_cast<const bf16_t*>(x), d, static_cast<const bf16_t*>(w_qkv_g), nullptr, d, B * R, 3 * dg, d};
+  EpiQKV epi{static_cast<bf16_t*>(q_out), static_cast<bf16_t*>(k_full), static_cast<bf16_t*>(v_full), d, dg, group * dg, R,
+             C, rank, D, S};
+  return run_single(op, epi, stream);
+}
+
+hipError_t launch_wo_group(const void* o, const void* w_o_g, int group, int groups, float* acc, void* out, int M, int d,
+                           int step, int steps, hipStream_t stream) {
+  const int dg = d / groups;
+  Operands op{static_cast<const bf16_t*>(o) + (int64_t)group * dg, d, static_cast<const bf16_t*>(w_o_g), nullptr, dg, M,
+              d, dg};
+  if (step == steps - 1) return run_single(op, EpiAccBf16{acc, static_cast<bf16_t*>(out), d, step == 0 ? 1 : 0}, stream);
+  return run_single(op, EpiAcc{acc, d, step > 0 ? 1 : 0}, stream);
 }
 
 hipError_t launch_proj_bf16(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc, int M, int N,

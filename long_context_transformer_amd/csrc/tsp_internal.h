@@ -12,6 +12,18 @@ namespace tsp {
 hipError_t launch_qkv(const void* x, const void* w_qkv, void* q_out, void* k_full, void* v_full,
                       int B, int64_t S, int D, int rank, int d, hipStream_t stream);
 
+// QKV projection of head group `group` of `groups` (its packed shard w_qkv_g: [3 d/groups, d],
+// the group's W_q, W_k and W_v rows): Q columns [group*dg, (group+1)*dg) of q_out, and the
+// same columns of the rank's K/V rows.
+hipError_t launch_qkv_group(const void* x, const void* w_qkv_g, int group, int groups, void* q_out, void* k_full,
+                            void* v_full, int B, int64_t S, int D, int rank, int d, hipStream_t stream);
+
+// Partial W_O of head group `group`: acc[M, d] (=, +=) O[:, group cols] w_o_g^T with w_o_g
+// [d, d/groups] (the group's W_o columns); at the last step (step == steps - 1) the sum is
+// stored as bf16 to out instead.
+hipError_t launch_wo_group(const void* o, const void* w_o_g, int group, int groups, float* acc, void* out, int M, int d,
+                           int step, int steps, hipStream_t stream);
+
 // Plain projection C[M, N] = A[M, K] W[N, K]^T, bf16 out (step a4, W_O).
 hipError_t launch_proj_bf16(const void* a, int64_t lda, const void* w, int64_t ldw, void* c,
                             int64_t ldc, int M, int N, int K, hipStream_t stream);
@@ -47,6 +59,17 @@ hipError_t launch_attn(const void* q, const void* k_full, const void* v_full, vo
 // those keys) [B, 2C, H, hd] and lse [B, H, 2C]; rows with no such key get 0 and -inf.
 // accumulate != 0: log-sum-exp merge into (o32, lse) instead (rows without such keys
 // untouched); o_out (bf16, may be null) receives the resulting O of every row.
+// Causal attention of heads [h0, h0 + h_run) as a split launch: two items per query tile,
+// keys [0, split) and [split, S), each writing fp32 O (normalised over its keys) and the
+// log-sum-exp; half 0 at o32 / lse, half 1 at o32 + B rows h_run hd / lse + B h_run rows,
+// in the group's [B, rows, h_run, hd] / [B, h_run, rows] layout. Every item covers at most
+// max(split, S - split) keys; launch_attn_merge_halves then writes bf16 O.
+hipError_t launch_attn_split(const void* q, const void* k_full, const void* v_full, float* o32, float* lse, int B,
+                             int64_t S, int D, int rank, int H, int hd, float scale, int h0, int h_run, int split,
+                             hipStream_t stream);
+hipError_t launch_attn_merge_halves(const float* o32, const float* lse, void* o_out, int B, int rows, int H, int hd,
+                                    int h0, int h_run, hipStream_t stream);
+
 hipError_t launch_attn_range(const void* q, const void* k_full, const void* v_full, float* o32, float* lse, int B,
                              int64_t S, int D, int rank, int H, int hd, float scale, int64_t key_lo, int64_t key_hi,
                              int accumulate, void* o_out, hipStream_t stream);

@@ -55,6 +55,10 @@ _SIGS = {
     "tsp_attn_fwd_range": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32, _I32,
                                   ctypes.c_float, _I64, _I64, _I32, _VP, _VP]),
     "tsp_attn_merge": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32, _VP]),
+    "tsp_layer_streamed_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc)]),
+    "tsp_layer_fwd_streamed": (_I32, [ctypes.POINTER(LayerDesc), _VP, ctypes.POINTER(_VP),
+                                      ctypes.POINTER(_VP), _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                                      ctypes.POINTER(_VP), _I32]),
     "tsp_timing_start": (_I32, [_I32]),
     "tsp_timing_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32, ctypes.POINTER(_I32)]),
 }
@@ -180,6 +184,65 @@ def layer_fwd(desc, x_shard, w_qkv, w_o, w1, w3, w2, k_full, v_full, attn_out, m
     _check(load().tsp_layer_fwd(ctypes.byref(desc), _ptr(x_shard), _ptr(w_qkv), _ptr(w_o), a1, a3, a2,
                                 _ptr(k_full), _ptr(v_full), _ptr(attn_out), _ptr(mlp_out), _ptr(ws),
                                 ws_bytes, _stream(stream, x_shard)))
+
+
+def layer_streamed_workspace_size(desc):
+    return int(load().tsp_layer_streamed_workspace_size(ctypes.byref(desc)))
+
+
+def layer_fwd_streamed(desc, x_shard, w_attn, w_mlp, k_full, v_full, attn_out, mlp_out, ws,
+                       ws_bytes=None, stream=None, streams=None):
+    """w_attn, w_mlp: sequences of D packed shards (pack_attn_shards / pack_mlp_shards).
+    streams: None (everything on `stream`, no overlap) or three more streams: the second
+    attention stream, the W_O stream and the copy stream."""
+    D = desc.fold
+    arr = _VP * D
+    aa = arr(*[_ptr(t) for t in w_attn])
+    am = arr(*[_ptr(t) for t in w_mlp])
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    st = _stream(stream, x_shard)
+    if streams is None:
+        sv, n = (_VP * 1)(st), 1
+    else:
+        if len(streams) != 3:
+            raise ValueError("streams: the second attention stream, the W_O stream, the copy stream")
+        sv, n = (_VP * 4)(st, *[_stream(x) for x in streams]), 4
+    _check(load().tsp_layer_fwd_streamed(ctypes.byref(desc), _ptr(x_shard), aa, am, _ptr(k_full),
+                                         _ptr(v_full), _ptr(attn_out), _ptr(mlp_out), _ptr(ws),
+                                         ws_bytes, sv, n))
+
+
+def pack_attn_shards(w_qkv, w_o, D):
+    """Weight layout helper: the D packed attention shards of a [3d, d] W_qkv (Q, K, V row
+    blocks) and a [d, d] W_o, as contiguous bf16 tensors of 4 (d/D) d elements each: the
+    group's W_q, W_k, W_v rows, then its W_o columns as a [d, d/D] row-major block."""
+    import torch
+    d = w_o.shape[0]
+    dg = d // D
+    out = []
+    for j in range(D):
+        rows = [w_qkv[p * d + j * dg:p * d + (j + 1) * dg] for p in range(3)]
+        cols = w_o[:, j * dg:(j + 1) * dg].contiguous()
+        out.append(torch.cat([r.reshape(-1) for r in rows] + [cols.reshape(-1)]).contiguous())
+    return out
+
+
+def pack_mlp_shards(w1, w3, w2, D):
+    """Weight layout helper: the D packed MLP shards of W1, W3 [F, d] and W2 [d, F], as
+    contiguous bf16 tensors: shard j's W1 rows, W3 rows ([F/D, d] each), then its W2
+    columns as [d, F/D] with row stride round_up(F/D, 8) (pad columns zero)."""
+    import torch
+    F, d = w1.shape
+    Fs = F // D
+    fp = (Fs + 7) // 8 * 8
+    out = []
+    for j in range(D):
+        sl = slice(j * Fs, (j + 1) * Fs)
+        w2p = torch.zeros((d, fp), dtype=w2.dtype, device=w2.device)
+        w2p[:, :Fs] = w2[:, sl]
+        out.append(torch.cat([w1[sl].reshape(-1), w3[sl].reshape(-1), w2p.reshape(-1)]).contiguous())
+    return out
 
 
 PHASES = ("qkv", "attention", "w_o", "mlp")

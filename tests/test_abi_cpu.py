@@ -160,6 +160,41 @@ def test_layer_errors():
     assert _code(f, bad, A, A, A, sh, sh, sh, A, A, A, A, A, ws, 0) == 2
 
 
+def test_streamed_layer_workspace_and_errors():
+    good = _desc()
+    M, d, Fs, dg = 64, 256, 172, 64
+    fp = 176
+    act = M * d * 2
+    rup = lambda x: (x + 255) // 256 * 256
+    hg = 1  # heads per group
+    part = rup(2 * M * dg * 4) + rup(2 * M * hg * 4)  # two key halves: fp32 O and lse
+    want = (2 * rup(act) + rup(M * fp * 2) + 2 * rup(4 * dg * d * 2) + 2 * rup((2 * Fs + fp) * d * 2)
+            + 2 * part)
+    ws = tsp.layer_streamed_workspace_size(good)
+    assert ws == want
+    # H % D != 0: a head group must hold whole heads
+    assert tsp.layer_streamed_workspace_size(_desc(n_heads=2, head_dim=128)) == 0
+    sh = [A] * 4
+    f = tsp.layer_fwd_streamed
+    assert _code(f, _desc(n_heads=2, head_dim=128), A, sh, sh, A, A, A, A, A, ws, 0) == 2
+    assert _code(f, _desc(S=100), A, sh, sh, A, A, A, A, A, ws, 0) == 2
+    assert _code(f, _desc(rank=5), A, sh, sh, A, A, A, A, A, ws, 0) == 3
+    assert _code(f, good, A, [A, None, A, A], sh, A, A, A, A, A, ws, 0) == 1
+    assert _code(f, good, A, sh, [A, A, A, MIS], A, A, A, A, A, ws, 0) == 6
+    assert _code(f, good, A, sh, sh, A, A, MIS, A, A, ws, 0) == 6
+    assert _code(f, good, A, sh, sh, A, A, A, None, A, ws, 0) == 1
+    assert _code(f, good, A, sh, sh, A, A, A, A, A, ws - 1, 0) == 5
+    with pytest.raises(ValueError):  # the binding takes exactly three extra streams
+        f(good, A, sh, sh, A, A, A, A, A, ws, 0, [0, 0])
+    lib = tsp.load()
+    arr = (ctypes.c_void_p * 4)()
+    aa = (ctypes.c_void_p * 4)(*([A] * 4))
+    for n in (0, 2, 3, 5):
+        assert lib.tsp_layer_fwd_streamed(ctypes.byref(good), A, aa, aa, A, A, A, A, A, ws, arr, n) == 2
+    assert lib.tsp_layer_fwd_streamed(ctypes.byref(good), A, aa, aa, A, A, A, A, A, ws, None, 1) == 1
+    tsp.layer_fwd_streamed(_desc(B=0), None, [None] * 4, [None] * 4, None, None, None, None, None, 0)
+
+
 def test_empty_problems_are_noops():
     """B = 0, S = 0 or M = 0: shape checks still apply, then TSP_OK with no pointer read
     (NULL pointers, as torch gives for empty tensors) and no launch (none can happen here:

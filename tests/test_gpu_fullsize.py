@@ -76,8 +76,9 @@ class LayerRig:
         self.w2s = [w2[:, j * Fs:(j + 1) * Fs].contiguous() for j in range(D)]
         self.kf, self.vf = nan_bf16((B, S, d)), nan_bf16((B, S, d))
         self.peers_of = None
+        self.packed = None
 
-    def run(self, rank):
+    def run(self, rank, streamed=False):
         w = self.w
         B, S, D, H, hd, d, F = w.B, w.S, w.D, w.n_heads, w.head_dim, w.d_model, w.ffn
         if self.peers_of is None:
@@ -90,18 +91,31 @@ class LayerRig:
         self.peers_of = rank
         xs = shard_rows(self.x_full, S, D, rank)
         desc = tsp.make_desc(B, S, D, rank, d, H, hd, F)
-        ws = torch.empty(tsp.layer_workspace_size(desc), dtype=torch.uint8, device="cuda")
         a = torch.empty((B, S // D, d), dtype=torch.bfloat16, device="cuda")
         y = torch.full((B, S // D, d), float("nan"), dtype=torch.float32, device="cuda")
-        tsp.layer_fwd(desc, xs, self.w_qkv, self.w_o, self.w1s, self.w3s, self.w2s, self.kf, self.vf,
-                      a, y, ws)
+        if streamed:
+            if self.packed is None:
+                w1 = torch.cat(self.w1s)
+                w3 = torch.cat(self.w3s)
+                w2 = torch.cat(self.w2s, dim=1)
+                self.packed = (tsp.pack_attn_shards(self.w_qkv, self.w_o, D), tsp.pack_mlp_shards(w1, w3, w2, D))
+                del w1, w3, w2
+            ws = torch.empty(tsp.layer_streamed_workspace_size(desc), dtype=torch.uint8, device="cuda")
+            streams = [torch.cuda.Stream() for _ in range(3)]
+            torch.cuda.synchronize()
+            tsp.layer_fwd_streamed(desc, xs, self.packed[0], self.packed[1], self.kf, self.vf, a, y, ws,
+                                   streams=streams)
+        else:
+            ws = torch.empty(tsp.layer_workspace_size(desc), dtype=torch.uint8, device="cuda")
+            tsp.layer_fwd(desc, xs, self.w_qkv, self.w_o, self.w1s, self.w3s, self.w2s, self.kf, self.vf,
+                          a, y, ws)
         torch.cuda.synchronize()
         idx = torch.from_numpy(tsp.zigzag_index(S, D, rank)).cuda()
         assert bool(torch.isfinite(self.kf[:, idx]).all()) and bool(torch.isfinite(self.vf[:, idx]).all())
         return a, y
 
 
-def check_layer_workload(name, ranks, batches):
+def check_layer_workload(name, ranks, batches, streamed=False):
     w0 = synth.WORKLOADS[name]
     print(f"full-size layer {name}: generating inputs", flush=True)
     inputs = synth.layer_inputs(w0)
@@ -115,8 +129,9 @@ def check_layer_workload(name, ranks, batches):
         kv[b] = (x_b, *oracle_kv(x_b, f64w["w_qkv"], d, H))
     for r in ranks:
         w = w0.with_rank(r)
-        print(f"  rank {r}: tsp_layer_fwd B={w.B} S={w.S} D={w.D}", flush=True)
-        a, y = rig.run(r)
+        entry = "tsp_layer_fwd_streamed" if streamed else "tsp_layer_fwd"
+        print(f"  rank {r}: {entry} B={w.B} S={w.S} D={w.D}", flush=True)
+        a, y = rig.run(r, streamed=streamed)
         a_h, y_h = host_f64(a), host_f64(y)
         idx = O.zigzag_index(w.S, w.D, r)
         rows = sample_rows(w.C, seed=7000 + 10 * w0.wid + r)
@@ -142,6 +157,15 @@ def test_fullsize_layer_s128k():
 
 def test_fullsize_layer_b4_s64k():
     check_layer_workload("7b_b4_s64k_d8", ranks=[0], batches=[0, 3])
+
+
+def test_fullsize_layer_streamed_s128k():
+    """The weight-streamed layer (two slots per weight kind, copies on their own stream)."""
+    check_layer_workload("7b_s128k_d8", ranks=[0], batches=[0], streamed=True)
+
+
+def test_fullsize_layer_streamed_s32k_ranks():
+    check_layer_workload("7b_s32k_d8", ranks=[3, 7], batches=[0], streamed=True)
 
 
 # ------------------------------------------------------------- attention alone, per head
