@@ -342,6 +342,9 @@ def main():
                     help="also time chunked-arrival attention (range launches + log-sum-exp merges)")
     ap.add_argument("--streamed", action="store_true",
                     help="also time the weight-streamed layer (two slots, copy stream) against this one")
+    ap.add_argument("--memory", default=None,
+                    help="also measure one rank's device memory for every workload (weight-streamed layer) "
+                    "against the analytic per-layout counts; one JSON line each to this file")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB plain copy kernel first (counter calibration)")
     ap.add_argument("--sweep", default=None, help="also time every workload (and every rank of the "
@@ -424,6 +427,17 @@ def main():
     if streamed:
         out["weight_streamed_layer"] = streamed
     print(json.dumps(out), flush=True)
+
+    if args.memory:
+        from long_context_transformer_amd import memory
+        del st
+        torch.cuda.empty_cache()
+        with open(args.memory, "w") as f:
+            for name, base in synth.WORKLOADS.items():
+                line = memory.measure_streamed(base.with_rank(0), 0)
+                f.write(json.dumps(line) + "\n")
+                f.flush()
+                print("# memory " + json.dumps(line), file=sys.stderr, flush=True)
 
     if args.sweep:
         with open(args.sweep, "w") as f:
