@@ -472,26 +472,37 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) acc[nb][mi][ni] = f32x16{};
 
+  // The fragments of k step ks+1 are read from LDS while the MFMAs of step ks run (two
+  // register sets), so only the first step of a stage waits for its reads.
   auto compute = [&] __device__(const char* st) {
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      bf16x8 af[MI];
-      bf16x8 bfr[NB][NI];
+    bf16x8 af[2][MI];
+    bf16x8 bfr[2][NB][NI];
+    auto load = [&] __device__(int ks, int b) {
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        af[mi] = as_bf16x8(*reinterpret_cast<const uint4*>(st + (wm * WM + 32 * mi) * ROWB + fo[ks]));
+        af[b][mi] = as_bf16x8(*reinterpret_cast<const uint4*>(st + (wm * WM + 32 * mi) * ROWB + fo[ks]));
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
-          bfr[nb][ni] = as_bf16x8(
+          bfr[b][nb][ni] = as_bf16x8(
               *reinterpret_cast<const uint4*>(st + ATILE + nb * BTILE + (wn * WN + 32 * ni) * ROWB + fo[ks]));
+    };
+    load(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int b = ks & 1;
+      if (ks + 1 < KSTEPS) load(ks + 1, b ^ 1);
+      // keep the next step's reads above this step's MFMAs (the scheduler would otherwise
+      // sink them to their uses and reuse one register set)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni) acc[nb][mi][ni] = mfma32x32x16(bfr[nb][ni], af[mi], acc[nb][mi][ni]);
+          for (int ni = 0; ni < NI; ++ni)
+            acc[nb][mi][ni] = mfma32x32x16(bfr[b][nb][ni], af[b][mi], acc[nb][mi][ni]);
     }
   };
 
