@@ -103,15 +103,17 @@ def test_streamed_tiny_all_ranks_glued():
 
 @pytest.mark.parametrize("name", ["tiny_s256_d4", "7b_s16k_d8", "7b_s128k_d8"])
 def test_streamed_memory_footprint(name):
-    """The rank's buffers for tsp_layer_fwd_streamed are exactly the analytic per-rank count
-    (up to the caching allocator's 512-byte rounding per tensor), and a call changes neither
-    the device's free memory nor the allocator's peak: the library allocates nothing."""
+    """The rank's buffers for tsp_layer_fwd_streamed are exactly the analytic per-rank count,
+    and a call changes neither the device's free memory nor the allocator's peak: the library
+    allocates nothing. (The allocator's own count of those tensors may exceed their sizes by
+    up to 1 MiB each: it rounds to 512 bytes and does not split a cached block when less than
+    1 MiB would remain.)"""
     from long_context_transformer_amd import memory
     print(f"memory footprint {name}", flush=True)
     r = memory.measure_streamed(synth.WORKLOADS[name], 0)
     print(f"  owned {r['measured_owned_bytes']} tensors {r['owned_tensor_bytes']} "
           f"analytic {r['analytic_tsp_streamed_bytes']} free change {r['free_bytes_change_during_call']}", flush=True)
     assert r["owned_tensor_bytes"] == r["analytic_tsp_streamed_bytes"]
-    assert 0 <= r["measured_owned_bytes"] - r["owned_tensor_bytes"] < 8 * 512
+    assert 0 <= r["measured_owned_bytes"] - r["owned_tensor_bytes"] <= 8 * (1 << 20)
     assert r["free_bytes_change_during_call"] == 0
     assert r["allocator_peak_growth_during_call"] == 0
