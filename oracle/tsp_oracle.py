@@ -64,6 +64,7 @@ __all__ = [
     "layer_flops",
     "attention_range",
     "lse_merge",
+    "causal_attention_bwd",
 ]
 
 
@@ -144,6 +145,55 @@ def causal_attention(q, q_pos, k, v, scale=None, row_block=512):
                 o[b, r0:r1, h, :] = (e / z) @ vv
                 lse[b, h, r0:r1] = (m + np.log(z))[:, 0]
     return o, lse
+
+
+def causal_attention_bwd(q, q_pos, k, v, d_o, scale=None, row_block=512):
+    """Gradients of causal_attention with respect to q, k and v, given the gradient d_o of
+    its output o. [TSP title: training; the pages do not describe the backward pass, so
+    this is the derivative of the forward definition above]
+
+    With s_ij = scale q_i.k_j over the visible keys (j <= p_i) and P_i = softmax_j(s_ij),
+    o_i = sum_j P_ij v_j. Differentiating:
+      dv_j  = sum_i P_ij do_i                       (v enters o linearly)
+      dP_ij = do_i . v_j
+      ds_ij = P_ij (dP_ij - sum_l P_il dP_il)        (Jacobian of the softmax of row i)
+      dq_i  = scale sum_j ds_ij k_j,   dk_j = scale sum_i ds_ij q_i
+    q, q_pos, k, v as in causal_attention; d_o [B, n, H, hd].
+    Returns (dq [B, n, H, hd], dk [B, S, H, hd], dv [B, S, H, hd]); keys after every
+    query's position get zero gradient. For one rank, dk and dv are its contributions:
+    the gradient of the whole sequence's K and V is their sum over the ranks.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d_o = np.asarray(d_o, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    B, n, H, hd = q.shape
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(hd)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, n, row_block):
+                r1 = min(n, r0 + row_block)
+                pos = q_pos[r0:r1]
+                kmax = int(pos.max()) + 1
+                kk = k[b, :kmax, h, :]
+                vv = v[b, :kmax, h, :]
+                qq = q[b, r0:r1, h, :]
+                g = d_o[b, r0:r1, h, :]
+                s = (qq @ kk.T) * scale
+                s = np.where(causal_scores_mask(pos, kmax), s, -np.inf)
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                p = e / e.sum(axis=1, keepdims=True)
+                dv[b, :kmax, h, :] += p.T @ g
+                dp = g @ vv.T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, r0:r1, h, :] = scale * (ds @ kk)
+                dk[b, :kmax, h, :] += scale * (ds.T @ qq)
+    return dq, dk, dv
 
 
 def attention_range(q, q_pos, k, v, key_lo, key_hi, scale=None, row_block=512):

@@ -328,12 +328,94 @@ def pin_merge_identity():
     assert np.all(eo == 0) and np.all(el == -np.inf)
 
 
+def _attn_loss(q, pos, k, v, g):
+    o, _ = O.causal_attention(q, pos, k, v)
+    return float((o * g).sum())
+
+
+def pin_attention_bwd_finite_differences():
+    """Every gradient entry of causal_attention_bwd against a central difference of the
+    forward oracle's loss sum(o * d_o), on zigzag rows of a tiny sequence."""
+    rng = _rng(31)
+    B, S, D, r, H, hd = 1, 16, 2, 1, 2, 4
+    pos = O.zigzag_index(S, D, r)
+    q = rng.standard_normal((B, S // D, H, hd))
+    k, v = rng.standard_normal((B, S, H, hd)), rng.standard_normal((B, S, H, hd))
+    g = rng.standard_normal((B, S // D, H, hd))
+    dq, dk, dv = O.causal_attention_bwd(q, pos, k, v, g)
+    eps = 1e-6
+    for name, x, dx in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[i] += eps
+            xm[i] -= eps
+            args = {"q": q, "k": k, "v": v}
+            lp = _attn_loss(**{**args, name: xp}, pos=pos, g=g)
+            lm = _attn_loss(**{**args, name: xm}, pos=pos, g=g)
+            num[i] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(dx, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def pin_attention_bwd_vs_autograd():
+    """Against torch autograd (CPU, float64) through an explicit masked softmax, with a
+    scale argument and two rank maps; and the invariants: the keys' dk sum to zero per
+    (sequence, head) (softmax rows sum to one), and the keys' dv sum equals the queries'
+    d_o sum."""
+    import torch
+    rng = _rng(37)
+    B, S, D, H, hd = 2, 32, 4, 3, 8
+    for r, scale in ((0, None), (3, 0.7)):
+        pos = O.zigzag_index(S, D, r)
+        q = rng.standard_normal((B, S // D, H, hd))
+        k, v = rng.standard_normal((B, S, H, hd)), rng.standard_normal((B, S, H, hd))
+        g = rng.standard_normal((B, S // D, H, hd))
+        dq, dk, dv = O.causal_attention_bwd(q, pos, k, v, g, scale=scale)
+        tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+        sc = (1.0 / np.sqrt(hd)) if scale is None else scale
+        s = torch.einsum("bihd,bjhd->bhij", tq, tk) * sc
+        mask = torch.tensor(np.arange(S)[None, :] <= pos[:, None])
+        s = s.masked_fill(~mask, float("-inf"))
+        o = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, dim=-1), tv)
+        (o * torch.tensor(g)).sum().backward()
+        np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-10)
+        np.testing.assert_allclose(dv.sum(axis=1), g.sum(axis=1), rtol=1e-10, atol=1e-10)
+        assert np.all(dk[:, pos.max() + 1:] == 0) and np.all(dv[:, pos.max() + 1:] == 0)
+
+
+def pin_attention_bwd_ranks_sum():
+    """Summed over the D ranks, the ranks' dk and dv equal those of the whole sequence at
+    D = 1, and the ranks' dq, placed at their positions, equal its dq."""
+    rng = _rng(41)
+    B, S, D, H, hd = 1, 24, 3, 2, 4
+    q_all = rng.standard_normal((B, S, H, hd))
+    k, v = rng.standard_normal((B, S, H, hd)), rng.standard_normal((B, S, H, hd))
+    g_all = rng.standard_normal((B, S, H, hd))
+    fq, fk, fv = O.causal_attention_bwd(q_all, np.arange(S), k, v, g_all)
+    sk, sv, sq = np.zeros_like(fk), np.zeros_like(fv), np.zeros_like(fq)
+    for r in range(D):
+        idx = O.zigzag_index(S, D, r)
+        dq, dk, dv = O.causal_attention_bwd(q_all[:, idx], idx, k, v, g_all[:, idx])
+        sk += dk
+        sv += dv
+        sq[:, idx] = dq
+    np.testing.assert_allclose(sk, fk, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(sv, fv, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(sq, fq, rtol=1e-10, atol=1e-12)
+
+
 PINS = [pin_zigzag_golden, pin_zigzag_partition, pin_zigzag_balance, pin_zigzag_identity,
         pin_attention_vs_brute, pin_attention_vs_library, pin_attention_concat_ranks,
         pin_attention_special_cases, pin_attention_scale, pin_silu_closed_form,
         pin_mlp_vs_brute, pin_mlp_shards_sum, pin_layer_vs_brute, pin_layer_concat_ranks,
         pin_layer_rows_subset, pin_layer_flops, pin_range_vs_brute, pin_range_merge_equals_full,
-        pin_merge_identity]
+        pin_merge_identity, pin_attention_bwd_finite_differences, pin_attention_bwd_vs_autograd,
+        pin_attention_bwd_ranks_sum]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -394,7 +476,37 @@ def _bad_merge(o_a, lse_a, o_b, lse_b):
     return o, lse
 
 
+_good_bwd = O.causal_attention_bwd
+
+
+def _bad_bwd_no_rowsum(q, q_pos, k, v, d_o, scale=None, row_block=512):
+    # drops the softmax Jacobian's row term: ds = P dP
+    q, k, v, d_o = (np.asarray(a, dtype=np.float64) for a in (q, k, v, d_o))
+    B, n, H, hd = q.shape
+    sc = 1.0 / np.sqrt(hd) if scale is None or scale <= 0 else scale
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            s = (q[b, :, h] @ k[b, :, h].T) * sc
+            s = np.where(O.causal_scores_mask(q_pos, k.shape[1]), s, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dv[b, :, h] = p.T @ d_o[b, :, h]
+            ds = p * (d_o[b, :, h] @ v[b, :, h].T)
+            dq[b, :, h] = sc * ds @ k[b, :, h]
+            dk[b, :, h] = sc * ds.T @ q[b, :, h]
+    return dq, dk, dv
+
+
+def _bad_bwd_unscaled_dk(q, q_pos, k, v, d_o, scale=None, row_block=512):
+    dq, dk, dv = _good_bwd(q, q_pos, k, v, d_o, scale, row_block)
+    hd = np.asarray(q).shape[-1]
+    return dq, dk * np.sqrt(hd), dv  # the scale left out of dk
+
+
 MUTANTS = {
+    "bwd_softmax_row_term_dropped": ("causal_attention_bwd", _bad_bwd_no_rowsum),
+    "bwd_dk_unscaled": ("causal_attention_bwd", _bad_bwd_unscaled_dk),
     "range_lower_bound_late": ("attention_range", _bad_range),
     "merge_weights_swapped": ("lse_merge", _bad_merge),
     "zigzag_mirror_off_by_one": ("zigzag_index", _bad_zigzag),
