@@ -177,6 +177,31 @@ TSP_API int tsp_attn_merge(float* o_acc, float* lse_acc, const float* o_part, co
                            int32_t head_dim, tsp_stream_t stream);
 
 /* Workspace bytes tsp_mlp_shard_accum needs for M rows and shard width Fs. */
+/*
+ * Gradients of the rank's causal attention (backward of tsp_attn_fwd). The pages name
+ * training but do not describe the backward pass: this is the derivative of the forward
+ * definition. With P_ij = exp(scale q_i.k_j - lse_i) over the visible keys j <= p_i and
+ * D_i = do_i . o_i:
+ *   dv_j = sum_i P_ij do_i,  ds_ij = P_ij (do_i . v_j - D_i),
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i.
+ *   q, o, d_o  bf16 [B, 2C, H, hd]  the rank's queries, forward output, output gradient
+ *   k_full, v_full  bf16 [B, S, H, hd]  as given to tsp_attn_fwd
+ *   lse        f32 [B, H, 2C]  the forward's log-sum-exp (natural log)
+ *   dq         f32 [B, 2C, H, hd]  overwritten
+ *   dk_full, dv_full  f32 [B, S, H, hd]  overwritten with this rank's contributions at
+ *              every key position (zero where no query of the rank looks); the gradient
+ *              of the sequence's K and V is their sum over the D ranks
+ *   ws         device workspace of tsp_attn_bwd_workspace_size bytes (the D_i)
+ *   scale      <= 0 means 1/sqrt(head_dim), as in the forward
+ * Errors: as tsp_attn_fwd; TSP_ERR_NULL for a missing pointer, TSP_ERR_WORKSPACE.
+ */
+TSP_API size_t tsp_attn_bwd_workspace_size(int32_t B, int64_t S, int32_t D, int32_t n_heads);
+TSP_API int tsp_attn_bwd(const void* q, const void* k_full, const void* v_full, const void* o,
+                         const float* lse, const void* d_o, float* dq, float* dk_full, float* dv_full,
+                         int32_t B, int64_t S, int32_t D, int32_t rank, int32_t n_heads,
+                         int32_t head_dim, float scale, void* ws, size_t ws_bytes,
+                         tsp_stream_t stream);
+
 TSP_API size_t tsp_mlp_workspace_size(int64_t M, int32_t Fs);
 
 /*

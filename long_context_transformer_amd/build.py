@@ -17,13 +17,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtsp.so")
-SOURCES = ["tsp_api.hip", "tsp_gemm.hip", "tsp_attn.hip"]
+SOURCES = ["tsp_api.hip", "tsp_gemm.hip", "tsp_attn.hip", "tsp_attn_bwd.hip"]
 # Per-source code generation flags. The attention kernel keeps its O accumulator and
 # scores in VGPRs (MFMA "VGPR form"); the rescale of O then stays a plain VALU multiply
 # instead of AGPR<->VGPR copies on every key block. It also runs with the IEEE mode bit
 # off and no NaN operands assumed (its scores are finite or -inf), so max/min need no
 # canonicalising moves.
-SOURCE_FLAGS = {"tsp_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]}
+SOURCE_FLAGS = {"tsp_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"],
+                "tsp_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

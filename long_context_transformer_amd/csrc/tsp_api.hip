@@ -173,6 +173,33 @@ int tsp_attn_fwd(const void* q, const void* k_full, const void* v_full, void* o,
   return ok();
 }
 
+size_t tsp_attn_bwd_workspace_size(int32_t B, int64_t S, int32_t D, int32_t n_heads) {
+  if (B < 0 || D < 1 || S < 0 || n_heads < 1 || S % (2 * (int64_t)D) != 0) return 0;
+  return round_up((size_t)B * (size_t)n_heads * (size_t)(S / D) * 4, kAlign);
+}
+
+int tsp_attn_bwd(const void* q, const void* k_full, const void* v_full, const void* o, const float* lse,
+                 const void* d_o, float* dq, float* dk_full, float* dv_full, int32_t B, int64_t S, int32_t D,
+                 int32_t rank, int32_t n_heads, int32_t head_dim, float scale, void* ws, size_t ws_bytes,
+                 tsp_stream_t stream) {
+  if (int rc = check_fold(B, S, D, rank)) return rc;
+  if (int rc = check_heads(n_heads, head_dim)) return rc;
+  if (!(scale == scale) || isinf(scale)) return fail(TSP_ERR_SHAPE, "scale must be finite");
+  if (B == 0 || S == 0) return ok();
+  if (!q || !k_full || !v_full || !o || !lse || !d_o || !dq || !dk_full || !dv_full || !ws)
+    return fail(TSP_ERR_NULL, "a required pointer is NULL");
+  if (misaligned(q) || misaligned(k_full) || misaligned(v_full) || misaligned(o) || misaligned(d_o) ||
+      misaligned(dq) || misaligned(dk_full) || misaligned(dv_full) || misaligned(ws) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(TSP_ERR_ALIGN, "tensors must be 16-byte aligned and lse 4-byte aligned");
+  const size_t need = tsp_attn_bwd_workspace_size(B, S, D, n_heads);
+  if (ws_bytes < need) return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (S > kMaxI32 / 2) return fail(TSP_ERR_UNSUPPORTED, "S too large for 32-bit key indices");
+  return hip_status(tsp::launch_attn_bwd(q, k_full, v_full, o, lse, d_o, dq, dk_full, dv_full, static_cast<float*>(ws),
+                                         B, S, D, rank, n_heads, head_dim, scale, static_cast<hipStream_t>(stream)),
+                    "attention backward launch");
+}
+
 int tsp_attn_fwd_range(const void* q, const void* k_full, const void* v_full, float* o_part, float* lse_part,
                        int32_t B, int64_t S, int32_t D, int32_t rank, int32_t n_heads, int32_t head_dim, float scale,
                        int64_t key_lo, int64_t key_hi, int32_t accumulate, void* o_out, tsp_stream_t stream) {

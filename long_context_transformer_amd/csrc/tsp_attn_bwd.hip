@@ -1,0 +1,347 @@
+// tsp_attn_bwd.hip -- gradients of the rank's causal attention: dq for its queries and its
+// dk/dv contributions for every key position.
+//
+// Forward (per query row i at global position p_i, visible keys j <= p_i):
+//   s_ij = scale q_i.k_j, P_ij = exp(s_ij - lse_i), o_i = sum_j P_ij v_j.
+// Backward, with D_i = do_i . o_i (= sum_j P_ij dP_ij):
+//   dv_j = sum_i P_ij do_i,  dP_ij = do_i . v_j,  ds_ij = P_ij (dP_ij - D_i),
+//   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i.
+// The forward's log-sum-exp gives P directly (no running max). Two kernels:
+//   attn_bwd_dq    query-stationary: a wave owns 32 query rows and streams the key blocks
+//                  its rows see; it also writes D_i for the second kernel.
+//   attn_bwd_dkdv  key-stationary: a wave owns 32 keys and streams the rank's query rows
+//                  that see them (a suffix of the local rows: they ascend in position).
+// MFMA v_mfma_f32_32x32x16_bf16 throughout, in the forward kernel's formulation: S^T = K Q^T
+// (and dP^T = V dO^T) leave each lane with one query's scores, which packed to bf16 are the
+// B operand of dQ^T += K^T dS^T, whose A operand comes from LDS by transpose reads. The
+// key-stationary kernel uses S = Q K^T instead, so that each lane holds one key's column.
+// Tiles are staged into LDS with plain loads between two barriers (no DMA ring).
+#include <hip/hip_runtime.h>
+
+#include "tsp_device.h"
+#include "tsp_internal.h"
+
+namespace tsp {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kRowsPerWg = 32 * kBwdWaves;  // query rows (dq) or keys (dk/dv) per workgroup
+constexpr int kStage = 64;                  // rows staged per LDS fill: two 32-row blocks
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int HD>
+struct BLay {
+  static constexpr int KS = HD / 16;   // 16-dim reduction steps
+  static constexpr int DB = HD / 32;   // 32-dim output blocks
+  static constexpr int ROWB = HD * 2;  // bytes per row
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int TILEB = kStage * ROWB;
+  // 16-byte chunk c of row r is stored at chunk c ^ sw(r). Transpose reads touch 4 rows
+  // (aligned to 4) x 4 chunks; this swizzle spreads them over the banks.
+  __device__ static int sw(int r) { return HD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
+
+struct BwdArgs {
+  const bf16_t* q;    // [B, rows, H, HD] the rank's queries
+  const bf16_t* k;    // [B, S, H, HD]
+  const bf16_t* v;
+  const bf16_t* o;    // [B, rows, H, HD] forward output
+  const bf16_t* d_o;  // [B, rows, H, HD]
+  const float* lse;   // [B, H, rows] natural log
+  float* dq;          // [B, rows, H, HD]
+  float* dk;          // [B, S, H, HD]
+  float* dv;
+  float* dsum;        // [B, H, rows] D_i, written by attn_bwd_dq
+  int64_t S, C;
+  int rows, D, rank, H;
+  float scale;
+};
+
+// Rows [first, first + kStage) of a row-major [*, HD] bf16 matrix (row stride tok elements)
+// into an LDS tile; rows past `last` repeat row `last` (their results are masked).
+template <int HD>
+__device__ __forceinline__ void stage_rows(char* tile, const bf16_t* src, int64_t tok, int first, int last,
+                                           int tid) {
+  using L = BLay<HD>;
+  for (int lin = tid; lin < kStage * L::CPR; lin += kBwdThreads) {
+    const int r = lin / L::CPR, c = lin - (lin / L::CPR) * L::CPR;
+    const int gr = min(first + r, last);
+    const uint4 val = *reinterpret_cast<const uint4*>(src + (int64_t)gr * tok + 8 * c);
+    *reinterpret_cast<uint4*>(tile + r * L::ROWB + 16 * (c ^ L::sw(r))) = val;
+  }
+}
+
+// A or B fragment of a 32-row block: lane (l32, hl) gets row rb + l32, dims 16 s + 8 hl .. +7.
+template <int HD>
+__device__ __forceinline__ bf16x8 row_frag(const char* tile, int rb, int l32, int hl, int s) {
+  using L = BLay<HD>;
+  const int r = rb + l32;
+  return as_bf16x8(*reinterpret_cast<const uint4*>(tile + r * L::ROWB + 16 * ((2 * s + hl) ^ L::sw(r))));
+}
+
+// Transpose-read bases of the [32 dims x 16 rows] A fragments (dims block db): lane
+// (G = lane / 16, j16 = lane % 16) reads row 4 hl + j16 / 4 of each group of 8, at the chunk
+// that holds its dims; two reads 8 rows apart make one fragment. The row order this gives
+// (rows 4 hl .. 4 hl + 3 and 8 + 4 hl .. 8 + 4 hl + 3 of a 16-row half) is the order in
+// which an MFMA result's registers 8 half .. 8 half + 7 hold their rows, so the packed
+// result of a previous MFMA serves directly as the B operand.
+template <int HD>
+__device__ __forceinline__ int tr_offset(int lane, int db) {
+  using L = BLay<HD>;
+  const int hl = lane >> 5, G = lane >> 4, j16 = lane & 15;
+  const int r = 4 * hl + (j16 >> 2);
+  const int c = 4 * db + 2 * (G & 1) + ((j16 & 3) >> 1);
+  return r * L::ROWB + 16 * (c ^ L::sw(r)) + 8 * (j16 & 1);
+}
+
+template <int HD>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int off, int rb) {
+  using L = BLay<HD>;
+  const lds_s16x4* p = (const lds_s16x4*)(tile + off + rb * L::ROWB);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + L::ROWB));
+  const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+  return as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+}
+
+// Registers 8 half .. 8 half + 7 of an MFMA result, as bf16 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack_half(const float (&x)[16], int half) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[8 * half + 2 * e], x[8 * half + 2 * e + 1]);
+  return as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+template <int HD>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_bwd_dq(BwdArgs a) {
+  using L = BLay<HD>;
+  constexpr int KS = L::KS, DB = L::DB;
+  __shared__ __attribute__((aligned(16))) char ktile[L::TILEB];
+  __shared__ __attribute__((aligned(16))) char vtile[L::TILEB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hl = lane >> 5;
+  const int n_qt = (a.rows + kRowsPerWg - 1) / kRowsPerWg;
+  const int bh = blockIdx.x / n_qt;
+  const int qt = n_qt - 1 - (int)(blockIdx.x - bh * n_qt);  // heaviest tile first
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const int row0 = qt * kRowsPerWg;
+  const int kv_end = (int)zigzag_pos(min(row0 + kRowsPerWg, a.rows) - 1, a.C, a.rank, a.D) + 1;
+  const int64_t tok = (int64_t)a.H * HD;
+
+  const int qi = row0 + 32 * wave + l32;
+  const bool valid = qi < a.rows;
+  const int qic = valid ? qi : a.rows - 1;
+  const int qpos = (int)zigzag_pos(qic, a.C, a.rank, a.D);
+  const int64_t rowoff = ((int64_t)b * a.rows + qic) * tok + (int64_t)h * HD + 8 * hl;
+  bf16x8 qf[KS], df[KS];
+  float dsum = 0.0f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + 16 * s));
+    df[s] = as_bf16x8(*reinterpret_cast<const uint4*>(a.d_o + rowoff + 16 * s));
+    const bf16x8 of = as_bf16x8(*reinterpret_cast<const uint4*>(a.o + rowoff + 16 * s));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum += (float)df[s][e] * (float)of[e];
+  }
+  dsum += __shfl_xor(dsum, 32);  // the other half of the row's dims
+  const int64_t li = ((int64_t)b * a.H + h) * a.rows + qic;
+  if (valid && hl == 0) a.dsum[li] = dsum;
+  const float lse2 = a.lse[li] * kLog2e;
+  const float c2 = a.scale * kLog2e;
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
+  int troff[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) troff[db] = tr_offset<HD>(lane, db);
+
+  const bf16_t* kseq = a.k + (int64_t)b * a.S * tok + (int64_t)h * HD;
+  const bf16_t* vseq = a.v + (int64_t)b * a.S * tok + (int64_t)h * HD;
+  for (int key0 = 0; key0 < kv_end; key0 += kStage) {
+    __syncthreads();  // the previous stage's reads are done
+    stage_rows<HD>(ktile, kseq, tok, key0, kv_end - 1, tid);
+    stage_rows<HD>(vtile, vseq, tok, key0, kv_end - 1, tid);
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int k0 = key0 + 32 * kb;
+      if (k0 >= kv_end) break;  // the same for the whole workgroup
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32x32x16(row_frag<HD>(ktile, 32 * kb, l32, hl, ks), qf[ks], s);
+        dp = mfma32x32x16(row_frag<HD>(vtile, 32 * kb, l32, hl, ks), df[ks], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const float p = key <= qpos ? __builtin_amdgcn_exp2f(s[r] * c2 - lse2) : 0.0f;
+        ds[r] = p * (dp[r] - dsum);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 dsf = pack_half(ds, half);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dqacc[db] = mfma32x32x16(tr_frag<HD>(ktile, troff[db], 32 * kb + 16 * half), dsf, dqacc[db]);
+      }
+    }
+  }
+  if (!valid) return;
+  float* out = a.dq + ((int64_t)b * a.rows + qi) * tok + (int64_t)h * HD;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x16& x = dqacc[db];
+      *reinterpret_cast<f32x4*>(out + 32 * db + 8 * g + 4 * hl) =
+          f32x4{x[4 * g] * a.scale, x[4 * g + 1] * a.scale, x[4 * g + 2] * a.scale, x[4 * g + 3] * a.scale};
+    }
+}
+
+template <int HD>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_bwd_dkdv(BwdArgs a) {
+  using L = BLay<HD>;
+  constexpr int KS = L::KS, DB = L::DB;
+  __shared__ __attribute__((aligned(16))) char qtile[L::TILEB];
+  __shared__ __attribute__((aligned(16))) char otile[L::TILEB];  // dO
+  __shared__ float lse_s[kStage], d_s[kStage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hl = lane >> 5;
+  const int n_kt = (int)((a.S + kRowsPerWg - 1) / kRowsPerWg);
+  const int bh = blockIdx.x / n_kt;
+  const int kt = (int)(blockIdx.x - bh * n_kt);
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const int key0 = kt * kRowsPerWg;
+  const int64_t tok = (int64_t)a.H * HD;
+
+  const int kj = key0 + 32 * wave + l32;
+  const bool kvalid = kj < a.S;
+  const int kjc = kvalid ? kj : (int)a.S - 1;
+  const int64_t keyoff = ((int64_t)b * a.S + kjc) * tok + (int64_t)h * HD + 8 * hl;
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(a.k + keyoff + 16 * s));
+    vf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(a.v + keyoff + 16 * s));
+  }
+
+  // The rank's local rows ascend in position (chunk r, then chunk 2D-1-r): the rows that see
+  // any of this workgroup's keys are the suffix from the first row at position >= key0.
+  const int64_t lo_a = (int64_t)a.rank * a.C, lo_b = (int64_t)(2 * a.D - 1 - a.rank) * a.C;
+  int i0;
+  if (key0 < lo_a + a.C) {
+    i0 = (int)max((int64_t)0, key0 - lo_a);
+  } else if (key0 < lo_b + a.C) {
+    i0 = (int)(a.C + max((int64_t)0, key0 - lo_b));
+  } else {
+    i0 = a.rows;
+  }
+  const float c2 = a.scale * kLog2e;
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dkacc[db] = dvacc[db] = f32x16{};
+  int troff[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) troff[db] = tr_offset<HD>(lane, db);
+
+  const bf16_t* qseq = a.q + (int64_t)b * a.rows * tok + (int64_t)h * HD;
+  const bf16_t* oseq = a.d_o + (int64_t)b * a.rows * tok + (int64_t)h * HD;
+  const int64_t lrow = ((int64_t)b * a.H + h) * a.rows;
+  for (int i = i0; i < a.rows; i += kStage) {
+    __syncthreads();
+    stage_rows<HD>(qtile, qseq, tok, i, a.rows - 1, tid);
+    stage_rows<HD>(otile, oseq, tok, i, a.rows - 1, tid);
+    for (int t = tid; t < kStage; t += kBwdThreads) {
+      const int ri = min(i + t, a.rows - 1);
+      lse_s[t] = a.lse[lrow + ri] * kLog2e;
+      d_s[t] = a.dsum[lrow + ri];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int q0 = i + 32 * qb;
+      if (q0 >= a.rows) break;  // the same for the whole workgroup
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32x32x16(row_frag<HD>(qtile, 32 * qb, l32, hl, ks), kf[ks], s);
+        dp = mfma32x32x16(row_frag<HD>(otile, 32 * qb, l32, hl, ks), vf[ks], dp);
+      }
+      float p[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
+        const int row = q0 + qr;
+        const bool ok = kvalid && row < a.rows && kj <= (int)zigzag_pos(min(row, a.rows - 1), a.C, a.rank, a.D);
+        p[r] = ok ? __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[32 * qb + qr]) : 0.0f;
+        ds[r] = p[r] * (dp[r] - d_s[32 * qb + qr]);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 pf = pack_half(p, half);
+        const bf16x8 dsf = pack_half(ds, half);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dvacc[db] = mfma32x32x16(tr_frag<HD>(otile, troff[db], 32 * qb + 16 * half), pf, dvacc[db]);
+          dkacc[db] = mfma32x32x16(tr_frag<HD>(qtile, troff[db], 32 * qb + 16 * half), dsf, dkacc[db]);
+        }
+      }
+    }
+  }
+  if (!kvalid) return;
+  const int64_t ko = ((int64_t)b * a.S + kj) * tok + (int64_t)h * HD;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dim = 32 * db + 8 * g + 4 * hl;
+      const f32x16& xk = dkacc[db];
+      const f32x16& xv = dvacc[db];
+      *reinterpret_cast<f32x4*>(a.dk + ko + dim) =
+          f32x4{xk[4 * g] * a.scale, xk[4 * g + 1] * a.scale, xk[4 * g + 2] * a.scale, xk[4 * g + 3] * a.scale};
+      *reinterpret_cast<f32x4*>(a.dv + ko + dim) = f32x4{xv[4 * g], xv[4 * g + 1], xv[4 * g + 2], xv[4 * g + 3]};
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const void* q, const void* k_full, const void* v_full, const void* o, const float* lse,
+                           const void* d_o, float* dq, float* dk_full, float* dv_full, float* dsum, int B, int64_t S,
+                           int D, int rank, int H, int hd, float scale, hipStream_t stream) {
+  BwdArgs a;
+  a.q = static_cast<const bf16_t*>(q);
+  a.k = static_cast<const bf16_t*>(k_full);
+  a.v = static_cast<const bf16_t*>(v_full);
+  a.o = static_cast<const bf16_t*>(o);
+  a.d_o = static_cast<const bf16_t*>(d_o);
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk_full;
+  a.dv = dv_full;
+  a.dsum = dsum;
+  a.S = S;
+  a.C = S / (2 * D);
+  a.rows = (int)(2 * a.C);
+  a.D = D;
+  a.rank = rank;
+  a.H = H;
+  a.scale = scale > 0.0f ? scale : 1.0f / sqrtf((float)hd);
+  const int n_qt = (a.rows + kRowsPerWg - 1) / kRowsPerWg;
+  const int n_kt = (int)((S + kRowsPerWg - 1) / kRowsPerWg);
+  const dim3 gq((unsigned)(B * H * n_qt)), gk((unsigned)(B * H * n_kt)), blk(kBwdThreads);
+  if (hd == 128) {
+    hipLaunchKernelGGL(attn_bwd_dq<128>, gq, blk, 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv<128>, gk, blk, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(attn_bwd_dq<64>, gq, blk, 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv<64>, gk, blk, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tsp

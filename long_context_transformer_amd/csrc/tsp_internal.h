@@ -70,6 +70,13 @@ hipError_t launch_attn_split(const void* q, const void* k_full, const void* v_fu
 hipError_t launch_attn_merge_halves(const float* o32, const float* lse, void* o_out, int B, int rows, int H, int hd,
                                     int h0, int h_run, hipStream_t stream);
 
+// Gradients of the rank's causal attention (two launches: dq and the row sums D_i, then
+// dk/dv of every key). lse [B, H, rows] natural log, from the forward; dsum [B, H, rows]
+// fp32 scratch. dq [B, rows, H, hd], dk_full / dv_full [B, S, H, hd] fp32, overwritten.
+hipError_t launch_attn_bwd(const void* q, const void* k_full, const void* v_full, const void* o, const float* lse,
+                           const void* d_o, float* dq, float* dk_full, float* dv_full, float* dsum, int B, int64_t S,
+                           int D, int rank, int H, int hd, float scale, hipStream_t stream);
+
 hipError_t launch_attn_range(const void* q, const void* k_full, const void* v_full, float* o32, float* lse, int B,
                              int64_t S, int D, int rank, int H, int hd, float scale, int64_t key_lo, int64_t key_hi,
                              int accumulate, void* o_out, hipStream_t stream);

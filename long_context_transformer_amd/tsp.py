@@ -59,6 +59,9 @@ _SIGS = {
     "tsp_layer_fwd_streamed": (_I32, [ctypes.POINTER(LayerDesc), _VP, ctypes.POINTER(_VP),
                                       ctypes.POINTER(_VP), _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
                                       ctypes.POINTER(_VP), _I32]),
+    "tsp_attn_bwd_workspace_size": (ctypes.c_size_t, [_I32, _I64, _I32, _I32]),
+    "tsp_attn_bwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32, _I32,
+                            ctypes.c_float, _VP, ctypes.c_size_t, _VP]),
     "tsp_timing_start": (_I32, [_I32]),
     "tsp_timing_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32, ctypes.POINTER(_I32)]),
 }
@@ -148,6 +151,19 @@ def attn_merge(o_acc, lse_acc, o_part, lse_part, o_out, B, S, D, n_heads, head_d
     receives the merged O."""
     _check(load().tsp_attn_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part), _ptr(o_out), B, S, D,
                                  n_heads, head_dim, _stream(stream, o_acc)))
+
+
+def attn_bwd_workspace_size(B, S, D, n_heads):
+    return int(load().tsp_attn_bwd_workspace_size(int(B), int(S), int(D), int(n_heads)))
+
+
+def attn_bwd(q, k_full, v_full, o, lse, d_o, dq, dk_full, dv_full, B, S, D, rank, n_heads, head_dim, ws,
+             ws_bytes=None, scale=0.0, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None and not isinstance(ws, int) else 0
+    _check(load().tsp_attn_bwd(_ptr(q), _ptr(k_full), _ptr(v_full), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq),
+                               _ptr(dk_full), _ptr(dv_full), B, S, D, rank, n_heads, head_dim, float(scale),
+                               _ptr(ws), ws_bytes, _stream(stream, q)))
 
 
 def mlp_workspace_size(M, Fs):
