@@ -283,6 +283,44 @@ def time_streamed(st, w, steps, warmup):
     return res
 
 
+def time_attn_bwd(st, w, rank, reps=3):
+    """Attention backward (tsp_attn_bwd) on the layer's Q/K/V: the forward with its
+    log-sum-exp once, then `reps` timed backward calls (HIP events on the launch stream).
+    FLOPs counted the usual way for attention backward: 2.5x the forward's exact causal
+    pairs (five products of hd per pair: the recomputed scores, dV, dP, dQ, dK)."""
+    import torch
+    from long_context_transformer_amd import tsp
+    B, S, D, H, hd = w.B, w.S, w.D, w.n_heads, w.head_dim
+    R = S // D
+    q = torch.empty((B, R, H * hd), dtype=torch.bfloat16, device="cuda")
+    tsp.qkv_fwd(st["xs"], st["dev"]["w_qkv"], q, st["kf"], st["vf"], B, S, D, rank, H, hd)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, R), dtype=torch.float32, device="cuda")
+    tsp.attn_fwd(q, st["kf"], st["vf"], o, lse, B, S, D, rank, H, hd)
+    g = torch.randn((B, R, H * hd), device="cuda", generator=torch.Generator("cuda").manual_seed(5)).to(torch.bfloat16)
+    dq = torch.empty((B, R, H * hd), dtype=torch.float32, device="cuda")
+    dk = torch.empty((B, S, H * hd), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    ws = torch.empty(tsp.attn_bwd_workspace_size(B, S, D, H), dtype=torch.uint8, device="cuda")
+    run = lambda: tsp.attn_bwd(q, st["kf"], st["vf"], o, lse, g, dq, dk, dv, B, S, D, rank, H, hd, ws)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    _, attn_fwd_flops = layer_flops(B, S, D, w.d_model, H, hd, w.ffn)
+    fl = 2.5 * attn_fwd_flops
+    tf = fl / (ms * 1e-3) / 1e12
+    del q, o, lse, g, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 3), "flops": fl, "tflops": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "note": "two launches: dq (query-stationary), dk/dv (key-stationary); fp32 gradients"}
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -345,6 +383,7 @@ def main():
     ap.add_argument("--memory", default=None,
                     help="also measure one rank's device memory for every workload (weight-streamed layer) "
                     "against the analytic per-layout counts; one JSON line each to this file")
+    ap.add_argument("--attn-bwd", action="store_true", help="also time the attention backward (tsp_attn_bwd)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB plain copy kernel first (counter calibration)")
     ap.add_argument("--sweep", default=None, help="also time every workload (and every rank of the "
@@ -391,6 +430,11 @@ def main():
         streamed["overhead_pct"] = round(100 * (streamed["four_streams_ms"] / ms - 1), 2)
         print("# streamed " + json.dumps(streamed), file=sys.stderr, flush=True)
 
+    attn_bwd = None
+    if args.attn_bwd:
+        attn_bwd = time_attn_bwd(st, w, args.rank)
+        print("# attention backward " + json.dumps(attn_bwd), file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, st["inputs"], args.rank, args.cpu_rows)
@@ -426,6 +470,8 @@ def main():
         out["chunked_attention"] = chunked
     if streamed:
         out["weight_streamed_layer"] = streamed
+    if attn_bwd:
+        out["attention_backward"] = attn_bwd
     print(json.dumps(out), flush=True)
 
     if args.memory:

@@ -15,7 +15,8 @@
 // (and dP^T = V dO^T) leave each lane with one query's scores, which packed to bf16 are the
 // B operand of dQ^T += K^T dS^T, whose A operand comes from LDS by transpose reads. The
 // key-stationary kernel uses S = Q K^T instead, so that each lane holds one key's column.
-// Tiles are staged into LDS with plain loads between two barriers (no DMA ring).
+// Tiles are staged into LDS through registers: the next stage's global loads are issued
+// before the current stage's MFMAs (no DMA ring).
 #include <hip/hip_runtime.h>
 
 #include "tsp_device.h"
@@ -61,17 +62,39 @@ struct BwdArgs {
   float scale;
 };
 
-// Rows [first, first + kStage) of a row-major [*, HD] bf16 matrix (row stride tok elements)
-// into an LDS tile; rows past `last` repeat row `last` (their results are masked).
+// Rows [first, first + kStage) of a row-major [*, HD] bf16 matrix (row stride tok elements),
+// staged through registers: load_rows reads a thread's 16-byte chunks from global memory
+// (rows past `last` repeat row `last`; their results are masked), store_rows writes them
+// to an LDS tile. Loading the next stage before computing the current one hides the global
+// latency behind the MFMAs.
 template <int HD>
-__device__ __forceinline__ void stage_rows(char* tile, const bf16_t* src, int64_t tok, int first, int last,
-                                           int tid) {
+struct Staged {
+  static constexpr int N = kStage * BLay<HD>::CPR / kBwdThreads;  // chunks per thread
+  static_assert(N * kBwdThreads == kStage * BLay<HD>::CPR, "whole tile per stage");
+  uint4 v[N];
+};
+
+template <int HD>
+__device__ __forceinline__ void load_rows(Staged<HD>& st, const bf16_t* src, int64_t tok, int first, int last,
+                                          int tid) {
   using L = BLay<HD>;
-  for (int lin = tid; lin < kStage * L::CPR; lin += kBwdThreads) {
+#pragma unroll
+  for (int n = 0; n < Staged<HD>::N; ++n) {
+    const int lin = tid + n * kBwdThreads;
     const int r = lin / L::CPR, c = lin - (lin / L::CPR) * L::CPR;
     const int gr = min(first + r, last);
-    const uint4 val = *reinterpret_cast<const uint4*>(src + (int64_t)gr * tok + 8 * c);
-    *reinterpret_cast<uint4*>(tile + r * L::ROWB + 16 * (c ^ L::sw(r))) = val;
+    st.v[n] = *reinterpret_cast<const uint4*>(src + (int64_t)gr * tok + 8 * c);
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void store_rows(char* tile, const Staged<HD>& st, int tid) {
+  using L = BLay<HD>;
+#pragma unroll
+  for (int n = 0; n < Staged<HD>::N; ++n) {
+    const int lin = tid + n * kBwdThreads;
+    const int r = lin / L::CPR, c = lin - (lin / L::CPR) * L::CPR;
+    *reinterpret_cast<uint4*>(tile + r * L::ROWB + 16 * (c ^ L::sw(r))) = st.v[n];
   }
 }
 
@@ -161,11 +184,19 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 
   const bf16_t* kseq = a.k + (int64_t)b * a.S * tok + (int64_t)h * HD;
   const bf16_t* vseq = a.v + (int64_t)b * a.S * tok + (int64_t)h * HD;
+  Staged<HD> sk, sv;
+  load_rows<HD>(sk, kseq, tok, 0, kv_end - 1, tid);
+  load_rows<HD>(sv, vseq, tok, 0, kv_end - 1, tid);
   for (int key0 = 0; key0 < kv_end; key0 += kStage) {
     __syncthreads();  // the previous stage's reads are done
-    stage_rows<HD>(ktile, kseq, tok, key0, kv_end - 1, tid);
-    stage_rows<HD>(vtile, vseq, tok, key0, kv_end - 1, tid);
+    store_rows<HD>(ktile, sk, tid);
+    store_rows<HD>(vtile, sv, tid);
     __syncthreads();
+    if (key0 + kStage < kv_end) {  // the next stage's loads, in flight during this stage's MFMAs
+      load_rows<HD>(sk, kseq, tok, key0 + kStage, kv_end - 1, tid);
+      load_rows<HD>(sv, vseq, tok, key0 + kStage, kv_end - 1, tid);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int k0 = key0 + 32 * kb;
@@ -252,16 +283,29 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
   const bf16_t* qseq = a.q + (int64_t)b * a.rows * tok + (int64_t)h * HD;
   const bf16_t* oseq = a.d_o + (int64_t)b * a.rows * tok + (int64_t)h * HD;
   const int64_t lrow = ((int64_t)b * a.H + h) * a.rows;
+  Staged<HD> sq, so;
+  float sl = 0.0f, sd = 0.0f;  // lse and D of row i + tid (threads below kStage)
+  auto load_stage = [&] __device__(int i) {
+    load_rows<HD>(sq, qseq, tok, i, a.rows - 1, tid);
+    load_rows<HD>(so, oseq, tok, i, a.rows - 1, tid);
+    if (tid < kStage) {
+      const int ri = min(i + tid, a.rows - 1);
+      sl = a.lse[lrow + ri] * kLog2e;
+      sd = a.dsum[lrow + ri];
+    }
+  };
+  if (i0 < a.rows) load_stage(i0);
   for (int i = i0; i < a.rows; i += kStage) {
     __syncthreads();
-    stage_rows<HD>(qtile, qseq, tok, i, a.rows - 1, tid);
-    stage_rows<HD>(otile, oseq, tok, i, a.rows - 1, tid);
-    for (int t = tid; t < kStage; t += kBwdThreads) {
-      const int ri = min(i + t, a.rows - 1);
-      lse_s[t] = a.lse[lrow + ri] * kLog2e;
-      d_s[t] = a.dsum[lrow + ri];
+    store_rows<HD>(qtile, sq, tid);
+    store_rows<HD>(otile, so, tid);
+    if (tid < kStage) {
+      lse_s[tid] = sl;
+      d_s[tid] = sd;
     }
     __syncthreads();
+    if (i + kStage < a.rows) load_stage(i + kStage);  // in flight during this stage's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int q0 = i + 32 * qb;

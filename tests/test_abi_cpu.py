@@ -160,6 +160,21 @@ def test_layer_errors():
     assert _code(f, bad, A, A, A, sh, sh, sh, A, A, A, A, A, ws, 0) == 2
 
 
+def test_attn_bwd_errors():
+    f = tsp.attn_bwd
+    ws = tsp.attn_bwd_workspace_size(1, 256, 4, 2)
+    assert ws == 1 * 2 * 64 * 4 and tsp.attn_bwd_workspace_size(1, 250, 4, 2) == 0
+    good = [A] * 9
+    shape = (1, 256, 4, 0, 2, 64)  # B, S, D, rank, H, hd
+    assert _code(f, *good, 1, 250, 4, 0, 2, 64, A, ws) == 2
+    assert _code(f, *good, 1, 256, 4, 4, 2, 64, A, ws) == 3
+    assert _code(f, *good, 1, 256, 4, 0, 2, 80, A, ws) == 4
+    assert _code(f, *([A] * 4 + [None] + [A] * 4), *shape, A, ws) == 1   # lse
+    assert _code(f, *([A] * 6 + [MIS] + [A] * 2), *shape, A, ws) == 6    # dq
+    assert _code(f, *good, *shape, A, ws - 4) == 5
+    f(*[None] * 9, 0, 256, 4, 1, 2, 64, None, 0)              # empty problem: OK, nothing read
+
+
 def test_streamed_layer_workspace_and_errors():
     good = _desc()
     M, d, Fs, dg = 64, 256, 172, 64
