@@ -236,11 +236,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 }
 
 template <int HD>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_bwd_dkdv(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv(BwdArgs a) {
   using L = BLay<HD>;
   constexpr int KS = L::KS, DB = L::DB;
   __shared__ __attribute__((aligned(16))) char qtile[L::TILEB];
   __shared__ __attribute__((aligned(16))) char otile[L::TILEB];  // dO
+  // V rows of the workgroup's keys: read as B fragments of dP = dO V^T each block (kept in
+  // LDS rather than registers, so that two waves fit on a SIMD)
+  __shared__ __attribute__((aligned(16))) char vkeys[kRowsPerWg * L::ROWB];
   __shared__ float lse_s[kStage], d_s[kStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hl = lane >> 5;
   const int n_kt = (int)((a.S + kRowsPerWg - 1) / kRowsPerWg);
@@ -254,11 +257,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
   const bool kvalid = kj < a.S;
   const int kjc = kvalid ? kj : (int)a.S - 1;
   const int64_t keyoff = ((int64_t)b * a.S + kjc) * tok + (int64_t)h * HD + 8 * hl;
-  bf16x8 kf[KS], vf[KS];
+  bf16x8 kf[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(a.k + keyoff + 16 * s));
-    vf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(a.v + keyoff + 16 * s));
+  for (int s = 0; s < KS; ++s) kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(a.k + keyoff + 16 * s));
+  {
+    const bf16_t* vrows = a.v + (int64_t)b * a.S * tok + (int64_t)h * HD;
+    for (int lin = tid; lin < kRowsPerWg * L::CPR; lin += kBwdThreads) {
+      const int r = lin / L::CPR, c = lin - (lin / L::CPR) * L::CPR;
+      const int gr = (int)min((int64_t)key0 + r, a.S - 1);
+      *reinterpret_cast<uint4*>(vkeys + r * L::ROWB + 16 * (c ^ L::sw(r))) =
+          *reinterpret_cast<const uint4*>(vrows + (int64_t)gr * tok + 8 * c);
+    }
   }
 
   // The rank's local rows ascend in position (chunk r, then chunk 2D-1-r): the rows that see
@@ -283,29 +292,23 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
   const bf16_t* qseq = a.q + (int64_t)b * a.rows * tok + (int64_t)h * HD;
   const bf16_t* oseq = a.d_o + (int64_t)b * a.rows * tok + (int64_t)h * HD;
   const int64_t lrow = ((int64_t)b * a.H + h) * a.rows;
-  Staged<HD> sq, so;
-  float sl = 0.0f, sd = 0.0f;  // lse and D of row i + tid (threads below kStage)
-  auto load_stage = [&] __device__(int i) {
-    load_rows<HD>(sq, qseq, tok, i, a.rows - 1, tid);
-    load_rows<HD>(so, oseq, tok, i, a.rows - 1, tid);
-    if (tid < kStage) {
-      const int ri = min(i + tid, a.rows - 1);
-      sl = a.lse[lrow + ri] * kLog2e;
-      sd = a.dsum[lrow + ri];
-    }
-  };
-  if (i0 < a.rows) load_stage(i0);
+  // Staged without a register prefetch: the accumulators and K fragments leave no room for
+  // it at two waves per SIMD, and the other wave on the SIMD covers the load latency.
   for (int i = i0; i < a.rows; i += kStage) {
     __syncthreads();
-    store_rows<HD>(qtile, sq, tid);
-    store_rows<HD>(otile, so, tid);
+    {
+      Staged<HD> sq, so;
+      load_rows<HD>(sq, qseq, tok, i, a.rows - 1, tid);
+      load_rows<HD>(so, oseq, tok, i, a.rows - 1, tid);
+      store_rows<HD>(qtile, sq, tid);
+      store_rows<HD>(otile, so, tid);
+    }
     if (tid < kStage) {
-      lse_s[tid] = sl;
-      d_s[tid] = sd;
+      const int ri = min(i + tid, a.rows - 1);
+      lse_s[tid] = a.lse[lrow + ri] * kLog2e;
+      d_s[tid] = a.dsum[lrow + ri];
     }
     __syncthreads();
-    if (i + kStage < a.rows) load_stage(i + kStage);  // in flight during this stage's MFMAs
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int q0 = i + 32 * qb;
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = mfma32x32x16(row_frag<HD>(qtile, 32 * qb, l32, hl, ks), kf[ks], s);
-        dp = mfma32x32x16(row_frag<HD>(otile, 32 * qb, l32, hl, ks), vf[ks], dp);
+        dp = mfma32x32x16(row_frag<HD>(otile, 32 * qb, l32, hl, ks), row_frag<HD>(vkeys, 32 * wave, l32, hl, ks), dp);
       }
       float p[16], ds[16];
 #pragma unroll
