@@ -25,9 +25,12 @@
 namespace tsp {
 namespace {
 
-constexpr int kBwdWaves = 4;
+constexpr int kDqWaves = 8;                 // query-stationary: 256 query rows per workgroup
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqRows = 32 * kDqWaves;
+constexpr int kBwdWaves = 4;                // key-stationary: 128 keys per workgroup
 constexpr int kBwdThreads = 64 * kBwdWaves;
-constexpr int kRowsPerWg = 32 * kBwdWaves;  // query rows (dq) or keys (dk/dv) per workgroup
+constexpr int kRowsPerWg = 32 * kBwdWaves;
 constexpr int kStage = 64;                  // rows staged per LDS fill: two 32-row blocks
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -67,32 +70,32 @@ struct BwdArgs {
 // (rows past `last` repeat row `last`; their results are masked), store_rows writes them
 // to an LDS tile. Loading the next stage before computing the current one hides the global
 // latency behind the MFMAs.
-template <int HD>
+template <int HD, int NT>
 struct Staged {
-  static constexpr int N = kStage * BLay<HD>::CPR / kBwdThreads;  // chunks per thread
-  static_assert(N * kBwdThreads == kStage * BLay<HD>::CPR, "whole tile per stage");
+  static constexpr int N = kStage * BLay<HD>::CPR / NT;  // chunks per thread (NT threads)
+  static_assert(N >= 1 && N * NT == kStage * BLay<HD>::CPR, "whole tile per stage");
   uint4 v[N];
 };
 
-template <int HD>
-__device__ __forceinline__ void load_rows(Staged<HD>& st, const bf16_t* src, int64_t tok, int first, int last,
+template <int HD, int NT>
+__device__ __forceinline__ void load_rows(Staged<HD, NT>& st, const bf16_t* src, int64_t tok, int first, int last,
                                           int tid) {
   using L = BLay<HD>;
 #pragma unroll
-  for (int n = 0; n < Staged<HD>::N; ++n) {
-    const int lin = tid + n * kBwdThreads;
+  for (int n = 0; n < Staged<HD, NT>::N; ++n) {
+    const int lin = tid + n * NT;
     const int r = lin / L::CPR, c = lin - (lin / L::CPR) * L::CPR;
     const int gr = min(first + r, last);
     st.v[n] = *reinterpret_cast<const uint4*>(src + (int64_t)gr * tok + 8 * c);
   }
 }
 
-template <int HD>
-__device__ __forceinline__ void store_rows(char* tile, const Staged<HD>& st, int tid) {
+template <int HD, int NT>
+__device__ __forceinline__ void store_rows(char* tile, const Staged<HD, NT>& st, int tid) {
   using L = BLay<HD>;
 #pragma unroll
-  for (int n = 0; n < Staged<HD>::N; ++n) {
-    const int lin = tid + n * kBwdThreads;
+  for (int n = 0; n < Staged<HD, NT>::N; ++n) {
+    const int lin = tid + n * NT;
     const int r = lin / L::CPR, c = lin - (lin / L::CPR) * L::CPR;
     *reinterpret_cast<uint4*>(tile + r * L::ROWB + 16 * (c ^ L::sw(r))) = st.v[n];
   }
@@ -140,18 +143,18 @@ __device__ __forceinline__ bf16x8 pack_half(const float (&x)[16], int half) {
 }
 
 template <int HD>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_bwd_dq(BwdArgs a) {
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq(BwdArgs a) {
   using L = BLay<HD>;
   constexpr int KS = L::KS, DB = L::DB;
   __shared__ __attribute__((aligned(16))) char ktile[L::TILEB];
   __shared__ __attribute__((aligned(16))) char vtile[L::TILEB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hl = lane >> 5;
-  const int n_qt = (a.rows + kRowsPerWg - 1) / kRowsPerWg;
+  const int n_qt = (a.rows + kDqRows - 1) / kDqRows;
   const int bh = blockIdx.x / n_qt;
   const int qt = n_qt - 1 - (int)(blockIdx.x - bh * n_qt);  // heaviest tile first
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int row0 = qt * kRowsPerWg;
-  const int kv_end = (int)zigzag_pos(min(row0 + kRowsPerWg, a.rows) - 1, a.C, a.rank, a.D) + 1;
+  const int row0 = qt * kDqRows;
+  const int kv_end = (int)zigzag_pos(min(row0 + kDqRows, a.rows) - 1, a.C, a.rank, a.D) + 1;
   const int64_t tok = (int64_t)a.H * HD;
 
   const int qi = row0 + 32 * wave + l32;
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 
   const bf16_t* kseq = a.k + (int64_t)b * a.S * tok + (int64_t)h * HD;
   const bf16_t* vseq = a.v + (int64_t)b * a.S * tok + (int64_t)h * HD;
-  Staged<HD> sk, sv;
+  Staged<HD, kDqThreads> sk, sv;
   load_rows<HD>(sk, kseq, tok, 0, kv_end - 1, tid);
   load_rows<HD>(sv, vseq, tok, 0, kv_end - 1, tid);
   for (int key0 = 0; key0 < kv_end; key0 += kStage) {
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   for (int i = i0; i < a.rows; i += kStage) {
     __syncthreads();
     {
-      Staged<HD> sq, so;
+      Staged<HD, kBwdThreads> sq, so;
       load_rows<HD>(sq, qseq, tok, i, a.rows - 1, tid);
       load_rows<HD>(so, oseq, tok, i, a.rows - 1, tid);
       store_rows<HD>(qtile, sq, tid);
@@ -378,15 +381,15 @@ hipError_t launch_attn_bwd(const void* q, const void* k_full, const void* v_full
   a.rank = rank;
   a.H = H;
   a.scale = scale > 0.0f ? scale : 1.0f / sqrtf((float)hd);
-  const int n_qt = (a.rows + kRowsPerWg - 1) / kRowsPerWg;
+  const int n_qt = (a.rows + kDqRows - 1) / kDqRows;
   const int n_kt = (int)((S + kRowsPerWg - 1) / kRowsPerWg);
-  const dim3 gq((unsigned)(B * H * n_qt)), gk((unsigned)(B * H * n_kt)), blk(kBwdThreads);
+  const dim3 gq((unsigned)(B * H * n_qt)), gk((unsigned)(B * H * n_kt));
   if (hd == 128) {
-    hipLaunchKernelGGL(attn_bwd_dq<128>, gq, blk, 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dkdv<128>, gk, blk, 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dq<128>, gq, dim3(kDqThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv<128>, gk, dim3(kBwdThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(attn_bwd_dq<64>, gq, blk, 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dkdv<64>, gk, blk, 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dq<64>, gq, dim3(kDqThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv<64>, gk, dim3(kBwdThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
