@@ -65,6 +65,7 @@ __all__ = [
     "attention_range",
     "lse_merge",
     "causal_attention_bwd",
+    "layer_bwd",
 ]
 
 
@@ -328,6 +329,50 @@ def rank_layer(x_full, w_qkv, w_o, w1, w3, w2, S, D, rank, n_heads, rows=None,
     mlp_out = swiglu_mlp(attn_out, w1, w3, w2)
     return {"idx": idx, "pos": pos, "q": q, "o": o, "lse": lse,
             "attn_out": attn_out, "mlp_out": mlp_out}
+
+
+def layer_bwd(x_full, w_qkv, w_o, w1, w3, w2, n_heads, d_y, scale=None):
+    """Gradients of the unsharded layer (QKV -> causal attention -> W_O -> SwiGLU MLP) given
+    the gradient d_y [B, S, d] of its output. [TSP title: training; the backward is the
+    derivative of the forward defined above]
+
+    With A = O W_o^T, G = A W1^T, U = A W3^T, Hh = silu(G) * U, Y = Hh W2^T:
+      dW2 = dY^T Hh,  dHh = dY W2,
+      dG = dHh * U * silu'(G)  (silu'(g) = s(g) (1 + g (1 - s(g))), s the sigmoid),
+      dU = dHh * silu(G),  dW1 = dG^T A,  dW3 = dU^T A,  dA = dG W1 + dU W3,
+      dW_o = dA^T O,  dO = dA W_o,  (dQ, dK, dV) = causal_attention_bwd(..., dO),
+      dW_qkv = [dQ; dK; dV]^T X,  dX = dQ W_q + dK W_k + dV W_v.
+    Returns a dict with dx [B, S, d], dw_qkv [3d, d], dw_o [d, d], dw1, dw3 [F, d], dw2 [d, F].
+    On D ranks every term is a sum over tokens: a rank's share of a weight gradient is the
+    same expression over its own rows, and the shares add up to these.
+    """
+    x = np.asarray(x_full, dtype=np.float64)
+    w_qkv, w_o = np.asarray(w_qkv, dtype=np.float64), np.asarray(w_o, dtype=np.float64)
+    w1, w3, w2 = (np.asarray(w, dtype=np.float64) for w in (w1, w3, w2))
+    dy = np.asarray(d_y, dtype=np.float64)
+    B, S, d = x.shape
+    pos = np.arange(S)
+    q, k, v = qkv_rows(x, w_qkv, n_heads)
+    o, _ = causal_attention(q, pos, k, v, scale=scale)
+    of = o.reshape(B, S, d)
+    a = project(of, w_o)
+    g, u = project(a, w1), project(a, w3)
+    sg = 1.0 / (1.0 + np.exp(-g))
+    hh = g * sg * u
+    flat = lambda t: t.reshape(-1, t.shape[-1])
+    dw2 = flat(dy).T @ flat(hh)
+    dhh = dy @ w2
+    dg = dhh * u * sg * (1.0 + g * (1.0 - sg))
+    du = dhh * g * sg
+    dw1, dw3 = flat(dg).T @ flat(a), flat(du).T @ flat(a)
+    da = dg @ w1 + du @ w3
+    dw_o = flat(da).T @ flat(of)
+    do = (da @ w_o).reshape(o.shape)
+    dq, dk, dv = causal_attention_bwd(q, pos, k, v, do, scale=scale)
+    dqkv = np.concatenate([dq.reshape(B, S, d), dk.reshape(B, S, d), dv.reshape(B, S, d)], axis=-1)
+    dw_qkv = flat(dqkv).T @ flat(x)
+    dx = dqkv @ w_qkv
+    return {"dx": dx, "dw_qkv": dw_qkv, "dw_o": dw_o, "dw1": dw1, "dw3": dw3, "dw2": dw2}
 
 
 def layer_flops(B, S, D, d, n_heads, head_dim, F):

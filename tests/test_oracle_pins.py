@@ -409,13 +409,58 @@ def pin_attention_bwd_ranks_sum():
     np.testing.assert_allclose(sq, fq, rtol=1e-10, atol=1e-12)
 
 
+def _torch_layer(x, w_qkv, w_o, w1, w3, w2, H):
+    """The layer in torch ops (an independent implementation for the autograd pin)."""
+    import torch
+    B, S, d = x.shape
+    hd = d // H
+    q, k, v = (x @ w_qkv[i * d:(i + 1) * d].T for i in range(3))
+    sh = lambda t: t.reshape(B, S, H, hd)
+    s = torch.einsum("bihd,bjhd->bhij", sh(q), sh(k)) / np.sqrt(hd)
+    s = s.masked_fill(~torch.ones(S, S, dtype=torch.bool).tril(), float("-inf"))
+    o = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, dim=-1), sh(v)).reshape(B, S, d)
+    a = o @ w_o.T
+    return (torch.nn.functional.silu(a @ w1.T) * (a @ w3.T)) @ w2.T
+
+
+def pin_layer_bwd_vs_autograd():
+    """layer_bwd against torch autograd (CPU, float64) of an independent torch layer, and
+    one finite difference per weight."""
+    import torch
+    rng = _rng(43)
+    B, S, d, H, F = 2, 12, 16, 2, 24
+    arrs = {"x": rng.standard_normal((B, S, d)), "w_qkv": 0.3 * rng.standard_normal((3 * d, d)),
+            "w_o": 0.3 * rng.standard_normal((d, d)), "w1": 0.3 * rng.standard_normal((F, d)),
+            "w3": 0.3 * rng.standard_normal((F, d)), "w2": 0.3 * rng.standard_normal((d, F))}
+    dy = rng.standard_normal((B, S, d))
+    ref = O.layer_bwd(arrs["x"], arrs["w_qkv"], arrs["w_o"], arrs["w1"], arrs["w3"], arrs["w2"], H, dy)
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in arrs.items()}
+    y = _torch_layer(t["x"], t["w_qkv"], t["w_o"], t["w1"], t["w3"], t["w2"], H)
+    (y * torch.tensor(dy)).sum().backward()
+    names = {"x": "dx", "w_qkv": "dw_qkv", "w_o": "dw_o", "w1": "dw1", "w3": "dw3", "w2": "dw2"}
+    for k, r in names.items():
+        np.testing.assert_allclose(ref[r], t[k].grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=k)
+    eps = 1e-6
+    for k, r in names.items():
+        i = tuple(int(rng.integers(n)) for n in arrs[k].shape)
+        plus, minus = {**arrs}, {**arrs}
+        plus[k], minus[k] = arrs[k].copy(), arrs[k].copy()
+        plus[k][i] += eps
+        minus[k][i] -= eps
+        f = lambda z: float((O.swiglu_mlp(O.project(O.causal_attention(
+            *O.qkv_rows(z["x"], z["w_qkv"], H)[:1], np.arange(S), *O.qkv_rows(z["x"], z["w_qkv"], H)[1:])[0]
+            .reshape(B, S, d), z["w_o"]), z["w1"], z["w3"], z["w2"]) * dy).sum())
+        num = (f(plus) - f(minus)) / (2 * eps)
+        np.testing.assert_allclose(ref[r][i], num, rtol=1e-5, atol=1e-7, err_msg=k)
+
+
 PINS = [pin_zigzag_golden, pin_zigzag_partition, pin_zigzag_balance, pin_zigzag_identity,
         pin_attention_vs_brute, pin_attention_vs_library, pin_attention_concat_ranks,
         pin_attention_special_cases, pin_attention_scale, pin_silu_closed_form,
         pin_mlp_vs_brute, pin_mlp_shards_sum, pin_layer_vs_brute, pin_layer_concat_ranks,
         pin_layer_rows_subset, pin_layer_flops, pin_range_vs_brute, pin_range_merge_equals_full,
         pin_merge_identity, pin_attention_bwd_finite_differences, pin_attention_bwd_vs_autograd,
-        pin_attention_bwd_ranks_sum]
+        pin_attention_bwd_ranks_sum, pin_layer_bwd_vs_autograd]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -504,7 +549,28 @@ def _bad_bwd_unscaled_dk(q, q_pos, k, v, d_o, scale=None, row_block=512):
     return dq, dk * np.sqrt(hd), dv  # the scale left out of dk
 
 
+_good_layer_bwd = O.layer_bwd
+
+
+def _bad_layer_bwd(x_full, w_qkv, w_o, w1, w3, w2, n_heads, d_y, scale=None):
+    # silu'(g) taken as sigmoid(g) alone: the gate's gradient loses its g (1 - s) term
+    saved = O.causal_attention_bwd
+    r = _good_layer_bwd(x_full, w_qkv, w_o, w1, w3, w2, n_heads, d_y, scale)
+    x = np.asarray(x_full, dtype=np.float64)
+    B, S, d = x.shape
+    q, k, v = O.qkv_rows(x, w_qkv, n_heads)
+    o, _ = O.causal_attention(q, np.arange(S), k, v, scale=scale)
+    a = O.project(o.reshape(B, S, d), w_o)
+    g, u = O.project(a, w1), O.project(a, w3)
+    sg = 1.0 / (1.0 + np.exp(-g))
+    dhh = np.asarray(d_y, dtype=np.float64) @ np.asarray(w2, dtype=np.float64)
+    r["dw1"] = (dhh * u * sg).reshape(-1, g.shape[-1]).T @ a.reshape(-1, d)
+    assert saved is O.causal_attention_bwd
+    return r
+
+
 MUTANTS = {
+    "layer_bwd_silu_derivative": ("layer_bwd", _bad_layer_bwd),
     "bwd_softmax_row_term_dropped": ("causal_attention_bwd", _bad_bwd_no_rowsum),
     "bwd_dk_unscaled": ("causal_attention_bwd", _bad_bwd_unscaled_dk),
     "range_lower_bound_late": ("attention_range", _bad_range),
