@@ -304,6 +304,40 @@ TSP_API int tsp_layer_fwd_streamed(const tsp_layer_desc* desc, const void* x_sha
                                    int32_t n_streams);
 
 /*
+ * Backward of one rank's layer, in two parts around the exchange of K/V gradients. The
+ * pages name training but do not describe the backward pass: this is the derivative of the
+ * forward (attention as tsp_attn_bwd; with A = O W_o^T, G = A W1^T, U = A W3^T,
+ * Y = (silu(G) U) W2^T, and dX = dQ W_q + dK W_k + dV W_v).
+ * Part 1, tsp_layer_bwd_attn_mlp: from the output gradient d_y (f32 [B 2C, d], the rank's
+ * rows) and the forward's q, o (bf16 [B 2C, d]) and lse (f32 [B, H, 2C]):
+ *   recomputes A and, per MLP shard in ring order j = (r - t) mod D, its gate pair; writes
+ *   dw13[j] (f32 [2 F/D, d]: the rank's share of dW1 rows then dW3 rows of shard j),
+ *   dw2[j] (f32 [d, F/D]), dw_o (f32 [d, d]), dq (f32 [B 2C, d]) and dk_full, dv_full
+ *   (f32 [B, S, d]: the rank's contributions at every position).
+ *   w_o bf16 [d, d]; w_mlp: D packed MLP shards as for tsp_layer_fwd_streamed (host array).
+ * Between the parts, each rank's dk/dv contributions are summed at the rank that owns the
+ * rows (a reduce-scatter; outside this library).
+ * Part 2, tsp_layer_bwd_qkv: from dq and the summed dk_own, dv_own (f32 [B 2C, d], the
+ *   rank's rows in local order), writes dx (f32 [B 2C, d]) and dw_qkv (f32 [3d, d], the
+ *   rank's share). x_shard and w_qkv as in tsp_layer_fwd.
+ * Weight gradients are the rank's shares: the model's gradient is their sum over ranks.
+ * Intermediates are rounded to bf16 before each GEMM (fp32 accumulation); outputs are f32.
+ * Workspace: tsp_layer_bwd_workspace_size(desc) bytes, for either part.
+ * Errors: as tsp_layer_fwd.
+ */
+TSP_API size_t tsp_layer_bwd_workspace_size(const tsp_layer_desc* desc);
+TSP_API int tsp_layer_bwd_attn_mlp(const tsp_layer_desc* desc, const void* q, const void* o,
+                                   const float* lse, const void* k_full, const void* v_full,
+                                   const void* w_o, const void* const* w_mlp, const float* d_y,
+                                   float* dq, float* dk_full, float* dv_full, float* dw_o,
+                                   float* const* dw13, float* const* dw2, void* ws,
+                                   size_t ws_bytes, tsp_stream_t stream);
+TSP_API int tsp_layer_bwd_qkv(const tsp_layer_desc* desc, const void* x_shard, const void* w_qkv,
+                              const float* dq, const float* dk_own, const float* dv_own,
+                              float* dx, float* dw_qkv, void* ws, size_t ws_bytes,
+                              tsp_stream_t stream);
+
+/*
  * Measurement hook (outside the method): phase timing of tsp_layer_fwd with HIP events
  * recorded on the call's own stream, between its launches.
  *   tsp_timing_start(max_calls)  creates (4 + 1) * max_calls events and arms the hook:

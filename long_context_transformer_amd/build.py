@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtsp.so")
-SOURCES = ["tsp_api.hip", "tsp_gemm.hip", "tsp_attn.hip", "tsp_attn_bwd.hip"]
+SOURCES = ["tsp_api.hip", "tsp_gemm.hip", "tsp_attn.hip", "tsp_attn_bwd.hip", "tsp_bwd_aux.hip"]
 # Per-source code generation flags. The attention kernel keeps its O accumulator and
 # scores in VGPRs (MFMA "VGPR form"); the rescale of O then stays a plain VALU multiply
 # instead of AGPR<->VGPR copies on every key block. It also runs with the IEEE mode bit

@@ -381,6 +381,169 @@ int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const void* w
 }
 
 
+namespace {
+
+// Workspace of the layer backward (both parts share one size: the larger).
+struct BwdCarve {
+  // part 1 (MLP, W_O, attention)
+  size_t a, at, dyb, dyt, da, gu, t2, dh, hb, dgu, t13, dgut, ht, dab, dat, wot, dob, ot, dsum;
+  // part 2 (QKV)
+  size_t dqkv, dqkvt, xt, wqkvt;
+  size_t total;
+};
+
+BwdCarve carve_bwd(const tsp_layer_desc* d) {
+  const size_t M = (size_t)d->batch * (size_t)(d->seq_len / d->fold);
+  const size_t dm = (size_t)d->d_model;
+  const size_t Fs = (size_t)(d->ffn / d->fold);
+  const size_t R = (size_t)(d->seq_len / d->fold);
+  BwdCarve c;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t off = at;
+    at += round_up(bytes, kAlign);
+    return off;
+  };
+  c.a = take(M * dm * 2);
+  c.at = take(M * dm * 2);
+  c.dyb = take(M * dm * 2);
+  c.dyt = take(M * dm * 2);
+  c.da = take(M * dm * 4);
+  c.gu = take(M * 2 * Fs * 2);
+  c.t2 = take(Fs * dm * 2);
+  c.dh = take(M * Fs * 4);
+  c.hb = take(M * Fs * 2);
+  c.dgu = take(M * 2 * Fs * 2);
+  c.t13 = take(2 * Fs * dm * 2);
+  c.dgut = take(M * 2 * Fs * 2);
+  c.ht = take(M * Fs * 2);
+  c.dab = take(M * dm * 2);
+  c.dat = take(M * dm * 2);
+  c.wot = take(dm * dm * 2);
+  c.dob = take(M * dm * 2);
+  c.ot = take(M * dm * 2);
+  c.dsum = take((size_t)d->batch * (size_t)d->n_heads * R * 4);
+  const size_t part1 = at;
+  at = 0;
+  c.dqkv = take(M * 3 * dm * 2);
+  c.dqkvt = take(M * 3 * dm * 2);
+  c.xt = take(M * dm * 2);
+  c.wqkvt = take(3 * dm * dm * 2);
+  c.total = part1 > at ? part1 : at;
+  return c;
+}
+
+}  // namespace
+
+size_t tsp_layer_bwd_workspace_size(const tsp_layer_desc* desc) {
+  if (check_desc(desc) != TSP_OK) return 0;
+  return carve_bwd(desc).total;
+}
+
+int tsp_layer_bwd_attn_mlp(const tsp_layer_desc* desc, const void* q, const void* o, const float* lse,
+                           const void* k_full, const void* v_full, const void* w_o, const void* const* w_mlp,
+                           const float* d_y, float* dq, float* dk_full, float* dv_full, float* dw_o,
+                           float* const* dw13, float* const* dw2, void* ws, size_t ws_bytes, tsp_stream_t stream) {
+  if (int rc = check_desc(desc)) return rc;
+  if (desc->batch == 0 || desc->seq_len == 0) return ok();
+  if (!q || !o || !lse || !k_full || !v_full || !w_o || !w_mlp || !d_y || !dq || !dk_full || !dv_full || !dw_o ||
+      !dw13 || !dw2 || !ws)
+    return fail(TSP_ERR_NULL, "a required pointer is NULL");
+  const int D = desc->fold;
+  for (int j = 0; j < D; ++j) {
+    if (!w_mlp[j] || !dw13[j] || !dw2[j]) return fail(TSP_ERR_NULL, "shard %d pointer is NULL", j);
+    if (misaligned(w_mlp[j]) || misaligned(dw13[j]) || misaligned(dw2[j]))
+      return fail(TSP_ERR_ALIGN, "shard %d pointer is not 16-byte aligned", j);
+  }
+  if (misaligned(q) || misaligned(o) || misaligned(k_full) || misaligned(v_full) || misaligned(w_o) ||
+      misaligned(d_y) || misaligned(dq) || misaligned(dk_full) || misaligned(dv_full) || misaligned(dw_o) ||
+      misaligned(ws) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(TSP_ERR_ALIGN, "device pointers must be 16-byte aligned (lse 4-byte)");
+  const BwdCarve c = carve_bwd(desc);
+  if (ws_bytes < c.total) return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, c.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int B = desc->batch, H = desc->n_heads, hd = desc->head_dim, d = desc->d_model, r = desc->rank;
+  const int64_t S = desc->seq_len;
+  const int M = (int)(B * (S / D));
+  const int Fs = desc->ffn / D;
+  const int64_t Fp = (int64_t)round_up((size_t)Fs, 8);  // W2 row stride in a packed MLP shard
+  char* base = static_cast<char*>(ws);
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  auto step = [](hipError_t e, const char* what) { return hip_status(e, what); };
+
+  // Recompute A = O W_o^T; transposes of A and of dY (bf16) for the weight gradients.
+  if (int rc = step(tsp::launch_proj_bf16(o, d, w_o, d, at(c.a), d, M, d, d, s), "W_O recompute")) return rc;
+  if (int rc = step(tsp::launch_transpose_bf16(at(c.a), d, at(c.at), M, M, d, s), "transpose")) return rc;
+  if (int rc = step(tsp::launch_convert_f32_bf16(d_y, d, at(c.dyb), d, M, d, s), "convert")) return rc;
+  if (int rc = step(tsp::launch_transpose_f32_bf16(d_y, d, at(c.dyt), M, M, d, s), "transpose")) return rc;
+  // MLP ring: shard j = (r - t) mod D at step t; dA summed in fp32 in that order.
+  for (int t = 0; t < D; ++t) {
+    const int j = ((r - t) % D + D) % D;
+    const tsp::bf16_t* w13 = static_cast<const tsp::bf16_t*>(w_mlp[j]);  // [2 Fs, d]: W1 rows, W3 rows
+    const tsp::bf16_t* w2j = w13 + 2 * (size_t)Fs * d;                   // [d, Fs], row stride Fp
+    if (int rc = step(tsp::launch_proj_bf16(at(c.a), d, w13, d, at(c.gu), 2 * Fs, M, 2 * Fs, d, s), "gate/up"))
+      return rc;
+    if (int rc = step(tsp::launch_transpose_bf16(w2j, Fp, at(c.t2), d, d, Fs, s), "transpose")) return rc;
+    if (int rc = step(tsp::launch_down_acc(at(c.dyb), d, at(c.t2), d, f32(c.dh), Fs, M, Fs, d, 0, s), "dH")) return rc;
+    if (int rc = step(tsp::launch_swiglu_bwd(at(c.gu), 2 * Fs, f32(c.dh), Fs, at(c.hb), Fs, at(c.dgu), 2 * Fs, M, Fs, s),
+                      "gate backward"))
+      return rc;
+    if (int rc = step(tsp::launch_transpose_bf16(w13, d, at(c.t13), 2 * Fs, 2 * Fs, d, s), "transpose")) return rc;
+    if (int rc = step(tsp::launch_down_acc(at(c.dgu), 2 * Fs, at(c.t13), 2 * Fs, f32(c.da), d, M, d, 2 * Fs, t > 0 ? 1 : 0,
+                                           s),
+                      "dA"))
+      return rc;
+    if (int rc = step(tsp::launch_transpose_bf16(at(c.dgu), 2 * Fs, at(c.dgut), M, M, 2 * Fs, s), "transpose")) return rc;
+    if (int rc = step(tsp::launch_down_acc(at(c.dgut), M, at(c.at), M, dw13[j], d, 2 * Fs, d, M, 0, s), "dW1/dW3"))
+      return rc;
+    if (int rc = step(tsp::launch_transpose_bf16(at(c.hb), Fs, at(c.ht), M, M, Fs, s), "transpose")) return rc;
+    if (int rc = step(tsp::launch_down_acc(at(c.dyt), M, at(c.ht), M, dw2[j], Fs, d, Fs, M, 0, s), "dW2")) return rc;
+  }
+  // W_O: dO = dA W_o (bf16, for the attention backward); dW_o = dA^T O.
+  if (int rc = step(tsp::launch_convert_f32_bf16(f32(c.da), d, at(c.dab), d, M, d, s), "convert")) return rc;
+  if (int rc = step(tsp::launch_transpose_f32_bf16(f32(c.da), d, at(c.dat), M, M, d, s), "transpose")) return rc;
+  if (int rc = step(tsp::launch_transpose_bf16(w_o, d, at(c.wot), d, d, d, s), "transpose")) return rc;
+  if (int rc = step(tsp::launch_proj_bf16(at(c.dab), d, at(c.wot), d, at(c.dob), d, M, d, d, s), "dO")) return rc;
+  if (int rc = step(tsp::launch_transpose_bf16(o, d, at(c.ot), M, M, d, s), "transpose")) return rc;
+  if (int rc = step(tsp::launch_down_acc(at(c.dat), M, at(c.ot), M, dw_o, d, d, d, M, 0, s), "dW_o")) return rc;
+  // Attention.
+  return step(tsp::launch_attn_bwd(q, k_full, v_full, o, lse, at(c.dob), dq, dk_full, dv_full, f32(c.dsum), B, S, D, r,
+                                   H, hd, desc->scale, s),
+              "attention backward");
+}
+
+int tsp_layer_bwd_qkv(const tsp_layer_desc* desc, const void* x_shard, const void* w_qkv, const float* dq,
+                      const float* dk_own, const float* dv_own, float* dx, float* dw_qkv, void* ws, size_t ws_bytes,
+                      tsp_stream_t stream) {
+  if (int rc = check_desc(desc)) return rc;
+  if (desc->batch == 0 || desc->seq_len == 0) return ok();
+  if (!x_shard || !w_qkv || !dq || !dk_own || !dv_own || !dx || !dw_qkv || !ws)
+    return fail(TSP_ERR_NULL, "a required pointer is NULL");
+  if (misaligned(x_shard) || misaligned(w_qkv) || misaligned(dq) || misaligned(dk_own) || misaligned(dv_own) ||
+      misaligned(dx) || misaligned(dw_qkv) || misaligned(ws))
+    return fail(TSP_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const BwdCarve c = carve_bwd(desc);
+  if (ws_bytes < c.total) return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, c.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = desc->d_model;
+  const int M = (int)(desc->batch * (desc->seq_len / desc->fold));
+  char* base = static_cast<char*>(ws);
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  auto step = [](hipError_t e, const char* what) { return hip_status(e, what); };
+  // dQKV = [dq | dk_own | dv_own] (bf16 [M, 3d]); dX = dQKV W_qkv; dW_qkv = dQKV^T X.
+  tsp::bf16_t* dqkv = static_cast<tsp::bf16_t*>(at(c.dqkv));
+  if (int rc = step(tsp::launch_convert_f32_bf16(dq, d, dqkv, 3 * d, M, d, s), "convert")) return rc;
+  if (int rc = step(tsp::launch_convert_f32_bf16(dk_own, d, dqkv + d, 3 * d, M, d, s), "convert")) return rc;
+  if (int rc = step(tsp::launch_convert_f32_bf16(dv_own, d, dqkv + 2 * d, 3 * d, M, d, s), "convert")) return rc;
+  if (int rc = step(tsp::launch_transpose_bf16(w_qkv, d, at(c.wqkvt), 3 * d, 3 * d, d, s), "transpose")) return rc;
+  if (int rc = step(tsp::launch_down_acc(dqkv, 3 * d, at(c.wqkvt), 3 * d, dx, d, M, d, 3 * d, 0, s), "dX")) return rc;
+  if (int rc = step(tsp::launch_transpose_bf16(dqkv, 3 * d, at(c.dqkvt), M, M, 3 * d, s), "transpose")) return rc;
+  if (int rc = step(tsp::launch_transpose_bf16(x_shard, d, at(c.xt), M, M, d, s), "transpose")) return rc;
+  return step(tsp::launch_down_acc(at(c.dqkvt), M, at(c.xt), M, dw_qkv, d, 3 * d, d, M, 0, s), "dW_qkv");
+}
+
 }  // extern "C"
 
 namespace {

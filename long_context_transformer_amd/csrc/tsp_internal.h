@@ -77,6 +77,18 @@ hipError_t launch_attn_bwd(const void* q, const void* k_full, const void* v_full
                            const void* d_o, float* dq, float* dk_full, float* dv_full, float* dsum, int B, int64_t S,
                            int D, int rank, int H, int hd, float scale, hipStream_t stream);
 
+// Memory-bound helpers of the layer backward (row-major, leading dimensions in elements).
+// dst[c][r] = src[r][c] for an R x C source; fp32 sources are rounded to bf16.
+hipError_t launch_transpose_bf16(const void* src, int64_t lds, void* dst, int64_t ldd, int R, int C,
+                                 hipStream_t stream);
+hipError_t launch_transpose_f32_bf16(const float* src, int64_t lds, void* dst, int64_t ldd, int R, int C,
+                                     hipStream_t stream);
+hipError_t launch_convert_f32_bf16(const float* src, int64_t lds, void* dst, int64_t ldd, int R, int C,
+                                   hipStream_t stream);
+// h = silu(g) u and dgu = [dh u silu'(g) | dh silu(g)] from gu = [g | u] and dh.
+hipError_t launch_swiglu_bwd(const void* gu, int64_t ldgu, const float* dh, int64_t lddh, void* h, int64_t ldh,
+                             void* dgu, int64_t lddgu, int M, int Fs, hipStream_t stream);
+
 hipError_t launch_attn_range(const void* q, const void* k_full, const void* v_full, float* o32, float* lse, int B,
                              int64_t S, int D, int rank, int H, int hd, float scale, int64_t key_lo, int64_t key_hi,
                              int accumulate, void* o_out, hipStream_t stream);

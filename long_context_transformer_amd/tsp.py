@@ -62,6 +62,12 @@ _SIGS = {
     "tsp_attn_bwd_workspace_size": (ctypes.c_size_t, [_I32, _I64, _I32, _I32]),
     "tsp_attn_bwd": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32, _I32,
                             ctypes.c_float, _VP, ctypes.c_size_t, _VP]),
+    "tsp_layer_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc)]),
+    "tsp_layer_bwd_attn_mlp": (_I32, [ctypes.POINTER(LayerDesc), _VP, _VP, _VP, _VP, _VP, _VP,
+                                      ctypes.POINTER(_VP), _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(_VP),
+                                      ctypes.POINTER(_VP), _VP, ctypes.c_size_t, _VP]),
+    "tsp_layer_bwd_qkv": (_I32, [ctypes.POINTER(LayerDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                 ctypes.c_size_t, _VP]),
     "tsp_timing_start": (_I32, [_I32]),
     "tsp_timing_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32, ctypes.POINTER(_I32)]),
 }
@@ -259,6 +265,32 @@ def pack_mlp_shards(w1, w3, w2, D):
         w2p[:, :Fs] = w2[:, sl]
         out.append(torch.cat([w1[sl].reshape(-1), w3[sl].reshape(-1), w2p.reshape(-1)]).contiguous())
     return out
+
+
+def layer_bwd_workspace_size(desc):
+    return int(load().tsp_layer_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def layer_bwd_attn_mlp(desc, q, o, lse, k_full, v_full, w_o, w_mlp, d_y, dq, dk_full, dv_full, dw_o, dw13, dw2,
+                       ws, ws_bytes=None, stream=None):
+    """w_mlp, dw13, dw2: sequences of D tensors (or addresses) indexed by shard id."""
+    D = desc.fold
+    arr = _VP * D
+    am, a13, a2 = (arr(*[_ptr(t) for t in seq]) for seq in (w_mlp, dw13, dw2))
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None and not isinstance(ws, int) else 0
+    _check(load().tsp_layer_bwd_attn_mlp(ctypes.byref(desc), _ptr(q), _ptr(o), _ptr(lse), _ptr(k_full),
+                                         _ptr(v_full), _ptr(w_o), am, _ptr(d_y), _ptr(dq), _ptr(dk_full),
+                                         _ptr(dv_full), _ptr(dw_o), a13, a2, _ptr(ws), ws_bytes,
+                                         _stream(stream, q)))
+
+
+def layer_bwd_qkv(desc, x_shard, w_qkv, dq, dk_own, dv_own, dx, dw_qkv, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None and not isinstance(ws, int) else 0
+    _check(load().tsp_layer_bwd_qkv(ctypes.byref(desc), _ptr(x_shard), _ptr(w_qkv), _ptr(dq), _ptr(dk_own),
+                                    _ptr(dv_own), _ptr(dx), _ptr(dw_qkv), _ptr(ws), ws_bytes,
+                                    _stream(stream, x_shard)))
 
 
 PHASES = ("qkv", "attention", "w_o", "mlp")
