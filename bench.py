@@ -321,6 +321,64 @@ def time_attn_bwd(st, w, rank, reps=3):
             "note": "two launches: dq (query-stationary), dk/dv (key-stationary); fp32 gradients"}
 
 
+def time_layer_bwd(st, w, rank, reps=3):
+    """Backward of the rank's layer: part 1 (MLP ring, W_O, attention) and part 2 (QKV) on
+    the layer's own forward activations, timed separately (HIP events on the launch stream).
+    The dK/dV exchange between the parts is outside the timing (another GPU's work). FLOPs
+    counted as the usual algorithmic backward: twice the forward GEMMs' FLOPs (an input and
+    a weight gradient each) plus 2.5x the forward attention; the recomputation of A and of
+    the gate pair is extra work not counted."""
+    import torch
+    from long_context_transformer_amd import tsp
+    B, S, D, H, hd, d, F = w.B, w.S, w.D, w.n_heads, w.head_dim, w.d_model, w.ffn
+    R, Fs = S // D, F // D
+    dev = st["dev"]
+    q = torch.empty((B, R, d), dtype=torch.bfloat16, device="cuda")
+    tsp.qkv_fwd(st["xs"], dev["w_qkv"], q, st["kf"], st["vf"], B, S, D, rank, H, hd)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, R), dtype=torch.float32, device="cuda")
+    tsp.attn_fwd(q, st["kf"], st["vf"], o, lse, B, S, D, rank, H, hd)
+    packed = tsp.pack_mlp_shards(dev["w1"], dev["w3"], dev["w2"], D)
+    gen = torch.Generator("cuda").manual_seed(7)
+    dy = torch.randn((B, R, d), device="cuda", generator=gen) * 1e-2
+    dq = torch.empty((B, R, d), device="cuda")
+    dk = torch.empty((B, S, d), device="cuda")
+    dv = torch.empty_like(dk)
+    dwo = torch.empty((d, d), device="cuda")
+    dw13 = [torch.empty((2 * Fs, d), device="cuda") for _ in range(D)]
+    dw2 = [torch.empty((d, Fs), device="cuda") for _ in range(D)]
+    dx = torch.empty((B, R, d), device="cuda")
+    dwqkv = torch.empty((3 * d, d), device="cuda")
+    desc = st["desc"]
+    ws = torch.empty(tsp.layer_bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    idx = torch.from_numpy(tsp.zigzag_index(S, D, rank)).cuda()
+    part1 = lambda: tsp.layer_bwd_attn_mlp(desc, q, o, lse, st["kf"], st["vf"], dev["w_o"], packed, dy, dq, dk, dv,
+                                           dwo, dw13, dw2, ws)
+    dk_own = dk.index_select(1, idx).contiguous()
+    dv_own = dv.index_select(1, idx).contiguous()
+    part2 = lambda: tsp.layer_bwd_qkv(desc, st["xs"], dev["w_qkv"], dq, dk_own, dv_own, dx, dwqkv, ws)
+    res = {}
+    for name, fn in (("attn_mlp", part1), ("qkv", part2)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_ms"] = round(e0.elapsed_time(e1) / reps, 3)
+    fwd, attn = layer_flops(B, S, D, d, H, hd, F)
+    fl = 2 * (fwd - attn) + 2.5 * attn
+    ms = res["attn_mlp_ms"] + res["qkv_ms"]
+    tf = fl / (ms * 1e-3) / 1e12
+    res.update({"ms": round(ms, 3), "flops": fl, "tflops": round(tf, 1),
+                "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)})
+    del q, o, lse, packed, dy, dq, dk, dv, dwo, dw13, dw2, dx, dwqkv, ws, dk_own, dv_own
+    torch.cuda.empty_cache()
+    return res
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -384,6 +442,7 @@ def main():
                     help="also measure one rank's device memory for every workload (weight-streamed layer) "
                     "against the analytic per-layout counts; one JSON line each to this file")
     ap.add_argument("--attn-bwd", action="store_true", help="also time the attention backward (tsp_attn_bwd)")
+    ap.add_argument("--layer-bwd", action="store_true", help="also time the layer backward (both parts)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB plain copy kernel first (counter calibration)")
     ap.add_argument("--sweep", default=None, help="also time every workload (and every rank of the "
@@ -435,6 +494,11 @@ def main():
         attn_bwd = time_attn_bwd(st, w, args.rank)
         print("# attention backward " + json.dumps(attn_bwd), file=sys.stderr, flush=True)
 
+    layer_bwd = None
+    if args.layer_bwd:
+        layer_bwd = time_layer_bwd(st, w, args.rank)
+        print("# layer backward " + json.dumps(layer_bwd), file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, st["inputs"], args.rank, args.cpu_rows)
@@ -472,6 +536,8 @@ def main():
         out["weight_streamed_layer"] = streamed
     if attn_bwd:
         out["attention_backward"] = attn_bwd
+    if layer_bwd:
+        out["layer_backward"] = layer_bwd
     print(json.dumps(out), flush=True)
 
     if args.memory:
