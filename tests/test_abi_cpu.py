@@ -175,6 +175,26 @@ def test_attn_bwd_errors():
     f(*[None] * 9, 0, 256, 4, 1, 2, 64, None, 0)              # empty problem: OK, nothing read
 
 
+def test_layer_bwd_errors():
+    good = _desc()
+    ws = tsp.layer_bwd_workspace_size(good)
+    assert ws > 0 and tsp.layer_bwd_workspace_size(_desc(ffn=690)) == 0
+    sh = [A] * 4
+    f1, f2 = tsp.layer_bwd_attn_mlp, tsp.layer_bwd_qkv
+    p1 = [A] * 6  # q, o, lse, k_full, v_full, w_o
+    assert _code(f1, _desc(S=100), *p1, sh, A, A, A, A, A, sh, sh, A, ws, 0) == 2
+    assert _code(f1, _desc(rank=4), *p1, sh, A, A, A, A, A, sh, sh, A, ws, 0) == 3
+    assert _code(f1, good, *p1, [A, None, A, A], A, A, A, A, A, sh, sh, A, ws, 0) == 1
+    assert _code(f1, good, *p1, sh, A, A, A, A, A, sh, [A, A, MIS, A], A, ws, 0) == 6
+    assert _code(f1, good, *p1, sh, A, A, A, A, A, sh, sh, A, ws - 1, 0) == 5
+    assert _code(f2, good, A, A, A, A, A, A, A, A, ws - 1, 0) == 5
+    assert _code(f2, good, A, A, None, A, A, A, A, A, ws, 0) == 1
+    assert _code(f2, good, A, A, A, A, A, MIS, A, A, ws, 0) == 6
+    e = _desc(B=0)
+    f1(e, *[None] * 6, [None] * 4, None, None, None, None, None, [None] * 4, [None] * 4, None, 0)
+    f2(e, *[None] * 8, 0)
+
+
 def test_streamed_layer_workspace_and_errors():
     good = _desc()
     M, d, Fs, dg = 64, 256, 172, 64
