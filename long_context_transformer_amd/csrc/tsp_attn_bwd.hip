@@ -161,6 +161,8 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const bool valid = qi < a.rows;
   const int qic = valid ? qi : a.rows - 1;
   const int qpos = (int)zigzag_pos(qic, a.C, a.rank, a.D);
+  // the wave's first row has its lowest position (local rows ascend in position)
+  const int wave_pos0 = (int)zigzag_pos(min(row0 + 32 * wave, a.rows - 1), a.C, a.rank, a.D);
   const int64_t rowoff = ((int64_t)b * a.rows + qic) * tok + (int64_t)h * HD + 8 * hl;
   bf16x8 qf[KS], df[KS];
   float dsum = 0.0f;
@@ -211,11 +213,16 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         dp = mfma32x32x16(row_frag<HD>(vtile, 32 * kb, l32, hl, ks), df[ks], dp);
       }
       float ds[16];
+      if (k0 + 31 <= wave_pos0) {  // every row of the wave sees every key of the block
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const float p = key <= qpos ? __builtin_amdgcn_exp2f(s[r] * c2 - lse2) : 0.0f;
-        ds[r] = p * (dp[r] - dsum);
+        for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(s[r] * c2 - lse2) * (dp[r] - dsum);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const float p = key <= qpos ? __builtin_amdgcn_exp2f(s[r] * c2 - lse2) : 0.0f;
+          ds[r] = p * (dp[r] - dsum);
+        }
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -257,6 +264,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int64_t tok = (int64_t)a.H * HD;
 
   const int kj = key0 + 32 * wave + l32;
+  const int wave_klast = key0 + 32 * wave + 31;
   const bool kvalid = kj < a.S;
   const int kjc = kvalid ? kj : (int)a.S - 1;
   const int64_t keyoff = ((int64_t)b * a.S + kjc) * tok + (int64_t)h * HD + 8 * hl;
@@ -323,13 +331,28 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
         dp = mfma32x32x16(row_frag<HD>(otile, 32 * qb, l32, hl, ks), row_frag<HD>(vkeys, 32 * wave, l32, hl, ks), dp);
       }
       float p[16], ds[16];
+      // The block's first row has its lowest position: if that row sees the wave's last key,
+      // every row sees every key and the mask is skipped.
+      if (q0 + 31 < a.rows && wave_klast < a.S && wave_klast <= (int)zigzag_pos(q0, a.C, a.rank, a.D)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
-        const int row = q0 + qr;
-        const bool ok = kvalid && row < a.rows && kj <= (int)zigzag_pos(min(row, a.rows - 1), a.C, a.rank, a.D);
-        p[r] = ok ? __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[32 * qb + qr]) : 0.0f;
-        ds[r] = p[r] * (dp[r] - d_s[32 * qb + qr]);
+        for (int r = 0; r < 16; ++r) {
+          const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
+          p[r] = __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[32 * qb + qr]);
+          ds[r] = p[r] * (dp[r] - d_s[32 * qb + qr]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // every operand read and the exponential unconditionally, then a select: a load
+          // under the condition would make a branch and a wait per register
+          const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);
+          const int row = q0 + qr;
+          const float e = __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[32 * qb + qr]);
+          const float dsub = dp[r] - d_s[32 * qb + qr];
+          const bool ok = kvalid & (row < a.rows) & (kj <= (int)zigzag_pos(min(row, a.rows - 1), a.C, a.rank, a.D));
+          p[r] = ok ? e : 0.0f;
+          ds[r] = p[r] * dsub;
+        }
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
