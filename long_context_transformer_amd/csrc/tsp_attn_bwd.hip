@@ -44,9 +44,17 @@ struct BLay {
   static constexpr int ROWB = HD * 2;  // bytes per row
   static constexpr int CPR = ROWB / 16;
   static constexpr int TILEB = kStage * ROWB;
-  // 16-byte chunk c of row r is stored at chunk c ^ sw(r). Transpose reads touch 4 rows
-  // (aligned to 4) x 4 chunks; this swizzle spreads them over the banks.
-  __device__ static int sw(int r) { return HD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+  // 16-byte chunk c of row r is stored at chunk c ^ sw(r). Each tile is read both ways: row
+  // fragments (16 consecutive rows, one chunk) and transpose reads (4 rows aligned to 4 x 4
+  // chunks aligned to 4). The swizzle's low bits separate the 16 rows of a row read and its
+  // high bits the 4 rows of a transpose read, so that both cover 16 distinct 16-byte bank
+  // groups (one 256-byte pass of the LDS).
+  __device__ static int sw(int r) {
+    return HD == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+  // A transpose read's second 8 rows (rows r + 8 for r < 8, in a 16-aligned group) have the
+  // swizzle sw(r) ^ 2: their offset is the first read's with bit 5 flipped, 8 rows down.
+  static constexpr int TR_HI_XOR = 32;
 };
 
 struct BwdArgs {
@@ -127,18 +135,19 @@ __device__ __forceinline__ int tr_offset(int lane, int db) {
 template <int HD>
 __device__ __forceinline__ bf16x8 tr_frag(const char* tile, int off, int rb) {
   using L = BLay<HD>;
-  const lds_s16x4* p = (const lds_s16x4*)(tile + off + rb * L::ROWB);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + L::ROWB));
+  const char* base = tile + rb * L::ROWB;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + (off ^ L::TR_HI_XOR) + 8 * L::ROWB));
   const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
   return as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
 }
 
-// Registers 8 half .. 8 half + 7 of an MFMA result, as bf16 (round to nearest even).
-__device__ __forceinline__ bf16x8 pack_half(const float (&x)[16], int half) {
+// Eight values (registers 8 half .. 8 half + 7 of an MFMA result) as bf16, rounded to
+// nearest even: the B operand of the products that consume them.
+__device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
   uint32_t w[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[8 * half + 2 * e], x[8 * half + 2 * e + 1]);
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
   return as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
 }
 
@@ -212,21 +221,21 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         s = mfma32x32x16(row_frag<HD>(ktile, 32 * kb, l32, hl, ks), qf[ks], s);
         dp = mfma32x32x16(row_frag<HD>(vtile, 32 * kb, l32, hl, ks), df[ks], dp);
       }
-      float ds[16];
-      if (k0 + 31 <= wave_pos0) {  // every row of the wave sees every key of the block
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(s[r] * c2 - lse2) * (dp[r] - dsum);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const float p = key <= qpos ? __builtin_amdgcn_exp2f(s[r] * c2 - lse2) : 0.0f;
-          ds[r] = p * (dp[r] - dsum);
-        }
-      }
+      // dS one half of the block (registers 8 half .. 8 half + 7) at a time, packed and
+      // consumed by the dQ products before the next half is computed
+      const bool whole = k0 + 31 <= wave_pos0;  // every row of the wave sees every key of the block
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const bf16x8 dsf = pack_half(ds, half);
+        float ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * half + e;
+          const float ex = __builtin_amdgcn_exp2f(s[r] * c2 - lse2);
+          const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const float p = (whole || key <= qpos) ? ex : 0.0f;
+          ds[e] = p * (dp[r] - dsum);
+        }
+        const bf16x8 dsf = pack8(ds);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           dqacc[db] = mfma32x32x16(tr_frag<HD>(ktile, troff[db], 32 * kb + 16 * half), dsf, dqacc[db]);
@@ -330,34 +339,35 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
         s = mfma32x32x16(row_frag<HD>(qtile, 32 * qb, l32, hl, ks), kf[ks], s);
         dp = mfma32x32x16(row_frag<HD>(otile, 32 * qb, l32, hl, ks), row_frag<HD>(vkeys, 32 * wave, l32, hl, ks), dp);
       }
-      float p[16], ds[16];
-      // The block's first row has its lowest position: if that row sees the wave's last key,
-      // every row sees every key and the mask is skipped.
-      if (q0 + 31 < a.rows && wave_klast < a.S && wave_klast <= (int)zigzag_pos(q0, a.C, a.rank, a.D)) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
-          p[r] = __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[32 * qb + qr]);
-          ds[r] = p[r] * (dp[r] - d_s[32 * qb + qr]);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // every operand read and the exponential unconditionally, then a select: a load
-          // under the condition would make a branch and a wait per register
-          const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);
-          const int row = q0 + qr;
-          const float e = __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[32 * qb + qr]);
-          const float dsub = dp[r] - d_s[32 * qb + qr];
-          const bool ok = kvalid & (row < a.rows) & (kj <= (int)zigzag_pos(min(row, a.rows - 1), a.C, a.rank, a.D));
-          p[r] = ok ? e : 0.0f;
-          ds[r] = p[r] * dsub;
-        }
-      }
+      // P and dS one half of the block (registers 8 half .. 8 half + 7) at a time, each packed
+      // and consumed by the dV and dK products before the next half is computed. The block's
+      // first row has its lowest position: if that row sees the wave's last key, every row
+      // sees every key and the mask is skipped.
+      const bool whole =
+          q0 + 31 < a.rows && wave_klast < a.S && wave_klast <= (int)zigzag_pos(q0, a.C, a.rank, a.D);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const bf16x8 pf = pack_half(p, half);
-        const bf16x8 dsf = pack_half(ds, half);
+        float p[8], ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * half + e;
+          const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
+          // every operand read and the exponential unconditionally, then a select: a load
+          // under the condition would make a branch and a wait per register
+          const float ex = __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[32 * qb + qr]);
+          const float dsub = dp[r] - d_s[32 * qb + qr];
+          if (whole) {
+            p[e] = ex;
+          } else {
+            const int row = q0 + qr;
+            const bool ok =
+                kvalid & (row < a.rows) & (kj <= (int)zigzag_pos(min(row, a.rows - 1), a.C, a.rank, a.D));
+            p[e] = ok ? ex : 0.0f;
+          }
+          ds[e] = p[e] * dsub;
+        }
+        const bf16x8 pf = pack8(p);
+        const bf16x8 dsf = pack8(ds);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           dvacc[db] = mfma32x32x16(tr_frag<HD>(otile, troff[db], 32 * qb + 16 * half), pf, dvacc[db]);
