@@ -15,8 +15,9 @@
 // (and dP^T = V dO^T) leave each lane with one query's scores, which packed to bf16 are the
 // B operand of dQ^T += K^T dS^T, whose A operand comes from LDS by transpose reads. The
 // key-stationary kernel uses S = Q K^T instead, so that each lane holds one key's column.
-// Tiles are staged into LDS through registers: the next stage's global loads are issued
-// before the current stage's MFMAs (no DMA ring).
+// The query-stationary kernel stages K/V tiles through registers (the next stage's global
+// loads are issued before the current stage's MFMAs). The key-stationary kernel, with no
+// registers to spare, stages its Q/dO blocks by LDS DMA into a two-stage ring.
 #include <hip/hip_runtime.h>
 
 #include "tsp_device.h"
@@ -31,7 +32,8 @@ constexpr int kDqRows = 32 * kDqWaves;
 constexpr int kBwdWaves = 4;                // key-stationary: 128 keys per workgroup
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kRowsPerWg = 32 * kBwdWaves;
-constexpr int kStage = 64;                  // rows staged per LDS fill: two 32-row blocks
+constexpr int kStage = 64;                  // query-stationary: keys staged per LDS fill
+constexpr int kKvStage = 32;                // key-stationary: query rows per DMA stage
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -257,14 +259,19 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 template <int HD>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv(BwdArgs a) {
   using L = BLay<HD>;
-  constexpr int KS = L::KS, DB = L::DB;
-  __shared__ __attribute__((aligned(16))) char qtile[L::TILEB];
-  __shared__ __attribute__((aligned(16))) char otile[L::TILEB];  // dO
+  constexpr int KS = L::KS, DB = L::DB, ROWB = L::ROWB, CPR = L::CPR;
+  constexpr int STB = kKvStage * ROWB;              // bytes of one staged Q (or dO) block
+  constexpr int NDMA = STB / (kBwdThreads * 16);    // 16-byte DMA loads per thread per block
+  static_assert(NDMA >= 1 && NDMA * kBwdThreads * 16 == STB, "whole block per stage");
+  // Q and dO rings of two 32-row stages, filled by LDS DMA one stage ahead of the MFMAs
+  __shared__ __attribute__((aligned(1024))) char qring[2 * STB];
+  __shared__ __attribute__((aligned(1024))) char oring[2 * STB];
   // V rows of the workgroup's keys: read as B fragments of dP = dO V^T each block (kept in
   // LDS rather than registers, so that two waves fit on a SIMD)
-  __shared__ __attribute__((aligned(16))) char vkeys[kRowsPerWg * L::ROWB];
-  __shared__ float lse_s[kStage], d_s[kStage];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hl = lane >> 5;
+  __shared__ __attribute__((aligned(16))) char vkeys[kRowsPerWg * ROWB];
+  __shared__ float lse_s[2][kKvStage], d_s[2][kKvStage];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_kt = (int)((a.S + kRowsPerWg - 1) / kRowsPerWg);
   const int bh = blockIdx.x / n_kt;
   const int kt = (int)(blockIdx.x - bh * n_kt);
@@ -272,8 +279,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int key0 = kt * kRowsPerWg;
   const int64_t tok = (int64_t)a.H * HD;
 
-  const int kj = key0 + 32 * wave + l32;
-  const int wave_klast = key0 + 32 * wave + 31;
+  const int kw0 = key0 + 32 * wave;  // the wave's first key
+  const int kj = kw0 + l32;
+  const int wave_klast = kw0 + 31;
   const bool kvalid = kj < a.S;
   const int kjc = kvalid ? kj : (int)a.S - 1;
   const int64_t keyoff = ((int64_t)b * a.S + kjc) * tok + (int64_t)h * HD + 8 * hl;
@@ -282,10 +290,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   for (int s = 0; s < KS; ++s) kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(a.k + keyoff + 16 * s));
   {
     const bf16_t* vrows = a.v + (int64_t)b * a.S * tok + (int64_t)h * HD;
-    for (int lin = tid; lin < kRowsPerWg * L::CPR; lin += kBwdThreads) {
-      const int r = lin / L::CPR, c = lin - (lin / L::CPR) * L::CPR;
+    for (int lin = tid; lin < kRowsPerWg * CPR; lin += kBwdThreads) {
+      const int r = lin / CPR, c = lin - (lin / CPR) * CPR;
       const int gr = (int)min((int64_t)key0 + r, a.S - 1);
-      *reinterpret_cast<uint4*>(vkeys + r * L::ROWB + 16 * (c ^ L::sw(r))) =
+      *reinterpret_cast<uint4*>(vkeys + r * ROWB + 16 * (c ^ L::sw(r))) =
           *reinterpret_cast<const uint4*>(vrows + (int64_t)gr * tok + 8 * c);
     }
   }
@@ -309,70 +317,103 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int db = 0; db < DB; ++db) troff[db] = tr_offset<HD>(lane, db);
 
-  const bf16_t* qseq = a.q + (int64_t)b * a.rows * tok + (int64_t)h * HD;
-  const bf16_t* oseq = a.d_o + (int64_t)b * a.rows * tok + (int64_t)h * HD;
+  // ---- stage loads: global -> LDS by DMA, 16 bytes per lane, lane-linear within the 1 KB a
+  // wave instruction writes. Load p of this wave fills linear chunk (NW p + wave) 64 + lane
+  // of the block: row lin / CPR at physical chunk lin % CPR, which holds logical chunk
+  // (lin % CPR) ^ sw(row); the source address is chosen accordingly.
+  const char* qseq = reinterpret_cast<const char*>(a.q + (int64_t)b * a.rows * tok + (int64_t)h * HD);
+  const char* oseq = reinterpret_cast<const char*>(a.d_o + (int64_t)b * a.rows * tok + (int64_t)h * HD);
+  const uint32_t tokb = (uint32_t)(tok * 2);
+  int drow[NDMA], dch[NDMA];
+#pragma unroll
+  for (int p = 0; p < NDMA; ++p) {
+    const int lin = (kBwdWaves * p + wave) * 64 + lane;
+    drow[p] = lin / CPR;
+    dch[p] = 16 * ((lin % CPR) ^ L::sw(drow[p]));
+  }
+  auto issue = [&] __device__(int buf, int i) {
+    const int lim = a.rows - 1 - i;  // rows past the last local row repeat it (masked)
+    const char* qb0 = qseq + (int64_t)i * tokb;
+    const char* ob0 = oseq + (int64_t)i * tokb;
+    const uint32_t lq = lds_addr(qring) + buf * STB + wave * 1024;
+    const uint32_t lo = lds_addr(oring) + buf * STB + wave * 1024;
+#pragma unroll
+    for (int p = 0; p < NDMA; ++p) {
+      const uint32_t roff = (uint32_t)min(drow[p], lim) * tokb + dch[p];
+      dma16_sbase(qb0, roff, lq + kBwdWaves * p * 1024);
+      dma16_sbase(ob0, roff, lo + kBwdWaves * p * 1024);
+    }
+  };
   const int64_t lrow = ((int64_t)b * a.H + h) * a.rows;
-  // Staged without a register prefetch: the accumulators and K fragments leave no room for
-  // it at two waves per SIMD, and the other wave on the SIMD covers the load latency.
-  for (int i = i0; i < a.rows; i += kStage) {
-    __syncthreads();
-    {
-      Staged<HD, kBwdThreads> sq, so;
-      load_rows<HD>(sq, qseq, tok, i, a.rows - 1, tid);
-      load_rows<HD>(so, oseq, tok, i, a.rows - 1, tid);
-      store_rows<HD>(qtile, sq, tid);
-      store_rows<HD>(otile, so, tid);
-    }
-    if (tid < kStage) {
+  float lse_n = 0.0f, d_n = 0.0f;  // lse (log2 units) and D of row i + tid of the next stage
+  auto fetch_rows = [&] __device__(int i) {
+    if (tid < kKvStage) {
       const int ri = min(i + tid, a.rows - 1);
-      lse_s[tid] = a.lse[lrow + ri] * kLog2e;
-      d_s[tid] = a.dsum[lrow + ri];
+      lse_n = a.lse[lrow + ri] * kLog2e;
+      d_n = a.dsum[lrow + ri];
+    }
+  };
+  if (i0 < a.rows) {
+    issue(0, i0);
+    fetch_rows(i0);
+  }
+  int buf = 0;
+  for (int q0 = i0; q0 < a.rows; q0 += kKvStage, buf ^= 1) {
+    // this wave's loads of the stage have landed; its lse and D go to LDS; then one barrier:
+    // every wave's loads have landed, and every wave is done with the other buffer
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if (tid < kKvStage) {
+      lse_s[buf][tid] = lse_n;
+      d_s[buf][tid] = d_n;
     }
     __syncthreads();
+    if (q0 + kKvStage < a.rows) {
+      issue(buf ^ 1, q0 + kKvStage);
+      fetch_rows(q0 + kKvStage);
+    }
+    const char* qtile = qring + buf * STB;
+    const char* otile = oring + buf * STB;
+    // no row of the block sees the wave's keys (its last row has the highest position)
+    if (kw0 > (int)zigzag_pos(min(q0 + kKvStage - 1, a.rows - 1), a.C, a.rank, a.D)) continue;
+    f32x16 s = {}, dp = {};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int q0 = i + 32 * qb;
-      if (q0 >= a.rows) break;  // the same for the whole workgroup
-      f32x16 s = {}, dp = {};
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32x32x16(row_frag<HD>(qtile, 0, l32, hl, ks), kf[ks], s);
+      dp = mfma32x32x16(row_frag<HD>(otile, 0, l32, hl, ks), row_frag<HD>(vkeys, 32 * wave, l32, hl, ks), dp);
+    }
+    // P and dS one half of the block (registers 8 half .. 8 half + 7) at a time, each packed
+    // and consumed by the dV and dK products before the next half is computed. The block's
+    // first row has its lowest position: if that row sees the wave's last key, every row
+    // sees every key and the mask is skipped.
+    const bool whole =
+        q0 + 31 < a.rows && wave_klast < a.S && wave_klast <= (int)zigzag_pos(q0, a.C, a.rank, a.D);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32x32x16(row_frag<HD>(qtile, 32 * qb, l32, hl, ks), kf[ks], s);
-        dp = mfma32x32x16(row_frag<HD>(otile, 32 * qb, l32, hl, ks), row_frag<HD>(vkeys, 32 * wave, l32, hl, ks), dp);
+    for (int half = 0; half < 2; ++half) {
+      float p[8], ds[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * half + e;
+        const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
+        // every operand read and the exponential unconditionally, then a select: a load
+        // under the condition would make a branch and a wait per register
+        const float ex = __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[buf][qr]);
+        const float dsub = dp[r] - d_s[buf][qr];
+        if (whole) {
+          p[e] = ex;
+        } else {
+          const int row = q0 + qr;
+          const bool ok =
+              kvalid & (row < a.rows) & (kj <= (int)zigzag_pos(min(row, a.rows - 1), a.C, a.rank, a.D));
+          p[e] = ok ? ex : 0.0f;
+        }
+        ds[e] = p[e] * dsub;
       }
-      // P and dS one half of the block (registers 8 half .. 8 half + 7) at a time, each packed
-      // and consumed by the dV and dK products before the next half is computed. The block's
-      // first row has its lowest position: if that row sees the wave's last key, every row
-      // sees every key and the mask is skipped.
-      const bool whole =
-          q0 + 31 < a.rows && wave_klast < a.S && wave_klast <= (int)zigzag_pos(q0, a.C, a.rank, a.D);
+      const bf16x8 pf = pack8(p);
+      const bf16x8 dsf = pack8(ds);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float p[8], ds[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * half + e;
-          const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
-          // every operand read and the exponential unconditionally, then a select: a load
-          // under the condition would make a branch and a wait per register
-          const float ex = __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[32 * qb + qr]);
-          const float dsub = dp[r] - d_s[32 * qb + qr];
-          if (whole) {
-            p[e] = ex;
-          } else {
-            const int row = q0 + qr;
-            const bool ok =
-                kvalid & (row < a.rows) & (kj <= (int)zigzag_pos(min(row, a.rows - 1), a.C, a.rank, a.D));
-            p[e] = ok ? ex : 0.0f;
-          }
-          ds[e] = p[e] * dsub;
-        }
-        const bf16x8 pf = pack8(p);
-        const bf16x8 dsf = pack8(ds);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dvacc[db] = mfma32x32x16(tr_frag<HD>(otile, troff[db], 32 * qb + 16 * half), pf, dvacc[db]);
-          dkacc[db] = mfma32x32x16(tr_frag<HD>(qtile, troff[db], 32 * qb + 16 * half), dsf, dkacc[db]);
-        }
+      for (int db = 0; db < DB; ++db) {
+        dvacc[db] = mfma32x32x16(tr_frag<HD>(otile, troff[db], 16 * half), pf, dvacc[db]);
+        dkacc[db] = mfma32x32x16(tr_frag<HD>(qtile, troff[db], 16 * half), dsf, dkacc[db]);
       }
     }
   }
