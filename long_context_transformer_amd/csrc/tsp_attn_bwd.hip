@@ -15,9 +15,10 @@
 // (and dP^T = V dO^T) leave each lane with one query's scores, which packed to bf16 are the
 // B operand of dQ^T += K^T dS^T, whose A operand comes from LDS by transpose reads. The
 // key-stationary kernel uses S = Q K^T instead, so that each lane holds one key's column.
-// The query-stationary kernel stages K/V tiles through registers (the next stage's global
-// loads are issued before the current stage's MFMAs). The key-stationary kernel, with no
-// registers to spare, stages its Q/dO blocks by LDS DMA into a two-stage ring.
+// Both kernels stage their streamed operand by LDS DMA (global_load_lds): the K/V tiles of
+// the query-stationary kernel in a three-stage ring, the Q/dO blocks of the key-stationary
+// kernel in a two-stage ring. The source address of each lane's 16 bytes is chosen so that
+// the tile lands in LDS already swizzled.
 #include <hip/hip_runtime.h>
 
 #include "tsp_device.h"
@@ -34,6 +35,7 @@ constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kRowsPerWg = 32 * kBwdWaves;
 constexpr int kStage = 64;                  // query-stationary: keys staged per LDS fill
 constexpr int kKvStage = 32;                // key-stationary: query rows per DMA stage
+constexpr int kDqRing = 3;                  // query-stationary: K/V stages in the DMA ring
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -74,42 +76,6 @@ struct BwdArgs {
   int rows, D, rank, H;
   float scale;
 };
-
-// Rows [first, first + kStage) of a row-major [*, HD] bf16 matrix (row stride tok elements),
-// staged through registers: load_rows reads a thread's 16-byte chunks from global memory
-// (rows past `last` repeat row `last`; their results are masked), store_rows writes them
-// to an LDS tile. Loading the next stage before computing the current one hides the global
-// latency behind the MFMAs.
-template <int HD, int NT>
-struct Staged {
-  static constexpr int N = kStage * BLay<HD>::CPR / NT;  // chunks per thread (NT threads)
-  static_assert(N >= 1 && N * NT == kStage * BLay<HD>::CPR, "whole tile per stage");
-  uint4 v[N];
-};
-
-template <int HD, int NT>
-__device__ __forceinline__ void load_rows(Staged<HD, NT>& st, const bf16_t* src, int64_t tok, int first, int last,
-                                          int tid) {
-  using L = BLay<HD>;
-#pragma unroll
-  for (int n = 0; n < Staged<HD, NT>::N; ++n) {
-    const int lin = tid + n * NT;
-    const int r = lin / L::CPR, c = lin - (lin / L::CPR) * L::CPR;
-    const int gr = min(first + r, last);
-    st.v[n] = *reinterpret_cast<const uint4*>(src + (int64_t)gr * tok + 8 * c);
-  }
-}
-
-template <int HD, int NT>
-__device__ __forceinline__ void store_rows(char* tile, const Staged<HD, NT>& st, int tid) {
-  using L = BLay<HD>;
-#pragma unroll
-  for (int n = 0; n < Staged<HD, NT>::N; ++n) {
-    const int lin = tid + n * NT;
-    const int r = lin / L::CPR, c = lin - (lin / L::CPR) * L::CPR;
-    *reinterpret_cast<uint4*>(tile + r * L::ROWB + 16 * (c ^ L::sw(r))) = st.v[n];
-  }
-}
 
 // A or B fragment of a 32-row block: lane (l32, hl) gets row rb + l32, dims 16 s + 8 hl .. +7.
 template <int HD>
@@ -157,9 +123,14 @@ template <int HD>
 __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq(BwdArgs a) {
   using L = BLay<HD>;
   constexpr int KS = L::KS, DB = L::DB;
-  __shared__ __attribute__((aligned(16))) char ktile[L::TILEB];
-  __shared__ __attribute__((aligned(16))) char vtile[L::TILEB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hl = lane >> 5;
+  constexpr int CPR = L::CPR, TILEB = L::TILEB;
+  constexpr int NDMA = TILEB / (kDqThreads * 16);  // 16-byte DMA loads per thread per tile
+  static_assert(NDMA >= 1 && NDMA * kDqThreads * 16 == TILEB, "whole tile per stage");
+  // K and V rings of kDqRing 64-key stages, filled by LDS DMA two stages ahead of the MFMAs
+  __shared__ __attribute__((aligned(1024))) char kring[kDqRing * TILEB];
+  __shared__ __attribute__((aligned(1024))) char vring[kDqRing * TILEB];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_qt = (a.rows + kDqRows - 1) / kDqRows;
   const int bh = blockIdx.x / n_qt;
   const int qt = n_qt - 1 - (int)(blockIdx.x - bh * n_qt);  // heaviest tile first
@@ -174,6 +145,8 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const int qpos = (int)zigzag_pos(qic, a.C, a.rank, a.D);
   // the wave's first row has its lowest position (local rows ascend in position)
   const int wave_pos0 = (int)zigzag_pos(min(row0 + 32 * wave, a.rows - 1), a.C, a.rank, a.D);
+  // and its last row the highest: key blocks past it add nothing to the wave's rows
+  const int wave_pos1 = (int)zigzag_pos(min(row0 + 32 * wave + 31, a.rows - 1), a.C, a.rank, a.D);
   const int64_t rowoff = ((int64_t)b * a.rows + qic) * tok + (int64_t)h * HD + 8 * hl;
   bf16x8 qf[KS], df[KS];
   float dsum = 0.0f;
@@ -198,25 +171,56 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
   for (int db = 0; db < DB; ++db) troff[db] = tr_offset<HD>(lane, db);
 
-  const bf16_t* kseq = a.k + (int64_t)b * a.S * tok + (int64_t)h * HD;
-  const bf16_t* vseq = a.v + (int64_t)b * a.S * tok + (int64_t)h * HD;
-  Staged<HD, kDqThreads> sk, sv;
-  load_rows<HD>(sk, kseq, tok, 0, kv_end - 1, tid);
-  load_rows<HD>(sv, vseq, tok, 0, kv_end - 1, tid);
-  for (int key0 = 0; key0 < kv_end; key0 += kStage) {
-    __syncthreads();  // the previous stage's reads are done
-    store_rows<HD>(ktile, sk, tid);
-    store_rows<HD>(vtile, sv, tid);
-    __syncthreads();
-    if (key0 + kStage < kv_end) {  // the next stage's loads, in flight during this stage's MFMAs
-      load_rows<HD>(sk, kseq, tok, key0 + kStage, kv_end - 1, tid);
-      load_rows<HD>(sv, vseq, tok, key0 + kStage, kv_end - 1, tid);
+  // ---- stage loads: global -> LDS by DMA, 16 bytes per lane, lane-linear within the 1 KB a
+  // wave instruction writes; load p of this wave fills linear chunk (NW p + wave) 64 + lane
+  // of the tile, whose source is the logical chunk that the swizzle puts there.
+  const char* kseq = reinterpret_cast<const char*>(a.k + (int64_t)b * a.S * tok + (int64_t)h * HD);
+  const char* vseq = reinterpret_cast<const char*>(a.v + (int64_t)b * a.S * tok + (int64_t)h * HD);
+  const uint32_t tokb = (uint32_t)(tok * 2);
+  int drow[NDMA], dch[NDMA];
+#pragma unroll
+  for (int p = 0; p < NDMA; ++p) {
+    const int lin = (kDqWaves * p + wave) * 64 + lane;
+    drow[p] = lin / CPR;
+    dch[p] = 16 * ((lin % CPR) ^ L::sw(drow[p]));
+  }
+  auto issue = [&] __device__(int st, int key0) {
+    const int lim = kv_end - 1 - key0;  // rows past the tile's last key repeat it (masked)
+    const char* kb0 = kseq + (int64_t)key0 * tokb;
+    const char* vb0 = vseq + (int64_t)key0 * tokb;
+    const uint32_t lk = lds_addr(kring) + st * TILEB + wave * 1024;
+    const uint32_t lv = lds_addr(vring) + st * TILEB + wave * 1024;
+#pragma unroll
+    for (int p = 0; p < NDMA; ++p) {
+      const uint32_t roff = (uint32_t)min(drow[p], lim) * tokb + dch[p];
+      dma16_sbase(kb0, roff, lk + kDqWaves * p * 1024);
+      dma16_sbase(vb0, roff, lv + kDqWaves * p * 1024);
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int n_st = (kv_end + kStage - 1) / kStage;
+  issue(0, 0);
+  if (n_st > 1) issue(1, kStage);
+  int st = 0;
+  for (int t = 0; t < n_st; ++t, st = (st + 1 == kDqRing ? 0 : st + 1)) {
+    // this wave's loads of stage t have landed (those of stage t + 1 may be in flight), then
+    // a bare barrier: every wave's have, and every wave is done with stage t - 1's buffer,
+    // which stage t + 2 refills
+    if (t + 1 < n_st) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NDMA));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS read moves above the barrier
+    if (t + 2 < n_st) issue(st + 2 >= kDqRing ? st + 2 - kDqRing : st + 2, (t + 2) * kStage);
+    const char* ktile = kring + st * TILEB;
+    const char* vtile = vring + st * TILEB;
+    const int key0 = t * kStage;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int k0 = key0 + 32 * kb;
-      if (k0 >= kv_end) break;  // the same for the whole workgroup
+      if (k0 >= kv_end || k0 > wave_pos1) break;  // no row of the wave sees these keys
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
