@@ -16,8 +16,8 @@
 // B operand of dQ^T += K^T dS^T, whose A operand comes from LDS by transpose reads. The
 // key-stationary kernel uses S = Q K^T instead, so that each lane holds one key's column.
 // Both kernels stage their streamed operand by LDS DMA (global_load_lds): the K/V tiles of
-// the query-stationary kernel in a three-stage ring, the Q/dO blocks of the key-stationary
-// kernel in a two-stage ring. The source address of each lane's 16 bytes is chosen so that
+// the query-stationary kernel in a three-stage ring, the Q/dO blocks (with their lse and D
+// words) of the key-stationary kernel in a four-stage ring. The source address of each lane's 16 bytes is chosen so that
 // the tile lands in LDS already swizzled.
 #include <hip/hip_runtime.h>
 
@@ -30,9 +30,10 @@ namespace {
 constexpr int kDqWaves = 8;                 // query-stationary: 256 query rows per workgroup
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kDqRows = 32 * kDqWaves;
-constexpr int kBwdWaves = 4;                // key-stationary: 128 keys per workgroup
-constexpr int kBwdThreads = 64 * kBwdWaves;
-constexpr int kRowsPerWg = 32 * kBwdWaves;
+constexpr int kKvWaves = 8;                 // key-stationary: 8 waves x 32 keys (two per SIMD)
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKeysPerWg = 32 * kKvWaves;
+constexpr int kKvRing = 4;                  // key-stationary: Q/dO stages in the DMA ring
 constexpr int kStage = 64;                  // query-stationary: keys staged per LDS fill
 constexpr int kKvStage = 32;                // key-stationary: query rows per DMA stage
 constexpr int kDqRing = 3;                  // query-stationary: K/V stages in the DMA ring
@@ -261,26 +262,28 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 }
 
 template <int HD>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv(BwdArgs a) {
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv(BwdArgs a) {
   using L = BLay<HD>;
   constexpr int KS = L::KS, DB = L::DB, ROWB = L::ROWB, CPR = L::CPR;
-  constexpr int STB = kKvStage * ROWB;              // bytes of one staged Q (or dO) block
-  constexpr int NDMA = STB / (kBwdThreads * 16);    // 16-byte DMA loads per thread per block
-  static_assert(NDMA >= 1 && NDMA * kBwdThreads * 16 == STB, "whole block per stage");
-  // Q and dO rings of two 32-row stages, filled by LDS DMA one stage ahead of the MFMAs
-  __shared__ __attribute__((aligned(1024))) char qring[2 * STB];
-  __shared__ __attribute__((aligned(1024))) char oring[2 * STB];
+  constexpr int STB = kKvStage * ROWB;                         // bytes of one staged Q (or dO) block
+  constexpr int CHUNKS = STB / 16;                             // its 16-byte chunks
+  constexpr int NDMA = (CHUNKS + kKvThreads - 1) / kKvThreads;  // DMA loads per thread per block
+  static_assert(CHUNKS % 64 == 0, "whole waves per block");
+  // Q and dO rings of kKvRing 32-row stages, and each stage's lse and D (64 words), filled
+  // by LDS DMA up to kKvRing - 1 stages ahead of the MFMAs
+  __shared__ __attribute__((aligned(1024))) char qring[kKvRing * STB];
+  __shared__ __attribute__((aligned(1024))) char oring[kKvRing * STB];
+  __shared__ __attribute__((aligned(256))) float lsed[kKvRing][2 * kKvStage];
   // V rows of the workgroup's keys: read as B fragments of dP = dO V^T each block (kept in
   // LDS rather than registers, so that two waves fit on a SIMD)
-  __shared__ __attribute__((aligned(16))) char vkeys[kRowsPerWg * ROWB];
-  __shared__ float lse_s[2][kKvStage], d_s[2][kKvStage];
+  __shared__ __attribute__((aligned(16))) char vkeys[kKeysPerWg * ROWB];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n_kt = (int)((a.S + kRowsPerWg - 1) / kRowsPerWg);
+  const int n_kt = (int)((a.S + kKeysPerWg - 1) / kKeysPerWg);
   const int bh = blockIdx.x / n_kt;
   const int kt = (int)(blockIdx.x - bh * n_kt);
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int key0 = kt * kRowsPerWg;
+  const int key0 = kt * kKeysPerWg;
   const int64_t tok = (int64_t)a.H * HD;
 
   const int kw0 = key0 + 32 * wave;  // the wave's first key
@@ -294,13 +297,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   for (int s = 0; s < KS; ++s) kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(a.k + keyoff + 16 * s));
   {
     const bf16_t* vrows = a.v + (int64_t)b * a.S * tok + (int64_t)h * HD;
-    for (int lin = tid; lin < kRowsPerWg * CPR; lin += kBwdThreads) {
+    for (int lin = tid; lin < kKeysPerWg * CPR; lin += kKvThreads) {
       const int r = lin / CPR, c = lin - (lin / CPR) * CPR;
       const int gr = (int)min((int64_t)key0 + r, a.S - 1);
       *reinterpret_cast<uint4*>(vkeys + r * ROWB + 16 * (c ^ L::sw(r))) =
           *reinterpret_cast<const uint4*>(vrows + (int64_t)gr * tok + 8 * c);
     }
   }
+  __syncthreads();  // vkeys complete (the ring below synchronises with bare barriers)
 
   // The rank's local rows ascend in position (chunk r, then chunk 2D-1-r): the rows that see
   // any of this workgroup's keys are the suffix from the first row at position >= key0.
@@ -324,59 +328,56 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // ---- stage loads: global -> LDS by DMA, 16 bytes per lane, lane-linear within the 1 KB a
   // wave instruction writes. Load p of this wave fills linear chunk (NW p + wave) 64 + lane
   // of the block: row lin / CPR at physical chunk lin % CPR, which holds logical chunk
-  // (lin % CPR) ^ sw(row); the source address is chosen accordingly.
+  // (lin % CPR) ^ sw(row); the source address is chosen accordingly. Wave 0 also copies
+  // the stage's 32 lse and 32 D words.
   const char* qseq = reinterpret_cast<const char*>(a.q + (int64_t)b * a.rows * tok + (int64_t)h * HD);
   const char* oseq = reinterpret_cast<const char*>(a.d_o + (int64_t)b * a.rows * tok + (int64_t)h * HD);
   const uint32_t tokb = (uint32_t)(tok * 2);
+  const int64_t lrow = ((int64_t)b * a.H + h) * a.rows;
   int drow[NDMA], dch[NDMA];
+  int per_stage = wave == 0 ? 1 : 0;  // this wave's loads per stage
 #pragma unroll
   for (int p = 0; p < NDMA; ++p) {
-    const int lin = (kBwdWaves * p + wave) * 64 + lane;
+    const int lin = (kKvWaves * p + wave) * 64 + lane;
     drow[p] = lin / CPR;
-    dch[p] = 16 * ((lin % CPR) ^ L::sw(drow[p]));
+    dch[p] = 16 * ((lin % CPR) ^ L::sw(drow[p] % kKvStage));
+    if ((kKvWaves * p + wave) * 64 < CHUNKS) per_stage += 2;
   }
-  auto issue = [&] __device__(int buf, int i) {
-    const int lim = a.rows - 1 - i;  // rows past the last local row repeat it (masked)
-    const char* qb0 = qseq + (int64_t)i * tokb;
-    const char* ob0 = oseq + (int64_t)i * tokb;
-    const uint32_t lq = lds_addr(qring) + buf * STB + wave * 1024;
-    const uint32_t lo = lds_addr(oring) + buf * STB + wave * 1024;
+  auto issue = [&] __device__(int st, int q0) {
+    const int lim = a.rows - 1 - q0;  // rows past the last local row repeat it (masked)
+    const char* qb0 = qseq + (int64_t)q0 * tokb;
+    const char* ob0 = oseq + (int64_t)q0 * tokb;
+    const uint32_t lq = lds_addr(qring) + st * STB + wave * 1024;
+    const uint32_t lo = lds_addr(oring) + st * STB + wave * 1024;
 #pragma unroll
     for (int p = 0; p < NDMA; ++p) {
+      if ((kKvWaves * p + wave) * 64 >= CHUNKS) break;  // the same for the whole wave
       const uint32_t roff = (uint32_t)min(drow[p], lim) * tokb + dch[p];
-      dma16_sbase(qb0, roff, lq + kBwdWaves * p * 1024);
-      dma16_sbase(ob0, roff, lo + kBwdWaves * p * 1024);
+      dma16_sbase(qb0, roff, lq + kKvWaves * p * 1024);
+      dma16_sbase(ob0, roff, lo + kKvWaves * p * 1024);
+    }
+    if (wave == 0) {
+      const int ri = min(q0 + (lane & 31), a.rows - 1);
+      dma4_vaddr((lane < 32 ? a.lse : a.dsum) + lrow + ri, lds_addr(&lsed[st][0]));
     }
   };
-  const int64_t lrow = ((int64_t)b * a.H + h) * a.rows;
-  float lse_n = 0.0f, d_n = 0.0f;  // lse (log2 units) and D of row i + tid of the next stage
-  auto fetch_rows = [&] __device__(int i) {
-    if (tid < kKvStage) {
-      const int ri = min(i + tid, a.rows - 1);
-      lse_n = a.lse[lrow + ri] * kLog2e;
-      d_n = a.dsum[lrow + ri];
-    }
-  };
-  if (i0 < a.rows) {
-    issue(0, i0);
-    fetch_rows(i0);
-  }
-  int buf = 0;
-  for (int q0 = i0; q0 < a.rows; q0 += kKvStage, buf ^= 1) {
-    // this wave's loads of the stage have landed; its lse and D go to LDS; then one barrier:
-    // every wave's loads have landed, and every wave is done with the other buffer
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    if (tid < kKvStage) {
-      lse_s[buf][tid] = lse_n;
-      d_s[buf][tid] = d_n;
-    }
-    __syncthreads();
-    if (q0 + kKvStage < a.rows) {
-      issue(buf ^ 1, q0 + kKvStage);
-      fetch_rows(q0 + kKvStage);
-    }
-    const char* qtile = qring + buf * STB;
-    const char* otile = oring + buf * STB;
+  const int n_st = i0 < a.rows ? (a.rows - i0 + kKvStage - 1) / kKvStage : 0;
+  for (int t = 0; t < kKvRing - 1 && t < n_st; ++t) issue(t, i0 + t * kKvStage);
+  int st = 0;
+  for (int t = 0; t < n_st; ++t, st = (st + 1 == kKvRing ? 0 : st + 1)) {
+    // this wave's loads of stage t have landed (later stages' may be in flight), then a bare
+    // barrier: every wave's have, and every wave is done with stage t - 1's buffers, which
+    // stage t + kKvRing - 1 refills
+    wait_vm(min(kKvRing - 2, n_st - 1 - t) * per_stage);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS read moves above the barrier
+    const int q0 = i0 + t * kKvStage;
+    if (t + kKvRing - 1 < n_st) issue(st == 0 ? kKvRing - 1 : st - 1, q0 + (kKvRing - 1) * kKvStage);
+    const char* qtile = qring + st * STB;
+    const char* otile = oring + st * STB;
+    const float* lse_s = &lsed[st][0];  // natural log
+    const float* d_s = &lsed[st][kKvStage];
     // no row of the block sees the wave's keys (its last row has the highest position)
     if (kw0 > (int)zigzag_pos(min(q0 + kKvStage - 1, a.rows - 1), a.C, a.rank, a.D)) continue;
     f32x16 s = {}, dp = {};
@@ -400,8 +401,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
         const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
         // every operand read and the exponential unconditionally, then a select: a load
         // under the condition would make a branch and a wait per register
-        const float ex = __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[buf][qr]);
-        const float dsub = dp[r] - d_s[buf][qr];
+        const float ex = __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[qr] * kLog2e);
+        const float dsub = dp[r] - d_s[qr];
         if (whole) {
           p[e] = ex;
         } else {
@@ -460,14 +461,14 @@ hipError_t launch_attn_bwd(const void* q, const void* k_full, const void* v_full
   a.H = H;
   a.scale = scale > 0.0f ? scale : 1.0f / sqrtf((float)hd);
   const int n_qt = (a.rows + kDqRows - 1) / kDqRows;
-  const int n_kt = (int)((S + kRowsPerWg - 1) / kRowsPerWg);
+  const int n_kt = (int)((S + kKeysPerWg - 1) / kKeysPerWg);
   const dim3 gq((unsigned)(B * H * n_qt)), gk((unsigned)(B * H * n_kt));
   if (hd == 128) {
     hipLaunchKernelGGL(attn_bwd_dq<128>, gq, dim3(kDqThreads), 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dkdv<128>, gk, dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv<128>, gk, dim3(kKvThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL(attn_bwd_dq<64>, gq, dim3(kDqThreads), 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dkdv<64>, gk, dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv<64>, gk, dim3(kKvThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
