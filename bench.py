@@ -40,9 +40,9 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "TSP rank-shard layer fwd TFLOP/s (% bf16 MFMA peak), 7B layer, S=16K-128K"
 DEFAULT_WORKLOAD = "7b_s128k_d8"
 PKG = os.path.join(ROOT, "long_context_transformer_amd")
-# Sources that determine the attention kernel's code; the counter summary records their hash.
-ATTN_SOURCES = [os.path.join(PKG, "csrc", "tsp_attn.hip"), os.path.join(PKG, "csrc", "tsp_device.h"),
-                os.path.join(PKG, "build.py")]
+# What determines the attention kernel's code: its source, the device header it includes
+# and its compile flags. The counter summary records their hash.
+ATTN_SOURCES = [os.path.join(PKG, "csrc", "tsp_attn.hip"), os.path.join(PKG, "csrc", "tsp_device.h")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_7b_s128k_d8_hbm_traffic.md")
 CALIB_MIB = 256
 
@@ -129,10 +129,15 @@ def calib_copy():
 
 
 def attn_sources_hash():
+    """sha256 of the attention kernel's source, its device header and its hipcc flags (paths
+    relative to the repository, so that the value does not depend on where it is checked out)."""
+    from long_context_transformer_amd import build as tsp_build
     h = hashlib.sha256()
     for p in ATTN_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
+    flags = tsp_build.HIPCC_FLAGS + tsp_build.SOURCE_FLAGS.get("tsp_attn.hip", [])
+    h.update("\0".join(f.replace(tsp_build.ROOT, ".") for f in flags).encode())
     return h.hexdigest()
 
 

@@ -42,6 +42,31 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// The 4-byte form of the LDS DMA copies (global_load_lds_dword): lane i's word lands at
+// `lds` + 4 i (M0 holds `lds`). Like the 16-byte forms it is issued from inline assembly
+// and ordered by explicit s_waitcnt vmcnt and s_barrier.
+__device__ __forceinline__ void dma4_vaddr(const void* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "s"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n known only at run time (s_waitcnt takes an
+// immediate). Counts above 15 wait for 15: a smaller count only waits longer.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define TSP_WAIT_VM_CASE(k)                    \
+  case k:                                      \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(k)); \
+    break;
+    TSP_WAIT_VM_CASE(0) TSP_WAIT_VM_CASE(1) TSP_WAIT_VM_CASE(2) TSP_WAIT_VM_CASE(3)
+    TSP_WAIT_VM_CASE(4) TSP_WAIT_VM_CASE(5) TSP_WAIT_VM_CASE(6) TSP_WAIT_VM_CASE(7)
+    TSP_WAIT_VM_CASE(8) TSP_WAIT_VM_CASE(9) TSP_WAIT_VM_CASE(10) TSP_WAIT_VM_CASE(11)
+    TSP_WAIT_VM_CASE(12) TSP_WAIT_VM_CASE(13) TSP_WAIT_VM_CASE(14)
+#undef TSP_WAIT_VM_CASE
+    default:
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(15));
+  }
+}
+
 template <int HD>
 struct BLay {
   static constexpr int KS = HD / 16;   // 16-dim reduction steps

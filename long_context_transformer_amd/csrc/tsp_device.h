@@ -70,10 +70,6 @@ __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t voff, uin
 __device__ __forceinline__ void dma16_vaddr(const void* addr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds) : "memory");
 }
-// The 4-byte form (global_load_lds_dword): lane i's word lands at `lds` + 4 i.
-__device__ __forceinline__ void dma4_vaddr(const void* addr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "s"(lds) : "memory");
-}
 // LDS byte address of a pointer into a __shared__ array, made wave-uniform.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(
@@ -94,24 +90,6 @@ __device__ __forceinline__ float max_swap32(float v) {
 // s_waitcnt immediate that waits until at most `vm` vector-memory loads of this wave are
 // in flight, leaving the export and LDS counters unconstrained.
 constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-// The same wait for a wave-uniform count known only at run time (s_waitcnt takes an
-// immediate). Counts above 15 wait for 15: a smaller count only waits longer.
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-#define TSP_WAIT_VM_CASE(k) \
-  case k:                   \
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(k)); \
-    break;
-    TSP_WAIT_VM_CASE(0) TSP_WAIT_VM_CASE(1) TSP_WAIT_VM_CASE(2) TSP_WAIT_VM_CASE(3)
-    TSP_WAIT_VM_CASE(4) TSP_WAIT_VM_CASE(5) TSP_WAIT_VM_CASE(6) TSP_WAIT_VM_CASE(7)
-    TSP_WAIT_VM_CASE(8) TSP_WAIT_VM_CASE(9) TSP_WAIT_VM_CASE(10) TSP_WAIT_VM_CASE(11)
-    TSP_WAIT_VM_CASE(12) TSP_WAIT_VM_CASE(13) TSP_WAIT_VM_CASE(14)
-#undef TSP_WAIT_VM_CASE
-    default:
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(15));
-  }
-}
 
 // Global position of local row i of rank r, for chunk length C and fold D.
 // Rows 0..C-1 are chunk r, rows C..2C-1 are the mirror chunk 2D-1-r.
