@@ -11,9 +11,8 @@
 // Local rows ascend in position, so a tile's last row bounds its keys: the workgroup
 // streams keys [0, pos(last)+1) in stages of 64 and never reads a key row after the
 // rank's last position (the final stage repeats that row instead; those keys are masked).
-// Within one (sequence, head) the heaviest tile is dispatched first, and each XCD takes a
-// contiguous range of (sequence, head) work so the tiles running together on it stream
-// the same K/V through its L2.
+// Each XCD takes a contiguous range of (sequence, head) work, so the tiles running together
+// on it stream the same K/V through its L2, and runs it longest tile first across its heads.
 //
 // Data movement. K and V stages go straight from global memory into LDS with 16-byte
 // global_load_lds (no register staging), into a 4-deep ring of separate LDS buffers, two
@@ -109,6 +108,7 @@ struct AttnArgs {
   int items;  // B * Hrun * n_qt
   int h0, Hrun;  // heads [h0, h0 + Hrun) of the H in the layout
   int strided;   // 1: item = block index (consecutive items on different XCDs)
+  int lpt;       // 1: longest tile first across an XCD's heads (set at launch)
   float scale_log2;
 };
 
@@ -159,8 +159,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       lse32 += half * a.part_l;
     }
   }
-  const int bh = item / a.n_qt;
-  const int qt = a.n_qt - 1 - (item - bh * a.n_qt);  // heaviest tile of the (b, h) first
+  // Item -> (sequence-head, query tile). A tile's work grows with its index (its last
+  // position bounds its keys). Each (sequence, head) runs its heaviest tile first. With few
+  // tiles per CU (lpt), an XCD's items instead go longest first across all its heads: the
+  // k-th heaviest tile of each head before any head's (k+1)-th, so the CUs that finish a
+  // heavy tile take the light ones; head-by-head order can give one CU two heavy tiles.
+  int bh, qt;
+  if (a.lpt) {
+    const int per_xcd = a.items / kNumXcd;
+    const int nbh_x = per_xcd / a.n_qt;
+    const int x = item / per_xcd;
+    const int L = item - x * per_xcd;
+    const int k = L / nbh_x;
+    bh = x * nbh_x + (L - k * nbh_x);
+    qt = a.n_qt - 1 - k;
+  } else {
+    bh = item / a.n_qt;
+    qt = a.n_qt - 1 - (item - bh * a.n_qt);
+  }
   const int b = bh / a.Hrun, h = a.h0 + bh - (bh / a.Hrun) * a.Hrun;
   const int row0 = qt * BR;
   int kv_end = (int)zigzag_pos(min(row0 + BR, a.rows) - 1, a.C, a.rank, a.D) + 1;
@@ -625,6 +641,7 @@ AttnArgs base_args(const void* q, const void* k_full, const void* v_full, int B,
   a.h0 = 0;
   a.Hrun = H;
   a.strided = 0;
+  a.lpt = 0;
   a.items = B * H * a.n_qt;
   a.key_lo = 0;
   a.key_hi = (int)S;
@@ -648,8 +665,17 @@ bool set_heads(AttnArgs& a, int B, int h0, int h_run) {
   return true;
 }
 
+// Longest-first order across an XCD's heads pays when there are few tiles per CU (at 7B
+// S=32K, two per CU: rank-to-rank spread of attention time 1.21x -> 1.01x). With many,
+// head-by-head order already balances and keeps each head's K/V in the XCD's L2 (7B B=4
+// S=64K, 16 per CU: 10% faster than longest first). Requires whole (sequence, head) ranges
+// per XCD and one item per tile.
+constexpr int kLptMaxItems = 4 * 256;
+
 template <bool PART>
-hipError_t launch(const AttnArgs& a, int hd, hipStream_t stream) {
+hipError_t launch(const AttnArgs& a_in, int hd, hipStream_t stream) {
+  AttnArgs a = a_in;
+  a.lpt = !a.strided && a.split == 0 && a.items <= kLptMaxItems && a.items % (kNumXcd * a.n_qt) == 0;
   if (hd == 128) {
     hipLaunchKernelGGL((attn_fwd<128, PART>), dim3(a.items), dim3(kThreads), 0, stream, a);
   } else {
