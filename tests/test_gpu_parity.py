@@ -69,6 +69,9 @@ ATTN_CASES = [  # B, S, D, rank, H, hd
     (2, 4096, 2, 1, 2, 128),    # C = 1024: many full stages
     (1, 640, 1, 0, 2, 128),     # D = 1: plain causal attention
     (1, 96, 3, 2, 1, 64),       # C = 16, one tile holding both chunks
+    # B*H a multiple of the 8 XCDs and few tiles: longest tile first across an XCD's heads
+    (1, 2048, 2, 1, 8, 64),     # 4 tiles per head
+    (2, 1536, 3, 2, 4, 128),    # two sequences, 2 tiles per head
 ]
 
 
