@@ -348,9 +348,19 @@ int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const void* w
   if (int rc = hip_status(tsp::launch_qkv(x_shard, w_qkv, q, k_full, v_full, B, S, D, r, d, s), "qkv launch"))
     return rc;
   if (int rc = mark(1)) return rc;
-  if (int rc = hip_status(tsp::launch_attn(q, k_full, v_full, o, nullptr, B, S, D, r, H, hd, desc->scale, s),
-                          "attention launch"))
-    return rc;
+  // With at most one tile per CU the attention time is that of the heaviest tile: the later
+  // chunk's tiles are then split in two key halves, whose fp32 partials use the MLP hidden
+  // buffer (not yet written at this point) when it is large enough.
+  if (tsp::attn_two_part_split(B, S, D, r, H) > 0 &&
+      tsp::attn_two_part_bytes(B, S, D, H, hd) <= c.total - c.h_off) {
+    if (int rc = hip_status(tsp::launch_attn_two_part(q, k_full, v_full, o, hbuf, B, S, D, r, H, hd, desc->scale, s),
+                            "attention launch"))
+      return rc;
+  } else {
+    if (int rc = hip_status(tsp::launch_attn(q, k_full, v_full, o, nullptr, B, S, D, r, H, hd, desc->scale, s),
+                            "attention launch"))
+      return rc;
+  }
   if (int rc = mark(2)) return rc;
   if (int rc = hip_status(tsp::launch_proj_bf16(o, d, w_o, d, attn_out, d, M, d, d, s), "W_O launch")) return rc;
   if (int rc = mark(3)) return rc;

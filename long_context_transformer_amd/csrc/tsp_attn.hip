@@ -105,7 +105,10 @@ struct AttnArgs {
   int rows;  // 2C local rows per sequence
   int D, rank, H;
   int n_qt;   // query tiles per (sequence, head)
-  int items;  // B * Hrun * n_qt
+  int qt_lo, qt_hi;  // tiles [qt_lo, qt_hi) of each (sequence, head) run (0, n_qt: all)
+  int items;  // B * Hrun * (qt_hi - qt_lo), twice that for a split launch
+  // Key-range attention: o32 and lse hold local rows [prow0, prow0 + prows) of each sequence.
+  int prow0, prows;
   int h0, Hrun;  // heads [h0, h0 + Hrun) of the H in the layout
   int strided;   // 1: item = block index (consecutive items on different XCDs)
   int lpt;       // 1: longest tile first across an XCD's heads (set at launch)
@@ -165,17 +168,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   // k-th heaviest tile of each head before any head's (k+1)-th, so the CUs that finish a
   // heavy tile take the light ones; head-by-head order can give one CU two heavy tiles.
   int bh, qt;
+  const int n_run = a.qt_hi - a.qt_lo;
   if (a.lpt) {
     const int per_xcd = a.items / kNumXcd;
-    const int nbh_x = per_xcd / a.n_qt;
+    const int nbh_x = per_xcd / n_run;
     const int x = item / per_xcd;
     const int L = item - x * per_xcd;
     const int k = L / nbh_x;
     bh = x * nbh_x + (L - k * nbh_x);
-    qt = a.n_qt - 1 - k;
+    qt = a.qt_hi - 1 - k;
   } else {
-    bh = item / a.n_qt;
-    qt = a.n_qt - 1 - (item - bh * a.n_qt);
+    bh = item / n_run;
+    qt = a.qt_hi - 1 - (item - bh * n_run);
   }
   const int b = bh / a.Hrun, h = a.h0 + bh - (bh / a.Hrun) * a.Hrun;
   const int row0 = qt * BR;
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       for (int qb = 0; qb < QB; ++qb) {
         if (qi[qb] >= a.rows) continue;
         const int64_t ro = ((int64_t)b * a.rows + qi[qb]) * tok + (int64_t)h * HD;
-        float* op = o32 + ((int64_t)b * a.rows + qi[qb]) * otok + (int64_t)oh * HD;
+        float* op = o32 + ((int64_t)b * a.prows + (qi[qb] - a.prow0)) * otok + (int64_t)oh * HD;
 #pragma unroll
         for (int db = 0; db < HD / 32; ++db)
 #pragma unroll
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
               if (a.o != nullptr) *reinterpret_cast<uint2*>(a.o + ro + dim) = make_uint2(0u, 0u);
             }
           }
-        if (!a.accumulate && hl == 0) lse32[((int64_t)b * a.oH + oh) * a.rows + qi[qb]] = -INFINITY;
+        if (!a.accumulate && hl == 0) lse32[((int64_t)b * a.oH + oh) * a.prows + (qi[qb] - a.prow0)] = -INFINITY;
       }
       return;
     }
@@ -561,8 +565,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     for (int qb = 0; qb < QB; ++qb) {
       if (qi[qb] >= a.rows) continue;
       const int64_t ro = ((int64_t)b * a.rows + qi[qb]) * tok + (int64_t)h * HD;
-      float* op = o32 + ((int64_t)b * a.rows + qi[qb]) * otok + (int64_t)oh * HD;
-      float* lp = lse32 + ((int64_t)b * a.oH + oh) * a.rows + qi[qb];
+      float* op = o32 + ((int64_t)b * a.prows + (qi[qb] - a.prow0)) * otok + (int64_t)oh * HD;
+      float* lp = lse32 + ((int64_t)b * a.oH + oh) * a.prows + (qi[qb] - a.prow0);
       const float lse_b = l_run[qb] > 0.0f ? (m_s[qb] + __log2f(l_run[qb])) * 0.69314718055994531f : -INFINITY;
       // Overwrite: weights (0, 1). Accumulate: the log-sum-exp merge with what the
       // accumulator holds (both lanes of the row read it before lane hl == 0 writes).
@@ -638,6 +642,10 @@ AttnArgs base_args(const void* q, const void* k_full, const void* v_full, int B,
   a.rank = rank;
   a.H = H;
   a.n_qt = (a.rows + BR - 1) / BR;
+  a.qt_lo = 0;
+  a.qt_hi = a.n_qt;
+  a.prow0 = 0;
+  a.prows = a.rows;
   a.h0 = 0;
   a.Hrun = H;
   a.strided = 0;
@@ -661,7 +669,7 @@ bool set_heads(AttnArgs& a, int B, int h0, int h_run) {
   if (h0 < 0 || h_run <= 0 || h0 + h_run > a.H) return false;
   a.h0 = h0;
   a.Hrun = h_run;
-  a.items = B * h_run * a.n_qt;
+  a.items = B * h_run * (a.qt_hi - a.qt_lo);
   return true;
 }
 
@@ -675,7 +683,7 @@ constexpr int kLptMaxItems = 4 * 256;
 template <bool PART>
 hipError_t launch(const AttnArgs& a_in, int hd, hipStream_t stream) {
   AttnArgs a = a_in;
-  a.lpt = !a.strided && a.split == 0 && a.items <= kLptMaxItems && a.items % (kNumXcd * a.n_qt) == 0;
+  a.lpt = !a.strided && a.split == 0 && a.items <= kLptMaxItems && a.items % (kNumXcd * (a.qt_hi - a.qt_lo)) == 0;
   if (hd == 128) {
     hipLaunchKernelGGL((attn_fwd<128, PART>), dim3(a.items), dim3(kThreads), 0, stream, a);
   } else {
@@ -774,7 +782,7 @@ __global__ __launch_bounds__(256) void attn_merge(float* o_acc, float* lse_acc, 
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_halves(const float* o32, const float* lse, int64_t part_o,
                                                          int64_t part_l, bf16_t* o_out, int64_t units, int rows,
-                                                         int h_run, int H, int h0) {
+                                                         int h_run, int H, int h0, int out_rows, int out_row0) {
   constexpr int PER = HD / 64;
   const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * rows + row) * h_run + h
   if (u >= units) return;
@@ -790,25 +798,89 @@ __global__ __launch_bounds__(256) void attn_merge_halves(const float* o32, const
   const float wa = ea / (ea + eb), wb = eb / (ea + eb);
   const float* pa = o32 + u * HD + lane * PER;
   const float* pb = o32 + part_o + u * HD + lane * PER;
-  bf16_t* po = o_out + (br * H + h0 + h) * HD + lane * PER;
+  // row `row` of the partials is local row out_row0 + row of O ([B, out_rows, H, HD])
+  bf16_t* po = o_out + ((b * out_rows + out_row0 + row) * H + h0 + h) * HD + lane * PER;
 #pragma unroll
   for (int e = 0; e < PER; ++e) po[e] = to_bf16(wa * pa[e] + wb * pb[e]);
 }
 
-hipError_t launch_attn_merge_halves(const float* o32, const float* lse, void* o_out, int B, int rows, int H, int hd,
-                                    int h0, int h_run, hipStream_t stream) {
-  if (h0 < 0 || h_run <= 0 || h0 + h_run > H) return hipErrorInvalidValue;
+namespace {
+hipError_t merge_halves_rows(const float* o32, const float* lse, void* o_out, int B, int rows, int H, int hd, int h0,
+                             int h_run, int out_rows, int out_row0, hipStream_t stream) {
+  if (h0 < 0 || h_run <= 0 || h0 + h_run > H || out_row0 < 0 || out_row0 + rows > out_rows)
+    return hipErrorInvalidValue;
   const int64_t units = (int64_t)B * rows * h_run;
   const int64_t part_o = units * hd, part_l = units;
   const dim3 grid((unsigned)((units + 3) / 4));
   if (hd == 128) {
     hipLaunchKernelGGL(attn_merge_halves<128>, grid, dim3(256), 0, stream, o32, lse, part_o, part_l,
-                       static_cast<bf16_t*>(o_out), units, rows, h_run, H, h0);
+                       static_cast<bf16_t*>(o_out), units, rows, h_run, H, h0, out_rows, out_row0);
   } else {
     hipLaunchKernelGGL(attn_merge_halves<64>, grid, dim3(256), 0, stream, o32, lse, part_o, part_l,
-                       static_cast<bf16_t*>(o_out), units, rows, h_run, H, h0);
+                       static_cast<bf16_t*>(o_out), units, rows, h_run, H, h0, out_rows, out_row0);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attn_merge_halves(const float* o32, const float* lse, void* o_out, int B, int rows, int H, int hd,
+                                    int h0, int h_run, hipStream_t stream) {
+  return merge_halves_rows(o32, lse, o_out, B, rows, H, hd, h0, h_run, rows, 0, stream);
+}
+
+// Two-part attention for launches of at most one round of tiles (one per CU): the time is
+// then that of the heaviest tile, and the later zigzag chunk's tiles see up to (2D - r) C
+// keys against at most (r + 1) C for the earlier chunk's. The earlier chunk's tiles run as
+// they are (bf16 O); each later-chunk tile runs as two items, keys [0, split) and
+// [split, end), with split at half of that chunk's key span, into fp32 partials of the later
+// chunk's rows only, merged by log-sum-exp into bf16 O. Every later-chunk row lies at or after
+// split, so both halves see keys. Applies when chunks hold whole tiles and the later chunk's
+// span is at least twice the earlier one's (r <= (2D - 2) / 3).
+constexpr int kCus = 256;
+
+int attn_two_part_split(int B, int64_t S, int D, int rank, int H) {
+  const int64_t C = S / (2 * D);
+  if (C <= 0 || C % BR != 0) return 0;
+  const int64_t n_qt = 2 * C / BR;
+  if ((int64_t)B * H * n_qt > kCus) return 0;
+  if (3 * (int64_t)rank > 2 * (int64_t)D - 2) return 0;
+  const int64_t split = ((2 * (int64_t)D - rank) * C / 2) / BC * BC;
+  if (split <= 0 || split > (2 * (int64_t)D - 1 - rank) * C) return 0;
+  return (int)split;
+}
+
+size_t attn_two_part_bytes(int B, int64_t S, int D, int H, int hd) {
+  const size_t C = (size_t)(S / (2 * D));
+  return 2 * (size_t)B * C * (size_t)H * ((size_t)hd + 1) * sizeof(float);
+}
+
+hipError_t launch_attn_two_part(const void* q, const void* k_full, const void* v_full, void* o, void* part, int B,
+                                int64_t S, int D, int rank, int H, int hd, float scale, hipStream_t stream) {
+  const int split = attn_two_part_split(B, S, D, rank, H);
+  if (split <= 0) return hipErrorInvalidValue;
+  AttnArgs e = base_args(q, k_full, v_full, B, S, D, rank, H, hd, scale);
+  const int c_tiles = (int)(e.C / BR);
+  // earlier chunk: tiles [0, C / BR), bf16 O
+  e.o = static_cast<bf16_t*>(o);
+  e.qt_hi = c_tiles;
+  e.items = B * H * c_tiles;
+  if (hipError_t err = launch<false>(e, hd, stream)) return err;
+  // later chunk: tiles [C / BR, 2C / BR), two key halves each, partials of rows [C, 2C)
+  AttnArgs l = base_args(q, k_full, v_full, B, S, D, rank, H, hd, scale);
+  const int64_t units = (int64_t)B * l.C * H;
+  float* o32 = static_cast<float*>(part);
+  l.o32 = o32;
+  l.lse = o32 + 2 * units * hd;
+  l.qt_lo = c_tiles;
+  l.prow0 = (int)l.C;
+  l.prows = (int)l.C;
+  l.split = split;
+  l.part_o = units * hd;
+  l.part_l = units;
+  l.items = 2 * B * H * (l.n_qt - c_tiles);
+  l.strided = 1;
+  if (hipError_t err = launch<true>(l, hd, stream)) return err;
+  return merge_halves_rows(o32, l.lse, o, B, (int)l.C, H, hd, 0, H, l.rows, (int)l.C, stream);
 }
 
 hipError_t launch_attn_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part, void* o_out,
