@@ -66,9 +66,29 @@ __device__ __forceinline__ uint4 load_chunk(const bf16_t* base, int64_t ld, int 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 // ---------------------------------------------------------------------------- epilogues
+// Epilogues with bf16 output (kWide) also take 8 columns at once, already packed (see the
+// lane exchange in gemm_fast): one 16-byte store per lane where the row allows it.
+__device__ __forceinline__ bf16_t bf16_at(const uint4& w, int e) {
+  const uint32_t word = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+  return (bf16_t)(word >> (16 * (e & 1)));
+}
+__device__ __forceinline__ void store8_bf16(bf16_t* p, const uint4& w, int valid) {
+  if (valid >= 8 && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+    *reinterpret_cast<uint4*>(p) = w;
+  } else {
+    for (int e = 0; e < 8 && e < valid; ++e) p[e] = bf16_at(w, e);
+  }
+}
+
 struct EpiBf16 {
+  static constexpr bool kWide = true;
   bf16_t* c;
   int64_t ldc;
+  __device__ __forceinline__ static uint2 pack(const f32x4& v) { return pack_bf16x4(v[0], v[1], v[2], v[3]); }
+  __device__ __forceinline__ void store8(int m, int n, const uint4& w, int M, int N) const {
+    if (m >= M || n >= N) return;
+    store8_bf16(c + (int64_t)m * ldc + n, w, N - n);
+  }
   __device__ __forceinline__ void operator()(int m, int n, const f32x4& v, int M, int N) const {
     if (m >= M || n >= N) return;
     bf16_t* p = c + (int64_t)m * ldc + n;
@@ -81,6 +101,7 @@ struct EpiBf16 {
 };
 
 struct EpiQKV {
+  static constexpr bool kWide = true;
   bf16_t* q;  // may be null
   bf16_t* k;
   bf16_t* v;
@@ -106,13 +127,36 @@ struct EpiQKV {
     bf16_t* dst = (which == 1 ? k : v) + row * d + col;
     *reinterpret_cast<uint2*>(dst) = packed;
   }
+  __device__ __forceinline__ static uint2 pack(const f32x4& v) { return pack_bf16x4(v[0], v[1], v[2], v[3]); }
+  // 8 columns never straddle Q/K/V: dg and n are multiples of 8.
+  __device__ __forceinline__ void store8(int m, int n, const uint4& w, int M, int N) const {
+    if (m >= M || n >= N) return;
+    const int which = n / dg;
+    const int col = col0 + n - which * dg;
+    if (which == 0) {
+      if (q) store8_bf16(q + (int64_t)m * d + col, w, N - n);
+      return;
+    }
+    const int b = m / R;
+    const int i = m - b * R;
+    const int64_t row = (int64_t)b * S + zigzag_pos(i, C, rank, D);
+    store8_bf16((which == 1 ? k : v) + row * d + col, w, N - n);
+  }
 };
 
 struct EpiSwiGLU {
+  static constexpr bool kWide = true;
   bf16_t* h;
   int64_t ldh;
   __device__ __forceinline__ void shift_cols(int64_t c) { h += c; }
   __device__ __forceinline__ static float silu(float g) { return g / (1.0f + __expf(-g)); }
+  __device__ __forceinline__ static uint2 pack(const f32x4& g, const f32x4& u) {
+    return pack_bf16x4(silu(g[0]) * u[0], silu(g[1]) * u[1], silu(g[2]) * u[2], silu(g[3]) * u[3]);
+  }
+  __device__ __forceinline__ void store8(int m, int n, const uint4& w, int M, int N) const {
+    if (m >= M || n >= N) return;
+    store8_bf16(h + (int64_t)m * ldh + n, w, N - n);
+  }
   __device__ __forceinline__ void operator()(int m, int n, const f32x4& g, const f32x4& u, int M,
                                              int N) const {
     if (m >= M || n >= N) return;
@@ -131,6 +175,7 @@ struct EpiSwiGLU {
 // fp32 accumulator plus this partial, stored as bf16 (the last step of an fp32
 // accumulation; first: the partial alone).
 struct EpiAccBf16 {
+  static constexpr bool kWide = false;
   const float* acc;
   bf16_t* out;
   int64_t ld;
@@ -144,6 +189,7 @@ struct EpiAccBf16 {
 };
 
 struct EpiAcc {
+  static constexpr bool kWide = false;
   float* c;
   int64_t ldc;
   int accumulate;
@@ -525,22 +571,57 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
     }
   }
 
+  if constexpr (Epi::kWide) {
+    // bf16 output: lane (row, hl) holds columns 8g + 4hl .. +3 of each 8-column block g of a
+    // 32-column tile. The two half-waves swap halves so that lane hl holds whole blocks hl and
+    // hl + 2, then store 16 bytes per lane (each row gets 32 contiguous bytes per store).
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-    const int m = m0 + wm * WM + mi * 32 + l32;
+    for (int mi = 0; mi < MI; ++mi) {
+      const int m = m0 + wm * WM + mi * 32 + l32;
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
+      for (int ni = 0; ni < NI; ++ni) {
+        uint2 pk[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN + ni * 32 + 8 * g + 4 * hl;
-        const f32x4 v0 = {acc[0][mi][ni][4 * g], acc[0][mi][ni][4 * g + 1], acc[0][mi][ni][4 * g + 2],
-                          acc[0][mi][ni][4 * g + 3]};
-        if constexpr (DUAL) {
-          const f32x4 v1 = {acc[1][mi][ni][4 * g], acc[1][mi][ni][4 * g + 1], acc[1][mi][ni][4 * g + 2],
-                            acc[1][mi][ni][4 * g + 3]};
-          epi(m, n, v0, v1, op.M, op.N);
-        } else {
-          epi(m, n, v0, op.M, op.N);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v0 = {acc[0][mi][ni][4 * g], acc[0][mi][ni][4 * g + 1], acc[0][mi][ni][4 * g + 2],
+                            acc[0][mi][ni][4 * g + 3]};
+          if constexpr (DUAL) {
+            const f32x4 v1 = {acc[1][mi][ni][4 * g], acc[1][mi][ni][4 * g + 1], acc[1][mi][ni][4 * g + 2],
+                              acc[1][mi][ni][4 * g + 3]};
+            pk[g] = Epi::pack(v0, v1);
+          } else {
+            pk[g] = Epi::pack(v0);
+          }
+        }
+        const uint2 s0 = hl ? pk[0] : pk[1];
+        const uint2 s1 = hl ? pk[2] : pk[3];
+        const uint2 r0 = make_uint2(__shfl_xor(s0.x, 32), __shfl_xor(s0.y, 32));
+        const uint2 r1 = make_uint2(__shfl_xor(s1.x, 32), __shfl_xor(s1.y, 32));
+        const uint4 b0 = hl ? make_uint4(r0.x, r0.y, pk[1].x, pk[1].y) : make_uint4(pk[0].x, pk[0].y, r0.x, r0.y);
+        const uint4 b1 = hl ? make_uint4(r1.x, r1.y, pk[3].x, pk[3].y) : make_uint4(pk[2].x, pk[2].y, r1.x, r1.y);
+        const int nt = n0 + wn * WN + ni * 32;
+        epi.store8(m, nt + 8 * hl, b0, op.M, op.N);
+        epi.store8(m, nt + 16 + 8 * hl, b1, op.M, op.N);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int m = m0 + wm * WM + mi * 32 + l32;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN + ni * 32 + 8 * g + 4 * hl;
+          const f32x4 v0 = {acc[0][mi][ni][4 * g], acc[0][mi][ni][4 * g + 1], acc[0][mi][ni][4 * g + 2],
+                            acc[0][mi][ni][4 * g + 3]};
+          if constexpr (DUAL) {
+            const f32x4 v1 = {acc[1][mi][ni][4 * g], acc[1][mi][ni][4 * g + 1], acc[1][mi][ni][4 * g + 2],
+                              acc[1][mi][ni][4 * g + 3]};
+            epi(m, n, v0, v1, op.M, op.N);
+          } else {
+            epi(m, n, v0, op.M, op.N);
+          }
         }
       }
     }
