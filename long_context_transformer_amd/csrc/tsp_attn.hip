@@ -712,6 +712,15 @@ hipError_t launch_attn_range(const void* q, const void* k_full, const void* v_fu
   a.lse = lse;
   a.key_lo = (int)key_lo;
   a.key_hi = (int)key_hi;
+  if (accumulate && o_out == nullptr) {
+    // Merging into the accumulator only: tiles whose rows all precede key_lo add nothing and
+    // write nothing. Positions ascend with the local row, so those are the first tiles.
+    int qt = 0;
+    while (qt < a.n_qt && zigzag_pos(min((qt + 1) * BR, a.rows) - 1, a.C, a.rank, a.D) < key_lo) ++qt;
+    if (qt == a.n_qt || key_lo >= key_hi) return hipSuccess;
+    a.qt_lo = qt;
+    a.items = B * H * (a.n_qt - qt);
+  }
   return launch<true>(a, hd, stream);
 }
 
