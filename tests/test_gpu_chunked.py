@@ -126,6 +126,38 @@ def test_merge_parity():
     check_close("merged bf16 O", host_f64(out), ref_o)
 
 
+def test_range_accumulate_leaves_earlier_rows():
+    """Merging one key range into the accumulator: rows whose position precedes the range are
+    left bit-for-bit as they were (whole query tiles of them are not launched at all), and the
+    other rows equal the oracle's log-sum-exp merge of the accumulator with the range."""
+    B, S, D, r, H, hd = 1, 4096, 2, 1, 2, 128  # C = 1024, 8 query tiles of 256 rows
+    R = S // D
+    q, k, v = qkv_inputs(B, S, D, H, hd, 977)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    idx = O.zigzag_index(S, D, r)
+    qf, kf, vf = synth.to_f64(q), synth.to_f64(k), synth.to_f64(v)
+    rng = np.random.default_rng(43)
+    oa = rng.standard_normal((B, R, H, hd)).astype(np.float32)
+    la = (rng.standard_normal((B, H, R)) * 3).astype(np.float32)
+    d = lambda x: torch.from_numpy(x).cuda()
+    # (first key past four whole tiles and inside the fifth, a single key, the last position
+    # only, a range that starts inside the second tile)
+    for lo, hi in [(2100, 3000), (2048, 2049), (3071, 4096), (1500, 2600)]:
+        print(f"accumulate range [{lo},{hi})", flush=True)
+        acc_o, acc_l = d(oa.copy()), d(la.copy())
+        tsp.attn_fwd_range(qd, kd, vd, acc_o, acc_l, B, S, D, r, H, hd, lo, hi, accumulate=True)
+        torch.cuda.synchronize()
+        got_o, got_l = acc_o.cpu().numpy(), acc_l.cpu().numpy()
+        before = idx < lo
+        assert np.array_equal(got_o[:, before], oa[:, before]), f"[{lo},{hi}): O of earlier rows changed"
+        assert np.array_equal(got_l[:, :, before], la[:, :, before]), f"[{lo},{hi}): lse of earlier rows changed"
+        part_o, part_l = O.attention_range(qf, idx, kf, vf, lo, hi)
+        ref_o, ref_l = O.lse_merge(oa, la, part_o, part_l)
+        after = ~before
+        check_lse(f"[{lo},{hi}) merged lse", got_l[:, :, after], ref_l[:, :, after])
+        check_close(f"[{lo},{hi}) merged O", got_o[:, after].astype(np.float64), ref_o[:, after])
+
+
 PIPE_CASES = [  # B, S, D, rank, H, hd
     (1, 256, 4, 2, 4, 64),
     (2, 2048, 4, 0, 2, 128),
