@@ -6,13 +6,15 @@
 // (chunk r with its mirror 2D-1-r) balances the causal work between ranks. This kernel
 // is that step for one rank: online softmax in fp32, S x S never materialised.
 //
-// Work decomposition. One workgroup (4 waves, one per SIMD) owns 256 consecutive local
-// query rows of one (sequence, head); each wave owns 64 of them as two 32-row blocks.
-// Local rows ascend in position, so a tile's last row bounds its keys: the workgroup
-// streams keys [0, pos(last)+1) in stages of 64 and never reads a key row after the
-// rank's last position (the final stage repeats that row instead; those keys are masked).
-// Each XCD takes a contiguous range of (sequence, head) work, so the tiles running together
-// on it stream the same K/V through its L2, and runs it longest tile first across its heads.
+// Work decomposition. One workgroup of 8 waves (two per SIMD) owns 256 consecutive local
+// query rows of one (sequence, head); each wave owns one 32-row block of them (a build
+// option gives 4 waves of two blocks each). Local rows ascend in position, so a tile's
+// last row bounds its keys: the workgroup streams keys [0, pos(last)+1) in stages of 64
+// and never reads a key row after the rank's last position (the final stage repeats that
+// row instead; those keys are masked). Each XCD takes a contiguous range of (sequence,
+// head) work, so the tiles running together on it stream the same K/V through its L2; it
+// runs each head's heaviest tile first, or, with at most 4 tiles per CU, the longest tiles
+// first across all its heads.
 //
 // Data movement. K and V stages go straight from global memory into LDS with 16-byte
 // global_load_lds (no register staging), into a 4-deep ring of separate LDS buffers, two
@@ -34,16 +36,17 @@
 //   O^T += V^T P^T  B = P straight from the S^T registers (bf16); A = V^T via transpose
 //                   reads with the same key labelling. O^T keeps each lane on its own
 //                   query, so the online-softmax rescale is a per-lane scalar.
-// Each K and V fragment feeds both 32-row query blocks.
+// With two query blocks per wave, each K and V fragment feeds both.
 //
 // Pipeline inside a wave, per 32-key block j: the S MFMAs of block j+1 are issued as one
 // block at raised wave priority, then the softmax of block j, the rare O rescale and the
 // PV MFMAs of block j. With two waves per SIMD, the S MFMAs of one wave run on the matrix
 // core while the other wave computes exponentials on the VALU.
-// Softmax in base 2 with the scale folded into one FMA: p = exp2(s*c - m), c =
-// scale*log2(e), m a running max of s*c. O is rescaled only when the running max grows by
-// more than 8 (p <= 2^8 stays exact in fp32 and bf16); the row sum adds the bf16-rounded
-// p with v_dot2, so numerator and denominator use the same p.
+// Softmax in base 2: p = exp2(s*c - m), c = scale*log2(e), m a running max of s*c. Q is
+// pre-multiplied by c and every S MFMA chain starts from -m, so the MFMAs produce s*c - m
+// and no FMA per score is needed. O is rescaled only when the running max grows by more
+// than 8 (p <= 2^8 stays exact in fp32 and bf16); the row sum adds the bf16-rounded p with
+// v_dot2, so numerator and denominator use the same p.
 #include <math.h>
 
 #include "tsp_device.h"
