@@ -10,16 +10,21 @@
 //   EpiSwiGLU   two weights at once (W1, W3); stores silu(G) * U as bf16
 //   EpiAcc      fp32 accumulator, overwrite or add (the down projection of a shard)
 //
-// Tiling: 256 threads = 4 waves in a 2 x 2 grid over a BM x BN output tile; each wave
-// owns a (BM/2) x (BN/2) block made of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16).
-// K advances in stages of 64 through a double-buffered LDS tile: while the MFMAs run
-// on stage k, the global loads of stage k+1 are in flight in registers, then written to
-// the other LDS buffer; one barrier per stage. In LDS each operand row holds 64 bf16 as
-// eight 16-byte chunks stored at position chunk ^ ((row / 2) % 8), so the 16-byte
-// fragment reads of 16 consecutive rows at one chunk hit 16 distinct bank groups.
-// The MFMA takes the weight tile as its A operand and the activation tile as B, so the
-// 32 x 32 result gives each lane four consecutive output columns of one row: 8-byte
-// bf16 stores or 16-byte fp32 read-modify-writes in the epilogue.
+// Two kernels share the epilogues. gemm_fast (below, "fast path") serves every operand
+// that takes 16-byte chunks, i.e. every layer shape but the tiny one's odd shard width;
+// gemm_nt, register-staged, serves the rest:
+// Tiling of gemm_nt: 256 threads = 4 waves in a 2 x 2 grid over a BM x BN output tile;
+// each wave owns a (BM/2) x (BN/2) block made of 32 x 32 MFMA tiles
+// (v_mfma_f32_32x32x16_bf16). K advances in stages of 64 through a double-buffered LDS
+// tile: while the MFMAs run on stage k, the global loads of stage k+1 are in flight in
+// registers, then written to the other LDS buffer; one barrier per stage. In LDS each
+// operand row holds 64 bf16 as eight 16-byte chunks stored at position
+// chunk ^ ((row / 2) % 8), so the 16-byte fragment reads of 16 consecutive rows at one
+// chunk hit 16 distinct bank groups.
+// Both kernels take the weight tile as the MFMA's A operand and the activation tile as B,
+// so the 32 x 32 result gives each lane four consecutive output columns of one row
+// (8-byte bf16 or 16-byte fp32 stores; gemm_fast pairs the half-waves for 16-byte bf16
+// stores).
 // Workgroup -> tile: XCD-contiguous ranges (xcd_remap), then groups of 8 row-tiles
 // walked column-major so tiles running together on one XCD share A and B in its L2.
 #include "tsp_device.h"
