@@ -11,7 +11,9 @@
 // option gives 4 waves of two blocks each). Local rows ascend in position, so a tile's
 // last row bounds its keys: the workgroup streams keys [0, pos(last)+1) in stages of 64
 // and never reads a key row after the rank's last position (the final stage repeats that
-// row instead; those keys are masked). Each XCD takes a contiguous range of (sequence,
+// row instead; those keys are masked). A key-range launch reads only rows of its range:
+// its first stage starts at the range's first key rounded down to 64, and the rows before
+// that key repeat it (masked). Each XCD takes a contiguous range of (sequence,
 // head) work, so the tiles running together on it stream the same K/V through its L2; it
 // runs each head's heaviest tile first, or, with at most 4 tiles per CU, the longest tiles
 // first across all its heads.
@@ -271,13 +273,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   auto issue = [&] __device__(int st, int t) {
     const int key0 = k_base + t * BC;
     const int lim = kv_end - 1 - key0;  // rows past the tile's last key repeat it (masked)
+    // In a key range, rows of the first stage before key_lo repeat row key_lo (masked), so
+    // no row outside [key_lo, kv_end) is addressed: K/V rows of chunks that have not arrived
+    // may hold anything, and a masked P of 0 times a NaN V row would still poison O.
+    const int low = PART ? key_lo - key0 : 0;  // <= 0 past the first stage
     const char* kb = kseq + (int64_t)key0 * tok * 2;
     const char* vb = vseq + (int64_t)key0 * tok * 2;
     const uint32_t lk = lds_addr(kring) + st * TILEB + wave * 1024;
     const uint32_t lv = lds_addr(vring) + st * TILEB + wave * 1024;
 #pragma unroll
     for (int p = 0; p < NDMA; ++p) {
-      const uint32_t roff = (uint32_t)min(drow[p], lim) * tokb;
+      const uint32_t roff = (uint32_t)(PART ? max(min(drow[p], lim), low) : min(drow[p], lim)) * tokb;
       dma16_sbase(kb, roff + dck[p], lk + NW * p * 1024);
       dma16_sbase(vb, roff + dcv[p], lv + NW * p * 1024);
     }

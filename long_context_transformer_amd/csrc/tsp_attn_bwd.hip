@@ -430,13 +430,16 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         const float dsub = dp[r] - d_s[qr];
         if (whole) {
           p[e] = ex;
+          ds[e] = ex * dsub;
         } else {
+          // A key past the rank's last position has K and V rows the caller need not fill:
+          // dsub may then be NaN, so dS is selected, not multiplied by a zero P.
           const int row = q0 + qr;
           const bool ok =
               kvalid & (row < a.rows) & (kj <= (int)zigzag_pos(min(row, a.rows - 1), a.C, a.rank, a.D));
           p[e] = ok ? ex : 0.0f;
+          ds[e] = ok ? ex * dsub : 0.0f;
         }
-        ds[e] = p[e] * dsub;
       }
       const bf16x8 pf = pack8(p);
       const bf16x8 dsf = pack8(ds);

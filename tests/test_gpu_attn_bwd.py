@@ -21,7 +21,7 @@ import torch
 from long_context_transformer_amd import synth, tsp
 from oracle import tsp_oracle as O
 
-from _gpu_helpers import check_close, dev_bf16, host_f64
+from _gpu_helpers import BF16_NAN, check_close, dev_bf16, host_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +81,32 @@ def test_attn_bwd_parity(B, S, D, rank, H, hd):
         check_close(f"{label} dv", host_f64(dv), rv)
         last = int(idx.max())
         assert torch.all(dk[:, last + 1:] == 0) and torch.all(dv[:, last + 1:] == 0), "keys no row sees"
+
+
+@pytest.mark.parametrize("B,S,D,rank,H,hd", [(2, 1200, 3, 1, 3, 128), (1, 1320, 3, 2, 2, 64)])
+def test_attn_bwd_unfilled_keys(B, S, D, rank, H, hd):
+    """K/V rows after the rank's last position hold NaN (the forward never reads them, so a
+    caller need not fill them). With C = 200 and C = 220 the rank's last position is not a
+    multiple of 32, so a 32-key wave of the key-stationary kernel straddles it; its gradients
+    must stay finite, match the oracle, and be exactly zero at keys no query of the rank sees."""
+    print(f"attention backward, NaN past the last position: B={B} S={S} D={D} rank={rank}", flush=True)
+    seed = 760 + rank
+    q = synth.normal_bf16((B, S // D, H, hd), seed, std=1.0)
+    k = synth.normal_bf16((B, S, H, hd), seed + 1, std=1.0)
+    v = synth.normal_bf16((B, S, H, hd), seed + 2, std=1.0)
+    g = synth.normal_bf16((B, S // D, H, hd), seed + 3, std=1.0)
+    idx = O.zigzag_index(S, D, rank)
+    last = int(idx.max())
+    assert last + 1 < S and (last + 1) % 32 != 0
+    k_nan, v_nan = k.copy(), v.copy()
+    k_nan[:, last + 1:] = BF16_NAN
+    v_nan[:, last + 1:] = BF16_NAN
+    rq, rk, rv = O.causal_attention_bwd(synth.to_f64(q), idx, synth.to_f64(k), synth.to_f64(v), synth.to_f64(g))
+    dq, dk, dv = run_bwd(q, k_nan, v_nan, g, B, S, D, rank, H, hd)
+    check_close("dq", host_f64(dq), rq)
+    check_close("dk", host_f64(dk), rk)
+    check_close("dv", host_f64(dv), rv)
+    assert torch.all(dk[:, last + 1:] == 0) and torch.all(dv[:, last + 1:] == 0), "keys no row sees"
 
 
 def test_attn_bwd_errors_and_empty():

@@ -55,6 +55,14 @@ def run_range(qd, kd, vd, B, S, D, r, H, hd, lo, hi):
     return o, lse
 
 
+def nan_outside(t, lo, hi):
+    """Copy of a [B, S, H, hd] bf16 K or V buffer whose rows outside [lo, hi) are NaN: the
+    chunks the all-gather has not delivered yet may hold anything."""
+    out = torch.full_like(t, float("nan"))
+    out[:, lo:hi] = t[:, lo:hi]
+    return out
+
+
 def check_range(name, o, lse, ref_o, ref_lse):
     o_h = o.cpu().numpy().astype(np.float64)
     l_h = lse.cpu().numpy().astype(np.float64)
@@ -83,7 +91,8 @@ def test_attn_range_parity(B, S, D, rank, H, hd, ranges):
     idx = O.zigzag_index(S, D, rank)
     qf, kf, vf = synth.to_f64(q), synth.to_f64(k), synth.to_f64(v)
     for lo, hi in ranges:
-        o, lse = run_range(qd, kd, vd, B, S, D, rank, H, hd, lo, hi)
+        # K/V rows outside the range are NaN: the kernel must read only [lo, hi)
+        o, lse = run_range(qd, nan_outside(kd, lo, hi), nan_outside(vd, lo, hi), B, S, D, rank, H, hd, lo, hi)
         torch.cuda.synchronize()
         ref_o, ref_lse = O.attention_range(qf, idx, kf, vf, lo, hi)
         check_range(f"[{lo},{hi})", o, lse, ref_o, ref_lse)
@@ -207,6 +216,55 @@ def test_chunked_pipeline(B, S, D, rank, H, hd):
             check_close(f"{tag} O vs oracle", host_f64(out), ref_o)
             check_lse(f"{tag} lse vs oracle", lse.cpu().numpy().astype(np.float64), ref_lse)
             check_close(f"{tag} O vs single launch", host_f64(out), host_f64(mono))
+
+
+ARRIVAL_CASES = [  # B, S, D, rank, H, hd: C = 32 (half the chunk starts off the 64-key stage) and C = 200
+    (1, 256, 4, 0, 4, 64),
+    (1, 256, 4, 1, 4, 64),
+    (1, 256, 4, 2, 4, 64),
+    (1, 256, 4, 3, 4, 64),
+    (2, 1200, 3, 1, 3, 128),
+    (1, 1200, 3, 2, 2, 64),
+]
+
+
+@pytest.mark.parametrize("B,S,D,rank,H,hd", ARRIVAL_CASES)
+def test_chunked_pipeline_as_delivered(B, S, D, rank, H, hd):
+    """K/V as the all-gather delivers it: every row starts as NaN and each chunk's rows are
+    written just before its range launch, in arrival order. A range launch that read a row
+    of a chunk still to come would carry NaN into the accumulator (a masked score gives
+    P = 0, but 0 * NaN is NaN), so a finite result that matches the oracle shows that each
+    launch reads only its own chunk."""
+    print(f"chunked pipeline as delivered B={B} S={S} D={D} rank={rank} H={H} hd={hd}", flush=True)
+    q, k, v = qkv_inputs(B, S, D, H, hd, 600 + S % 83 + rank)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    idx = O.zigzag_index(S, D, rank)
+    ref_o, ref_lse = O.causal_attention(synth.to_f64(q), idx, synth.to_f64(k), synth.to_f64(v))
+    C = S // (2 * D)
+    R = S // D
+    for fused in (True, False):
+        kbuf, vbuf = torch.full_like(kd, float("nan")), torch.full_like(vd, float("nan"))
+        acc_o = torch.zeros((B, R, H, hd), dtype=torch.float32, device="cuda")
+        acc_l = torch.full((B, H, R), float("-inf"), dtype=torch.float32, device="cuda")
+        out = torch.full((B, R, H, hd), float("nan"), dtype=torch.bfloat16, device="cuda")
+        po, pl = torch.empty_like(acc_o), torch.empty_like(acc_l)
+        order = arrival_order(D, rank)
+        for n, c in enumerate(order):
+            lo, hi = c * C, (c + 1) * C
+            kbuf[:, lo:hi] = kd[:, lo:hi]  # this chunk arrives (same stream as the launches)
+            vbuf[:, lo:hi] = vd[:, lo:hi]
+            last = out if n == len(order) - 1 else None
+            if fused:
+                tsp.attn_fwd_range(qd, kbuf, vbuf, acc_o, acc_l, B, S, D, rank, H, hd, lo, hi, accumulate=True,
+                                   o_out=last)
+            else:
+                tsp.attn_fwd_range(qd, kbuf, vbuf, po, pl, B, S, D, rank, H, hd, lo, hi)
+                tsp.attn_merge(acc_o, acc_l, po, pl, last, B, S, D, H, hd)
+        torch.cuda.synchronize()
+        tag = "fused" if fused else "range+merge"
+        assert bool(torch.isfinite(acc_o).all()), f"{tag}: non-finite accumulator"
+        check_close(f"{tag} O vs oracle", host_f64(out), ref_o)
+        check_lse(f"{tag} lse vs oracle", acc_l.cpu().numpy().astype(np.float64), ref_lse)
 
 
 @pytest.mark.parametrize("name,rank", [("7b_s128k_d8", 0), ("7b_s32k_d8", 5)])
