@@ -176,7 +176,6 @@ TSP_API int tsp_attn_merge(float* o_acc, float* lse_acc, const float* o_part, co
                            void* o_out, int32_t B, int64_t S, int32_t D, int32_t n_heads,
                            int32_t head_dim, tsp_stream_t stream);
 
-/* Workspace bytes tsp_mlp_shard_accum needs for M rows and shard width Fs. */
 /*
  * Gradients of the rank's causal attention (backward of tsp_attn_fwd). The pages name
  * training but do not describe the backward pass: this is the derivative of the forward
@@ -202,6 +201,7 @@ TSP_API int tsp_attn_bwd(const void* q, const void* k_full, const void* v_full, 
                          int32_t head_dim, float scale, void* ws, size_t ws_bytes,
                          tsp_stream_t stream);
 
+/* Workspace bytes tsp_mlp_shard_accum needs for M rows and shard width Fs. */
 TSP_API size_t tsp_mlp_workspace_size(int64_t M, int32_t Fs);
 
 /*
@@ -223,7 +223,9 @@ TSP_API int tsp_mlp_shard_accum(const void* x, const void* w1_j, const void* w3_
 
 /* Workspace bytes tsp_layer_fwd needs for `desc` (0 if desc is invalid): Q and O of the
  * rank, bf16 [B, 2C, d] each, and the gated hidden of all D shards, bf16
- * [B*2C, D * round_up(F/D, 8)]. */
+ * [B*2C, D * round_up(F/D, 8)], in that order, each starting at a multiple of 256 bytes
+ * (Q at offset 0, O at round_up(B*2C*d*2, 256)). After a call O holds the rank's attention
+ * output, bf16 [B, 2C, H, hd] in local row order. */
 TSP_API size_t tsp_layer_workspace_size(const tsp_layer_desc* desc);
 
 /*

@@ -1,21 +1,26 @@
-"""Full-size GPU parity at the five layer workloads, on sampled outputs.
+"""Full-size GPU parity at the five layer workloads.
 
 The layer runs exactly as the benchmark times it: tsp_layer_fwd at the workload's own
 sizes, W1/W3 shards as row blocks of one tensor, W2 shards contiguous, the peers' K/V
 rows filled by their own QKV projections (the one-GPU stand-in for the all-gather), and
-the rank's own K/V rows set to NaN beforehand so the call must write them. The fp64
-oracle then evaluates only sampled local rows: K and V of every position are projected
-once per workload and sequence, then Q, causal attention, W_O and the SwiGLU at the
-sampled rows (the unsharded layer's outputs at those positions).
+the rank's own K/V rows set to NaN beforehand so the call must write them. attn_out and
+mlp_out start as NaN, and every element of both must be finite afterwards.
 
-Sampled rows: both ends of each zigzag chunk (the first query positions, the chunk seam,
-the rank's last rows, which see the longest key prefix) plus seeded random rows.
+Element-wise, every row: S=16K rank 0 (the 256x256 QKV and 256x128 gate/up tiles), and
+all 8 ranks of S=32K glued back into the whole sequence (every GEMM on its large tile),
+against the fp64 oracle's unsharded layer over all positions; the attention output O
+(read from the layer's workspace) is also checked per (zigzag chunk, head).
+Sampled rows at S=128K and B=4 S=64K, where the fp64 oracle of every row would take hours:
+both ends of each zigzag chunk (the first query positions, the chunk seam, the rank's
+last rows, which see the longest key prefix) plus seeded random rows.
 
 Method: summary of "Folding Tensor and Sequence Parallelism for Memory-Efficient
 Transformer Training & Inference" (gist.science 2604.26294), §2 (zigzag partition,
 attention over the all-gathered K/V, MLP shards accumulated in ring order).
 Tolerance: max-abs <= 2e-2 max|ref|, mean-abs <= 2e-3 max|ref| per sampled tensor.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -24,7 +29,7 @@ import torch
 from long_context_transformer_amd import synth, tsp
 from oracle import tsp_oracle as O
 
-from _gpu_helpers import (check_close, check_lse, dev_bf16, fill_peer_kv, host_f64,
+from _gpu_helpers import (MAX_REL, MEAN_REL, check_close, check_lse, dev_bf16, fill_peer_kv, host_f64,
                           nan_bf16, shard_rows)
 
 pytestmark = pytest.mark.gpu
@@ -61,6 +66,63 @@ def oracle_rows(x_b, f64w, k, v, pos, d, H):
     return a, y
 
 
+def attention_by_head(q, pos, k, v):
+    """The oracle's causal_attention evaluated one head at a time on a thread pool (numpy
+    releases the interpreter lock inside its array loops, so heads run side by side; each
+    head's arithmetic is the oracle's own). BLAS runs one thread per call meanwhile."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    B, n, H, hd = q.shape
+    o = np.empty((B, n, H, hd))
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), H))
+
+    def one(h):
+        oh, _ = O.causal_attention(q[:, :, h:h + 1], pos, k[:, :, h:h + 1], v[:, :, h:h + 1])
+        o[:, :, h:h + 1] = oh
+
+    with threadpool_limits(1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, range(H)))
+    return o
+
+
+def oracle_all_rows(x_b, f64w, k, v, pos, d, H):
+    """fp64 O [1, n, H, hd], attn_out and mlp_out of one sequence at global positions `pos`
+    (every row of a rank, or the whole sequence)."""
+    q = O.split_heads(O.project(x_b[:, pos], f64w["w_qkv"][0:d]), H)
+    o = attention_by_head(q, pos, k, v)
+    del q
+    a = O.project(o.reshape(1, len(pos), d), f64w["w_o"])
+    y = O.swiglu_mlp(a, f64w["w1"], f64w["w3"], f64w["w2"])
+    return o, a, y
+
+
+def ws_attention_out(ws, B, R, H, hd):
+    """The rank's attention output O (bf16 [B, 2C, H, hd]) as tsp_layer_fwd leaves it in its
+    workspace: Q at offset 0, O at the next 256-byte boundary after B*2C*d bf16 values."""
+    n = B * R * H * hd
+    off = (2 * n + 255) // 256 * 256
+    return ws[off:off + 2 * n].view(torch.bfloat16).view(B, R, H, hd)
+
+
+def check_per_chunk_head(name, got, ref, chunk_of_row):
+    """The contract per (zigzag chunk, head) of an attention output [n, H, hd]: max-abs and
+    mean-abs against that slice's own max|ref|. Prints the worst slice."""
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    worst_max = worst_mean = 0.0
+    for c in np.unique(chunk_of_row):
+        sel = chunk_of_row == c
+        err = np.abs(got[sel] - ref[sel])          # [rows, H, hd]
+        scale = np.abs(ref[sel]).max(axis=(0, 2))  # [H]
+        mx = err.max(axis=(0, 2)) / scale
+        mean = err.mean(axis=(0, 2)) / scale
+        worst_max, worst_mean = max(worst_max, float(mx.max())), max(worst_mean, float(mean.max()))
+        assert np.all(mx <= MAX_REL), f"{name}: chunk {c} heads {np.nonzero(mx > MAX_REL)[0]} max-abs {mx.max():.3g}"
+        assert np.all(mean <= MEAN_REL), f"{name}: chunk {c} mean-abs {mean.max():.3g}"
+    print(f"  {name}: worst (chunk, head) max-abs {worst_max:.2e}, mean-abs {worst_mean:.2e} of max|ref|",
+          flush=True)
+
+
 class LayerRig:
     """Device copies of one workload's inputs, shared by the ranks run on it."""
 
@@ -91,7 +153,7 @@ class LayerRig:
         self.peers_of = rank
         xs = shard_rows(self.x_full, S, D, rank)
         desc = tsp.make_desc(B, S, D, rank, d, H, hd, F)
-        a = torch.empty((B, S // D, d), dtype=torch.bfloat16, device="cuda")
+        a = torch.full((B, S // D, d), float("nan"), dtype=torch.bfloat16, device="cuda")
         y = torch.full((B, S // D, d), float("nan"), dtype=torch.float32, device="cuda")
         if streamed:
             if self.packed is None:
@@ -112,6 +174,9 @@ class LayerRig:
         torch.cuda.synchronize()
         idx = torch.from_numpy(tsp.zigzag_index(S, D, rank)).cuda()
         assert bool(torch.isfinite(self.kf[:, idx]).all()) and bool(torch.isfinite(self.vf[:, idx]).all())
+        assert bool(torch.isfinite(a).all()), "non-finite attn_out"
+        assert bool(torch.isfinite(y).all()), "non-finite mlp_out"
+        self.ws = ws
         return a, y
 
 
@@ -143,12 +208,53 @@ def check_layer_workload(name, ranks, batches, streamed=False):
         assert np.all(np.isfinite(y_h)), "non-finite mlp_out row"
 
 
-def test_fullsize_layer_s16k():
-    check_layer_workload("7b_s16k_d8", ranks=[0], batches=[0])
+def check_layer_every_row(name, ranks):
+    """Every row of the given ranks (batch 0) against the oracle's unsharded layer; the ranks'
+    rows glued back into natural position order when they are all D ranks."""
+    w0 = synth.WORKLOADS[name]
+    assert w0.B == 1
+    print(f"full-size layer {name}, every row of ranks {list(ranks)}: generating inputs", flush=True)
+    inputs = synth.layer_inputs(w0)
+    f64w = {k: synth.to_f64(v) for k, v in inputs.items() if k != "x_full"}
+    rig = LayerRig(w0, inputs)
+    S, D, C, d, H, hd = w0.S, w0.D, w0.C, w0.d_model, w0.n_heads, w0.head_dim
+    R = S // D
+    pos = np.concatenate([O.zigzag_index(S, D, r) for r in ranks])
+    got_o = np.empty((len(pos), H, hd))
+    got_a = np.empty((len(pos), d))
+    got_y = np.empty((len(pos), d))
+    for n, r in enumerate(ranks):
+        print(f"  rank {r}: tsp_layer_fwd B=1 S={S} D={D}", flush=True)
+        a, y = rig.run(r)
+        rows = slice(n * R, (n + 1) * R)
+        got_a[rows], got_y[rows] = host_f64(a)[0], host_f64(y)[0]
+        got_o[rows] = host_f64(ws_attention_out(rig.ws, 1, R, H, hd))[0]
+    del rig
+    torch.cuda.empty_cache()
+    order = np.argsort(pos, kind="stable")
+    pos = pos[order]
+    got_o, got_a, got_y = got_o[order], got_a[order], got_y[order]
+    print(f"  oracle: K/V of {S} positions, then the layer at {len(pos)} positions", flush=True)
+    x_b = synth.to_f64(inputs["x_full"][0:1])
+    k, v = oracle_kv(x_b, f64w["w_qkv"], d, H)
+    ro, ra, ry = oracle_all_rows(x_b, f64w, k, v, pos, d, H)
+    label = f"{name} ranks {ranks[0]}..{ranks[-1]}" if len(ranks) > 1 else f"{name} r{ranks[0]}"
+    check_per_chunk_head(f"{label} O", got_o, ro[0], pos // C)
+    check_close(f"{label} attn_out (every row)", got_a, ra[0])
+    check_close(f"{label} mlp_out (every row)", got_y, ry[0])
 
 
-def test_fullsize_layer_s32k_all_ranks():
-    check_layer_workload("7b_s32k_d8", ranks=range(8), batches=[0])
+@pytest.mark.timeout(600)
+def test_fullsize_layer_s16k_every_row():
+    check_layer_every_row("7b_s16k_d8", ranks=[0])
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_layer_s32k_all_ranks_glued():
+    """All 8 ranks of S=32K glued back into the whole sequence: the concatenated shards
+    reproduce the unsharded layer over every position (the zigzag partition covers the
+    sequence once)."""
+    check_layer_every_row("7b_s32k_d8", ranks=list(range(8)))
 
 
 def test_fullsize_layer_s128k():

@@ -33,6 +33,7 @@ QKV_CASES = [  # B, S, D, rank, H, hd
     (1, 256, 4, 3, 4, 64),
     (2, 1200, 3, 1, 4, 128),   # C = 200: ragged row tiles
     (1, 640, 1, 0, 2, 128),    # D = 1
+    (1, 4096, 2, 1, 32, 128),  # M = 2048, N = 12288: 384 tiles of 256 x 256 (the large-tile kernel)
 ]
 
 
@@ -137,6 +138,9 @@ MLP_CASES = [  # M, d, Fs, ld_w2 (0 = Fs)
     (64, 256, 172, 688),     # W2 shard as a column block of the full W2
     (300, 512, 344, 0),      # ragged M and N
     (1000, 256, 1376, 0),    # the 7B shard width: K tail of 32 in the down projection
+    # the large-tile kernels: gate/up 256 x 128 per weight (512 tiles), down 256 x 256 (256 tiles)
+    (4096, 4096, 4096, 0),
+    (4000, 4096, 4104, 0),   # ragged: M tail 160, gate/up N tail 8, down K tail 8
 ]
 
 
