@@ -10,10 +10,12 @@ synthetic tensors already resident in HBM; the peers' K/V rows (what the all-gat
 delivers) are filled before timing by the peers' own QKV projections.
 
 Prints ONE JSON line: whole-step throughput in TFLOP/s of algorithmic work (exact
-causal pairs), the attention kernel's roofline, and the CPU oracle timed on a bounded
-sample of the same workload. The attention time is the average over the K timed steps
-of the library's own phase events, recorded on the launch stream around the attention
-launch inside each tsp_layer_fwd call (tsp_timing_start / tsp_timing_read). The
+causal pairs) at the median step time (each of the K timed steps has its own pair of HIP
+events on the launch stream; min, max and mean are reported beside it), the attention
+kernel's roofline, and the CPU oracle timed on a bounded sample of the same workload
+(cores = the host CPUs this process may run on). The attention time is the average over
+the K timed steps of the library's own phase events, recorded on the launch stream around
+the attention launch inside each tsp_layer_fwd call (tsp_timing_start / tsp_timing_read). The
 roofline's HBM traffic comes from the committed FETCH_SIZE / WRITE_SIZE counter summary
 of the attention kernel, and is reported only while the kernel's sources still hash to
 the value recorded there.
@@ -95,25 +97,35 @@ def step(st):
 
 
 def time_layer(st, steps, warmup):
-    """Average step time (ms) over `steps` timed steps, and the per-phase averages from the
-    library's events recorded inside those same steps."""
+    """Times `steps` steps, each between its own pair of HIP events on the launch stream
+    (torch's current stream, which the library launches on). Returns per-step statistics
+    (median, min, max, mean, and the whole timed region) in ms, the wall time, and the
+    per-phase averages from the library's events recorded inside those same steps."""
+    import statistics
     import torch
     from long_context_transformer_amd import tsp
     for _ in range(warmup):
         step(st)
     torch.cuda.synchronize()
     tsp.timing_start(steps)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = [(ev(), ev()) for _ in range(steps)]
+    ev0, ev1 = ev(), ev()
     wall0 = time.perf_counter()
     ev0.record()
-    for _ in range(steps):
+    for e0, e1 in marks:
+        e0.record()
         step(st)
+        e1.record()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    per = [e0.elapsed_time(e1) for e0, e1 in marks]
+    stats = {"median": statistics.median(per), "min": min(per), "max": max(per),
+             "mean": sum(per) / len(per), "region": ev0.elapsed_time(ev1)}
     calls = tsp.timing_read(steps)
     phases = {p: sum(c[p] for c in calls) / len(calls) for p in tsp.PHASES}
-    return ev0.elapsed_time(ev1) / steps, wall, phases
+    return stats, wall, phases
 
 
 def calib_copy():
@@ -422,7 +434,8 @@ def cpu_baseline(w, inputs, rank, rows_sample):
     flops = (2 * 2 * kmax * d * d + 2 * R * d * d + 4 * H * hd * pairs + 2 * R * d * d
              + 6 * R * d * F)
     threads, api = blas_threads()
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
+            "blas_threads": threads, "kind": "oracle",
             "sample": (f"{w.name} rank {rank}, batch 0: local rows {R2 - R}..{R2 - 1} (positions "
                        f"{int(idx[rows].min())}..{int(idx[rows].max())}) through QKV, causal "
                        f"attention, W_O and SwiGLU, plus K/V projections of positions 0..{kmax - 1}; "
@@ -472,7 +485,8 @@ def main():
     print(f"# setup {st['setup_s']:.1f}s", file=sys.stderr, flush=True)
     if args.calib_copy:
         calib_copy()
-    ms, wall, phases = time_layer(st, args.steps, args.warmup)
+    stats, wall, phases = time_layer(st, args.steps, args.warmup)
+    ms = stats["median"]
     flops, attn_flops = layer_flops(w.B, w.S, w.D, w.d_model, w.n_heads, w.head_dim, w.ffn)
     tflops = flops / (ms * 1e-3) / 1e12
     attn_ms = phases["attention"]
@@ -519,6 +533,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_median": round(stats["median"], 4),
+        "ms_min": round(stats["min"], 4),
+        "ms_max": round(stats["max"], 4),
+        "ms_mean": round(stats["mean"], 4),
+        "ms_timed_region": round(stats["region"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -563,7 +582,8 @@ def main():
                 for r in ranks:
                     ww = base.with_rank(r)
                     s2 = setup(ww, r)
-                    ms2, _, ph2 = time_layer(s2, 10 if ww.S >= 65536 else 20, 3)
+                    st2, _, ph2 = time_layer(s2, 10 if ww.S >= 65536 else 20, 3)
+                    ms2 = st2["median"]
                     fl, afl = layer_flops(ww.B, ww.S, ww.D, ww.d_model, ww.n_heads, ww.head_dim, ww.ffn)
                     ams = ph2["attention"]
                     line = {"workload": name, "rank": r, "ms": round(ms2, 4),
