@@ -221,6 +221,29 @@ TSP_API int tsp_mlp_shard_accum(const void* x, const void* w1_j, const void* w3_
                         int64_t ld_w2, float* acc, int64_t M, int32_t d, int32_t Fs,
                         int32_t accumulate, void* ws, size_t ws_bytes, tsp_stream_t stream);
 
+/*
+ * tsp_mlp_shard_accum without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, semantics and errors as tsp_mlp_shard_accum; the gated hidden
+ * lives in a scratch array of tsp_mlp_noalloc_max_bytes() bytes (64 MiB) that the library
+ * holds on every GPU it runs on until the process ends. The call allocates and frees
+ * nothing itself; its first call on a device looks up that device's scratch address
+ * (hipGetSymbolAddress), which is when the HIP runtime materialises the 64 MiB on that
+ * device. A caller that must not see that happen, e.g. before a graph capture, makes one
+ * call first (M = 0 does not count: it returns before any HIP call).
+ *   Limit: tsp_mlp_workspace_size(M, Fs) <= tsp_mlp_noalloc_max_bytes(), e.g. at most
+ *   24385 rows at the 7B shard width Fs = 1376; larger calls return TSP_ERR_WORKSPACE
+ *   before any HIP call (the rows are independent, so a caller may split them).
+ *   The stream must belong to the current device. Every call on one GPU shares that GPU's
+ *   scratch: calls that overlap on one GPU (different streams, host threads or graphs
+ *   replayed concurrently) race; calls ordered on one stream do not.
+ */
+TSP_API size_t tsp_mlp_noalloc_max_bytes(void);
+TSP_API int tsp_mlp_shard_accum_noalloc(const void* x, const void* w1_j, const void* w3_j,
+                                        const void* w2_j, int64_t ld_w2, float* acc, int64_t M,
+                                        int32_t d, int32_t Fs, int32_t accumulate,
+                                        tsp_stream_t stream);
+
 /* Workspace bytes tsp_layer_fwd needs for `desc` (0 if desc is invalid): Q and O of the
  * rank, bf16 [B, 2C, d] each, and the gated hidden of all D shards, bf16
  * [B*2C, D * round_up(F/D, 8)], in that order, each starting at a multiple of 256 bytes

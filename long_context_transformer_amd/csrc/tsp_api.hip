@@ -85,6 +85,56 @@ hipEvent_t* timing_slot() {
 
 size_t mlp_ws_bytes(int64_t M, int64_t Fs) { return round_up((size_t)M * (size_t)round_up((size_t)Fs, 8) * 2, kAlign); }
 
+// Scratch of tsp_mlp_shard_accum_noalloc: the gated hidden of one ring step. A device global,
+// so every GPU the library runs on holds its own copy from the module's load until the
+// process ends. In host code `scratch` names a host-side stand-in, not device memory: the
+// kernels get this device's address of it, taken once per device by hipGetSymbolAddress.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first call per device).
+int scratch_address(void** out) {
+  int dev = 0;
+  if (int rc = hip_status(hipGetDevice(&dev), "hipGetDevice")) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(TSP_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (int rc = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress")) return rc;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TSP_OK;
+}
+
+// Shape and pointer checks of one MLP ring step (everything but the workspace).
+int check_mlp_step(const void* x, const void* w1_j, const void* w3_j, const void* w2_j, int64_t ld_w2, const float* acc,
+                   int64_t M, int32_t d, int32_t Fs) {
+  if (M < 0 || d < 1 || Fs < 1) return fail(TSP_ERR_SHAPE, "M must be >= 0, d and Fs >= 1");
+  if (M > kMaxI32 / 4) return fail(TSP_ERR_UNSUPPORTED, "M too large for 32-bit row indices");
+  if (ld_w2 < Fs) return fail(TSP_ERR_SHAPE, "ld_w2 %lld < Fs %d", (long long)ld_w2, Fs);
+  if (M == 0) return TSP_OK;
+  if (!x || !w1_j || !w3_j || !w2_j || !acc) return fail(TSP_ERR_NULL, "x, w1_j, w3_j, w2_j and acc must be non-NULL");
+  if (misaligned(x) || misaligned(w1_j) || misaligned(w3_j) || misaligned(w2_j) || misaligned(acc))
+    return fail(TSP_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  return TSP_OK;
+}
+
+// The two launches of one ring step: gated hidden into h, then its down projection into acc.
+int launch_mlp_step(const void* x, const void* w1_j, const void* w3_j, const void* w2_j, int64_t ld_w2, float* acc,
+                    int64_t M, int32_t d, int32_t Fs, int32_t accumulate, void* h, hipStream_t s) {
+  const int64_t ldh = (int64_t)round_up((size_t)Fs, 8);
+  if (int rc = hip_status(tsp::launch_gate_up(x, d, w1_j, w3_j, d, h, ldh, (int)M, Fs, d, s), "gate/up launch"))
+    return rc;
+  if (int rc = hip_status(tsp::launch_down_acc(h, ldh, w2_j, ld_w2, acc, d, (int)M, d, Fs, accumulate ? 1 : 0, s),
+                          "down projection launch"))
+    return rc;
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,24 +299,33 @@ size_t tsp_mlp_workspace_size(int64_t M, int32_t Fs) {
 int tsp_mlp_shard_accum(const void* x, const void* w1_j, const void* w3_j, const void* w2_j, int64_t ld_w2, float* acc,
                         int64_t M, int32_t d, int32_t Fs, int32_t accumulate, void* ws, size_t ws_bytes,
                         tsp_stream_t stream) {
-  if (M < 0 || d < 1 || Fs < 1) return fail(TSP_ERR_SHAPE, "M must be >= 0, d and Fs >= 1");
-  if (M > kMaxI32 / 4) return fail(TSP_ERR_UNSUPPORTED, "M too large for 32-bit row indices");
-  if (ld_w2 < Fs) return fail(TSP_ERR_SHAPE, "ld_w2 %lld < Fs %d", (long long)ld_w2, Fs);
+  if (int rc = check_mlp_step(x, w1_j, w3_j, w2_j, ld_w2, acc, M, d, Fs)) return rc;
   if (M == 0) return ok();
-  if (!x || !w1_j || !w3_j || !w2_j || !acc || !ws)
-    return fail(TSP_ERR_NULL, "x, w1_j, w3_j, w2_j, acc and ws must be non-NULL");
-  if (misaligned(x) || misaligned(w1_j) || misaligned(w3_j) || misaligned(w2_j) || misaligned(acc) || misaligned(ws))
-    return fail(TSP_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  if (!ws) return fail(TSP_ERR_NULL, "ws must be non-NULL");
+  if (misaligned(ws)) return fail(TSP_ERR_ALIGN, "device pointers must be 16-byte aligned");
   if (ws_bytes < mlp_ws_bytes(M, Fs))
     return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, mlp_ws_bytes(M, Fs));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t ldh = (int64_t)round_up((size_t)Fs, 8);
-  if (int rc = hip_status(tsp::launch_gate_up(x, d, w1_j, w3_j, d, ws, ldh, (int)M, Fs, d, s), "gate/up launch"))
-    return rc;
-  if (int rc = hip_status(tsp::launch_down_acc(ws, ldh, w2_j, ld_w2, acc, d, (int)M, d, Fs, accumulate ? 1 : 0, s),
-                          "down projection launch"))
-    return rc;
-  return ok();
+  return launch_mlp_step(x, w1_j, w3_j, w2_j, ld_w2, acc, M, d, Fs, accumulate, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t tsp_mlp_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int tsp_mlp_shard_accum_noalloc(const void* x, const void* w1_j, const void* w3_j, const void* w2_j, int64_t ld_w2,
+                                float* acc, int64_t M, int32_t d, int32_t Fs, int32_t accumulate,
+                                tsp_stream_t stream) {
+  if (int rc = check_mlp_step(x, w1_j, w3_j, w2_j, ld_w2, acc, M, d, Fs)) return rc;
+  if (M == 0) return ok();
+  const size_t need = mlp_ws_bytes(M, Fs);
+  if (need > kScratchBytes)
+    return fail(TSP_ERR_WORKSPACE,
+                "M=%lld rows of width Fs=%d need %zu bytes of scratch, above the %zu-byte maximum of the "
+                "allocation-free entry point (use tsp_mlp_shard_accum with a workspace, or fewer rows per call)",
+                (long long)M, Fs, need, kScratchBytes);
+  void* h = nullptr;
+  if (int rc = scratch_address(&h)) return rc;
+  // Nothing in the scratch needs to start at zero: the gate/up launch writes every element of
+  // the [M, Fs] hidden before the down projection reads it.
+  return launch_mlp_step(x, w1_j, w3_j, w2_j, ld_w2, acc, M, d, Fs, accumulate, h, static_cast<hipStream_t>(stream));
 }
 
 namespace {

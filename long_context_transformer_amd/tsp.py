@@ -48,6 +48,8 @@ _SIGS = {
     "tsp_mlp_workspace_size": (ctypes.c_size_t, [_I64, _I32]),
     "tsp_mlp_shard_accum": (_I32, [_VP, _VP, _VP, _VP, _I64, _VP, _I64, _I32, _I32, _I32, _VP,
                                    ctypes.c_size_t, _VP]),
+    "tsp_mlp_noalloc_max_bytes": (ctypes.c_size_t, []),
+    "tsp_mlp_shard_accum_noalloc": (_I32, [_VP, _VP, _VP, _VP, _I64, _VP, _I64, _I32, _I32, _I32, _VP]),
     "tsp_layer_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc)]),
     "tsp_layer_fwd": (_I32, [ctypes.POINTER(LayerDesc), _VP, _VP, _VP, ctypes.POINTER(_VP),
                              ctypes.POINTER(_VP), ctypes.POINTER(_VP), _VP, _VP, _VP, _VP, _VP,
@@ -183,6 +185,15 @@ def mlp_shard_accum(x, w1_j, w3_j, w2_j, ld_w2, acc, M, d, Fs, accumulate, ws, w
     _check(load().tsp_mlp_shard_accum(_ptr(x), _ptr(w1_j), _ptr(w3_j), _ptr(w2_j), ld_w2, _ptr(acc), M,
                                       d, Fs, 1 if accumulate else 0, _ptr(ws), ws_bytes,
                                       _stream(stream, x)))
+
+
+def mlp_noalloc_max_bytes():
+    return int(load().tsp_mlp_noalloc_max_bytes())
+
+
+def mlp_shard_accum_noalloc(x, w1_j, w3_j, w2_j, ld_w2, acc, M, d, Fs, accumulate, stream=None):
+    _check(load().tsp_mlp_shard_accum_noalloc(_ptr(x), _ptr(w1_j), _ptr(w3_j), _ptr(w2_j), ld_w2, _ptr(acc), M,
+                                              d, Fs, 1 if accumulate else 0, _stream(stream, x)))
 
 
 def make_desc(B, S, D, rank, d_model, n_heads, head_dim, ffn, w2_ld=0, scale=0.0):

@@ -125,6 +125,23 @@ def test_mlp_errors():
     assert tsp.mlp_workspace_size(0, 172) == 0
 
 
+def test_mlp_noalloc_errors():
+    """The allocation-free MLP step: the same argument checks as the workspace form, and a
+    call whose gated hidden exceeds the scratch maximum is refused before any HIP call."""
+    f = tsp.load().tsp_mlp_shard_accum_noalloc
+    cap = tsp.mlp_noalloc_max_bytes()
+    assert cap == 64 << 20
+    assert f(A, A, A, None, 172, A, 64, 256, 172, 0, None) == 1
+    assert f(A, A, A, A, 171, A, 64, 256, 172, 0, None) == 2
+    assert f(A, A, A, A, 172, A, -1, 256, 172, 0, None) == 2
+    assert f(A, A, A, A, 172, MIS, 64, 256, 172, 0, None) == 6
+    rows = cap // (1376 * 2)                         # 24385 rows of the 7B shard width fit
+    assert tsp.mlp_workspace_size(rows, 1376) <= cap < tsp.mlp_workspace_size(rows + 1, 1376)
+    assert f(A, A, A, A, 1376, A, rows + 1, 4096, 1376, 0, None) == 5
+    assert b"maximum" in tsp.load().tsp_last_error()
+    assert f(None, None, None, None, 1376, None, 0, 4096, 1376, 0, None) == 0  # empty: no device access
+
+
 def _desc(**kw):
     base = dict(B=1, S=256, D=4, rank=0, d_model=256, n_heads=4, head_dim=64, ffn=688)
     base.update(kw)
