@@ -57,31 +57,21 @@
 namespace tsp {
 namespace {
 
-// Tile shape. Each wave owns QB 32-row query blocks; a workgroup owns BR rows (NW = BR /
-// (32 QB) waves) and streams keys through LDS in stages of BC = 64 (two 32-key softmax
-// blocks), with a 4-stage ring.
-//   BR 256, QB 1: 8 waves sharing one ring; two waves per SIMD, so one wave's softmax can
-//                 overlap the other's MFMAs (the default, fastest measured at 7B S=128K).
-//   BR 256, QB 2: one wave per SIMD; each K/V fragment feeds two query blocks.
-#ifndef TSP_ATTN_BR
-#define TSP_ATTN_BR 256
-#endif
-#ifndef TSP_ATTN_QB
-#define TSP_ATTN_QB 1
-#endif
-// CINIT 1: Q is pre-multiplied by scale*log2(e) (rounded to bf16) and every S MFMA chain
-// starts from -m, so the MFMAs produce s*c - m directly and the softmax needs no FMA per
-// score. CINIT 0: S = K Q^T, then one FMA per score.
-#ifndef TSP_ATTN_CINIT
-#define TSP_ATTN_CINIT 1
-#endif
-constexpr int BR = TSP_ATTN_BR;
+// Tile shape. A workgroup owns BR = 256 consecutive local query rows of one (sequence, head)
+// and streams keys through LDS in stages of BC = 64 (two 32-key softmax blocks), with a
+// 4-stage ring. Two kernels:
+//   attn_fwd      (head_dim 64)  8 waves of QB = 1 32-row block, two waves per SIMD, so one
+//                                wave's softmax can overlap the other's MFMAs;
+//   attn_fwd_w64  (head_dim 128) 4 waves of two 32-row blocks, one wave per SIMD; each K and
+//                                V fragment read from LDS feeds both blocks, and the wave
+//                                interleaves its own softmax with its MFMAs.
+constexpr int BR = 256;
 constexpr int BC = 64;
-constexpr int QB = TSP_ATTN_QB;
+constexpr int QB = 1;
 constexpr int RING = 4;
 constexpr int NW = BR / (32 * QB);
 constexpr int kThreads = 64 * NW;
-constexpr int kWavesPerSimd = (QB == 1) ? 2 : 1;
+constexpr int kWavesPerSimd = 2;
 constexpr float kLazy = 8.0f;     // rescale O only when the max grows by more than this (log2)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -120,20 +110,182 @@ struct AttnArgs {
   float scale_log2;
 };
 
-template <int HD>
+template <int HD, int THREADS = kThreads>
 struct Lay {
   static constexpr int KS = HD / 16;            // 16-dim reduction steps of Q K^T
   static constexpr int DB = HD / 32;            // 32-dim output blocks
   static constexpr int ROWB = HD * 2;           // bytes per key row
   static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
   static constexpr int TILEB = BC * ROWB;       // bytes of one K (or V) tile
-  static constexpr int NDMA = TILEB / (kThreads * 16);  // 16-byte loads per thread per tile
-  static_assert(NDMA >= 1 && NDMA * kThreads * 16 == TILEB, "whole tile per stage");
+  static constexpr int NDMA = TILEB / (THREADS * 16);  // 16-byte loads per thread per tile
+  static_assert(NDMA >= 1 && NDMA * THREADS * 16 == TILEB, "whole tile per stage");
   // K fragment reads touch 16 consecutive rows at one chunk; V transpose reads touch 4
   // consecutive rows (aligned to 4) x 4 chunks. Both swizzles spread those over all banks.
   __device__ static int fk(int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); }
   __device__ static int fv(int r) { return HD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
+
+// The work item of this workgroup: (sequence, head, query tile), and for a split launch the
+// key half with its partial outputs.
+struct TileSel {
+  int b, h, qt;
+  int key_lo, key_hi;
+  float* o32;
+  float* lse32;
+};
+
+// Item -> (sequence-head, query tile). A tile's work grows with its index (its last position
+// bounds its keys). Each (sequence, head) runs its heaviest tile first. With few tiles per CU
+// (lpt), an XCD's items instead go longest first across all its heads: the k-th heaviest tile
+// of each head before any head's (k+1)-th, so the CUs that finish a heavy tile take the light
+// ones; head-by-head order can give one CU two heavy tiles.
+template <bool PART>
+__device__ __forceinline__ TileSel select_tile(const AttnArgs& a) {
+  TileSel t;
+  int item = a.strided ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.items);
+  t.key_lo = a.key_lo;
+  t.key_hi = a.key_hi;
+  t.o32 = a.o32;
+  t.lse32 = a.lse;
+  if constexpr (PART) {
+    if (a.split > 0) {  // both halves of a tile are consecutive items
+      const int half = item & 1;
+      item >>= 1;
+      t.key_lo = half ? a.split : 0;
+      t.key_hi = half ? (int)a.S : a.split;
+      t.o32 += half * a.part_o;
+      t.lse32 += half * a.part_l;
+    }
+  }
+  int bh, qt;
+  const int n_run = a.qt_hi - a.qt_lo;
+  if (a.lpt) {
+    const int per_xcd = a.items / kNumXcd;
+    const int nbh_x = per_xcd / n_run;
+    const int x = item / per_xcd;
+    const int L = item - x * per_xcd;
+    const int k = L / nbh_x;
+    bh = x * nbh_x + (L - k * nbh_x);
+    qt = a.qt_hi - 1 - k;
+  } else {
+    bh = item / n_run;
+    qt = a.qt_hi - 1 - (item - bh * n_run);
+  }
+  t.b = bh / a.Hrun;
+  t.h = a.h0 + bh - t.b * a.Hrun;
+  t.qt = qt;
+  return t;
+}
+
+// Key-range attention, a tile whose keys all lie outside the range: O = 0 and lse = -inf for
+// its rows (accumulate: the range adds nothing; only the bf16 O is written if asked).
+template <int HD, int QB>
+__device__ __forceinline__ void store_no_keys(const AttnArgs& a, const TileSel& t, const int (&qi)[QB], int hl) {
+  if (a.accumulate && a.o == nullptr) return;
+  const int64_t tok = (int64_t)a.H * HD, otok = (int64_t)a.oH * HD;
+  const int oh = t.h - a.oh0;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (qi[qb] >= a.rows) continue;
+    const int64_t ro = ((int64_t)t.b * a.rows + qi[qb]) * tok + (int64_t)t.h * HD;
+    float* op = t.o32 + ((int64_t)t.b * a.prows + (qi[qb] - a.prow0)) * otok + (int64_t)oh * HD;
+#pragma unroll
+    for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = db * 32 + 8 * g + 4 * hl;
+        if (a.accumulate) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(op + dim);
+          *reinterpret_cast<uint2*>(a.o + ro + dim) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+        } else {
+          *reinterpret_cast<f32x4*>(op + dim) = f32x4{};
+          if (a.o != nullptr) *reinterpret_cast<uint2*>(a.o + ro + dim) = make_uint2(0u, 0u);
+        }
+      }
+    if (!a.accumulate && hl == 0) t.lse32[((int64_t)t.b * a.oH + oh) * a.prows + (qi[qb] - a.prow0)] = -INFINITY;
+  }
+}
+
+// Normalise and store one wave's rows: QB blocks of 32 rows with O^T accumulators oacc[qb][db]
+// (lane l32 + 32 hl: query l32 of block qb, dims 32 db + 8 (r / 4) + 4 hl + r % 4 in register
+// r), running max m_s (log2 units) and this half-wave's share of the row sum in l_run.
+//   PART = false: bf16 O, and the log-sum-exp if a.lse is set.
+//   PART = true:  fp32 O and log-sum-exp of the range (overwrite), or their log-sum-exp merge
+//                 into the accumulator (accumulate); bf16 O too if a.o is set.
+template <int HD, int QB, bool PART>
+__device__ __forceinline__ void store_rows(const AttnArgs& a, const TileSel& t, const int (&qi)[QB],
+                                           const f32x16 (&oacc)[QB][HD / 32], const float (&m_s)[QB],
+                                           const float (&l_half)[QB], int hl) {
+  constexpr int DB = HD / 32;
+  const int64_t tok = (int64_t)a.H * HD;
+  float inv[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_half[qb] + __shfl_xor(l_half[qb], 32);
+    inv[qb] = PART ? (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) : 1.0f / l_tot;
+    l_run[qb] = l_tot;
+  }
+  if constexpr (PART) {
+    const int64_t otok = (int64_t)a.oH * HD;
+    const int oh = t.h - a.oh0;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (qi[qb] >= a.rows) continue;
+      const int64_t ro = ((int64_t)t.b * a.rows + qi[qb]) * tok + (int64_t)t.h * HD;
+      float* op = t.o32 + ((int64_t)t.b * a.prows + (qi[qb] - a.prow0)) * otok + (int64_t)oh * HD;
+      float* lp = t.lse32 + ((int64_t)t.b * a.oH + oh) * a.prows + (qi[qb] - a.prow0);
+      const float lse_b = l_run[qb] > 0.0f ? (m_s[qb] + __log2f(l_run[qb])) * 0.69314718055994531f : -INFINITY;
+      // Overwrite: weights (0, 1). Accumulate: the log-sum-exp merge with what the
+      // accumulator holds (both lanes of the row read it before lane hl == 0 writes).
+      float wa = 0.0f, wb = 1.0f, lse_new = lse_b;
+      if (a.accumulate) {
+        const float lse_a = *lp;
+        const float mm = fmaxf(lse_a, lse_b);
+        wb = 0.0f;
+        if (mm != -INFINITY) {
+          wa = __expf(lse_a - mm);
+          wb = __expf(lse_b - mm);
+          const float z = wa + wb;
+          lse_new = mm + __logf(z);
+          wa /= z;
+          wb /= z;
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dim = db * 32 + 8 * g + 4 * hl;
+          const f32x16& o = oacc[qb][db];
+          const float s = wb * inv[qb];
+          f32x4 val = {o[4 * g] * s, o[4 * g + 1] * s, o[4 * g + 2] * s, o[4 * g + 3] * s};
+          if (a.accumulate) val += wa * *reinterpret_cast<const f32x4*>(op + dim);
+          *reinterpret_cast<f32x4*>(op + dim) = val;
+          if (a.o != nullptr) *reinterpret_cast<uint2*>(a.o + ro + dim) = pack_bf16x4(val[0], val[1], val[2], val[3]);
+        }
+      }
+      if (hl == 0) *lp = lse_new;
+    }
+    return;
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (qi[qb] >= a.rows) continue;
+    bf16_t* op = a.o + ((int64_t)t.b * a.rows + qi[qb]) * tok + (int64_t)t.h * HD;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = db * 32 + 8 * g + 4 * hl;
+        const f32x16& o = oacc[qb][db];
+        *reinterpret_cast<uint2*>(op + dim) =
+            pack_bf16x4(o[4 * g] * inv[qb], o[4 * g + 1] * inv[qb], o[4 * g + 2] * inv[qb], o[4 * g + 3] * inv[qb]);
+      }
+    }
+    if (a.lse != nullptr && hl == 0)
+      a.lse[((int64_t)t.b * a.H + t.h) * a.rows + qi[qb]] = (m_s[qb] + __log2f(l_run[qb])) * 0.69314718055994531f;
+  }
+}
 
 // PART = false: every key up to the query's position, bf16 O. PART = true: only keys in
 // [key_lo, key_hi) (a chunk of the sequence as the all-gather delivers it), fp32 O and the
@@ -153,41 +305,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
 
-  int item = a.strided ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.items);
-  int key_lo = a.key_lo, key_hi = a.key_hi;
-  float* o32 = a.o32;
-  float* lse32 = a.lse;
-  if constexpr (PART) {
-    if (a.split > 0) {  // both halves of a tile are consecutive items
-      const int half = item & 1;
-      item >>= 1;
-      key_lo = half ? a.split : 0;
-      key_hi = half ? (int)a.S : a.split;
-      o32 += half * a.part_o;
-      lse32 += half * a.part_l;
-    }
-  }
-  // Item -> (sequence-head, query tile). A tile's work grows with its index (its last
-  // position bounds its keys). Each (sequence, head) runs its heaviest tile first. With few
-  // tiles per CU (lpt), an XCD's items instead go longest first across all its heads: the
-  // k-th heaviest tile of each head before any head's (k+1)-th, so the CUs that finish a
-  // heavy tile take the light ones; head-by-head order can give one CU two heavy tiles.
-  int bh, qt;
-  const int n_run = a.qt_hi - a.qt_lo;
-  if (a.lpt) {
-    const int per_xcd = a.items / kNumXcd;
-    const int nbh_x = per_xcd / n_run;
-    const int x = item / per_xcd;
-    const int L = item - x * per_xcd;
-    const int k = L / nbh_x;
-    bh = x * nbh_x + (L - k * nbh_x);
-    qt = a.qt_hi - 1 - k;
-  } else {
-    bh = item / n_run;
-    qt = a.qt_hi - 1 - (item - bh * n_run);
-  }
-  const int b = bh / a.Hrun, h = a.h0 + bh - (bh / a.Hrun) * a.Hrun;
-  const int row0 = qt * BR;
+  const TileSel t = select_tile<PART>(a);
+  const int b = t.b, h = t.h, key_lo = t.key_lo, key_hi = t.key_hi;
+  const int row0 = t.qt * BR;
   int kv_end = (int)zigzag_pos(min(row0 + BR, a.rows) - 1, a.C, a.rank, a.D) + 1;
   int k_base = 0;  // position of the first key of stage 0
   if constexpr (PART) {
@@ -199,10 +319,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int wrow0 = row0 + wave * (32 * QB);
   const int wmin_pos = wrow0 < a.rows ? (int)zigzag_pos(wrow0, a.C, a.rank, a.D) : 0;
   const int64_t tok = (int64_t)a.H * HD;  // elements between consecutive tokens
-  const int64_t otok = (int64_t)a.oH * HD;  // the same in o32
-  const int oh = h - a.oh0;
 
-  // This lane's two query rows and their Q fragments (dims 16s + 8hl .. +7).
+  // This lane's query rows and their Q fragments (dims 16s + 8hl .. +7).
   int qi[QB], qpos[QB];
   bf16x8 qf[QB][KS];
 #pragma unroll
@@ -216,7 +334,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     for (int s = 0; s < KS; ++s)
       qf[qb][s] = valid ? as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s)) : bf16x8{};
   }
-#if TSP_ATTN_CINIT
   // Q * scale * log2(e), rounded to bf16 (round to nearest even): S comes out in log2 units.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
@@ -224,34 +341,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[qb][s][e] = (__bf16)((float)qf[qb][s][e] * a.scale_log2);
-#endif
 
   // A tile whose keys all lie outside the range: O = 0, lse = -inf, no LDS work (the whole
   // workgroup returns here, before any barrier).
   if constexpr (PART) {
     if (kv_end <= key_lo) {
-      // accumulate: the range adds nothing to these rows; only the bf16 O is written if asked
-      if (a.accumulate && a.o == nullptr) return;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (qi[qb] >= a.rows) continue;
-        const int64_t ro = ((int64_t)b * a.rows + qi[qb]) * tok + (int64_t)h * HD;
-        float* op = o32 + ((int64_t)b * a.prows + (qi[qb] - a.prow0)) * otok + (int64_t)oh * HD;
-#pragma unroll
-        for (int db = 0; db < HD / 32; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int dim = db * 32 + 8 * g + 4 * hl;
-            if (a.accumulate) {
-              const f32x4 v = *reinterpret_cast<const f32x4*>(op + dim);
-              *reinterpret_cast<uint2*>(a.o + ro + dim) = pack_bf16x4(v[0], v[1], v[2], v[3]);
-            } else {
-              *reinterpret_cast<f32x4*>(op + dim) = f32x4{};
-              if (a.o != nullptr) *reinterpret_cast<uint2*>(a.o + ro + dim) = make_uint2(0u, 0u);
-            }
-          }
-        if (!a.accumulate && hl == 0) lse32[((int64_t)b * a.oH + oh) * a.prows + (qi[qb] - a.prow0)] = -INFINITY;
-      }
+      store_no_keys<HD, QB>(a, t, qi, hl);
       return;
     }
   }
@@ -337,7 +432,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) m_at[qb] = m_cm[qb];
   };
-  const float c2 = a.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // K fragments of 32-key block kb (0/1) of a stage: 16 keys per lane group, dims of step s.
@@ -356,7 +450,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[qb][r] = TSP_ATTN_CINIT ? -m_cm[qb] : 0.0f;
+      for (int r = 0; r < 16; ++r) sacc[qb][r] = -m_cm[qb];
       sacc[qb] = mfma32x32x16(kf[0], qf[qb][0], sacc[qb]);
     }
 #pragma unroll
@@ -376,7 +470,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                       kstart + 8 * (r >> 2) + 4 * hl + (r & 3) >= key_hi)))
           sacc[qb][r] = -INFINITY;
   };
-#if TSP_ATTN_CINIT
   // sacc = s*c - m_at (m_at: the reference max the block was computed against). Row max;
   // in the rare case that the max grew by more than kLazy or the block was computed
   // against an older reference, shift it to the current reference (and move the reference
@@ -432,43 +525,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
     return any;
   };
-#else
-  // Row max, reference max, exponentials, bf16 P and their sum. Returns whether this lane
-  // needs the O rescale (then by the factors in alpha).
-  auto softmax = [&] __device__(f32x16 (&sacc)[QB], const float (&)[QB], bf16x8 (&pf)[QB][2],
-                                float (&alpha)[QB]) {
-    bool any = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = sacc[qb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[qb][r]);
-      mx = max_swap32(mx);
-      const float mxs = mx * c2;
-      const bool upd = mxs > m_s[qb] + kLazy;
-      const float m_new = upd ? mxs : m_s[qb];
-      alpha[qb] = __builtin_amdgcn_exp2f(m_s[qb] - m_new);
-      any |= upd;
-      m_s[qb] = m_new;
-      const float nm = -m_new;
-      float lsum = 0.0f;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][8 * half + 2 * e], c2, nm));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][8 * half + 2 * e + 1], c2, nm));
-          w[e] = pack_bf16x2(p0, p1);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, lsum, false);
-        }
-        pf[qb][half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-      }
-      l_run[qb] = __builtin_fmaf(l_run[qb], alpha[qb], lsum);
-    }
-    return any;
-  };
-#endif
   // Pins P and the row sums in registers at the end of the softmax, so the exponentials
   // cannot sink below the rescale branch into the PV region.
   auto close_region = [&] __device__(const bf16x8 (&pf)[QB][2]) {
@@ -562,72 +618,503 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     if (t + 3 < n_kt) body(t + 3, 3, 0, 2);
   }
 
-  float inv[QB];
+  store_rows<HD, QB, PART>(a, t, qi, oacc, m_s, l_run, hl);
+}
+
+// ------------------------------------------------------------------- head_dim 128 kernel
+// attn_fwd_w64: one wave per SIMD, 64 query rows per wave (two 32-row blocks that share every
+// K and V^T fragment read from LDS: half the LDS bytes per MFMA of a 32-row wave).
+// Registers: the O^T accumulators (2 x 4 x 16) sit in a0..a127 and the pre-scaled Q fragments
+// (2 x 8 x 4) in a128..a191, fixed AGPRs named only inside inline assembly (the MFMAs, the
+// zeroing, the rare rescale and the final read-out), so no compiler-placed copy ever moves
+// them; every such statement lists a0..a191 as clobbered, which keeps the compiler's own values
+// out of them. S of two key blocks, P of two key blocks and the K / V^T fragments stay in
+// VGPRs.
+// Per 32-key block j one pass issues 32 MFMAs, alternating the 16 of S_{j+1} = K Q^T with the
+// 16 of O^T += V^T P_{j-1}^T, and puts the softmax of S_j (row max, exponentials, bf16 P_j,
+// row sums) and the LDS reads of the next K and V^T fragments in fixed slots between them, so
+// the matrix core and the VALU work side by side within the one wave. P_{j-1} meets V_{j-1}
+// one pass late: the rescale of O^T for block j (when its max moved) follows the pass's last
+// PV MFMA, which is exactly when O^T holds blocks < j.
+// The compiler's hazard checks do not see into inline assembly, so the waits are explicit:
+// 2 wait states between a VALU write and an MFMA reading it (the S chains' start values, AGPR
+// writes before an MFMA), 12 between an MFMA and a VALU read of its result (S before the
+// softmax; O before a rescale or the read-out). A VALU or LDS write into an MFMA's A or B
+// operand right after the MFMA needs none.
+namespace w64 {
+constexpr int HD = 128, QB = 2, NW = 4, THREADS = 64 * NW;
+using L = Lay<HD, THREADS>;
+constexpr int kOReg = 0;    // O^T[qb][db] in a[kOReg + 16 (4 qb + db) .. +15]
+constexpr int kQReg = 128;  // Q[qb][ks] in a[kQReg + 4 (8 qb + ks) .. +3]
+}  // namespace w64
+
+#define TSP_STR(x) #x
+#define TSP_A10(p) TSP_STR(a##p##0), TSP_STR(a##p##1), TSP_STR(a##p##2), TSP_STR(a##p##3), TSP_STR(a##p##4), \
+    TSP_STR(a##p##5), TSP_STR(a##p##6), TSP_STR(a##p##7), TSP_STR(a##p##8), TSP_STR(a##p##9)
+// a0 .. a191
+#define TSP_AGPRS "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", TSP_A10(1), TSP_A10(2), TSP_A10(3), \
+    TSP_A10(4), TSP_A10(5), TSP_A10(6), TSP_A10(7), TSP_A10(8), TSP_A10(9), TSP_A10(10), TSP_A10(11), TSP_A10(12), \
+    TSP_A10(13), TSP_A10(14), TSP_A10(15), TSP_A10(16), TSP_A10(17), TSP_A10(18), "a190", "a191"
+
+// s += K-fragment x Q-fragment (Q in a[QR .. QR+3]); the first step of a chain also waits for
+// the VALU write of its start value.
+template <int QR>
+__device__ __forceinline__ void mma_s(f32x16& s, const bf16x8& k) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, a[%2:%3], %0" : "+v"(s) : "v"(k), "n"(QR), "n"(QR + 3) : TSP_AGPRS);
+}
+template <int QR>
+__device__ __forceinline__ void mma_s_first(f32x16& s, const bf16x8& k) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, a[%2:%3], %0" : "+v"(s) : "v"(k), "n"(QR), "n"(QR + 3)
+               : TSP_AGPRS);
+}
+// O^T in a[OR .. OR+15] += V^T-fragment x P-fragment.
+template <int OR>
+__device__ __forceinline__ void mma_pv(const bf16x8& v, const bf16x8& p) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 a[%2:%3], %0, %1, a[%2:%3]" ::"v"(v), "v"(p), "n"(OR), "n"(OR + 15)
+               : TSP_AGPRS);
+}
+// Q fragment into a[QR .. QR+3].
+template <int QR>
+__device__ __forceinline__ void q_to_agpr(const bf16x8& q) {
+  const uint4 u = __builtin_bit_cast(uint4, q);
+  asm volatile(
+      "v_accvgpr_write_b32 a[%4], %0\n\tv_accvgpr_write_b32 a[%5], %1\n\t"
+      "v_accvgpr_write_b32 a[%6], %2\n\tv_accvgpr_write_b32 a[%7], %3" ::"v"(u.x),
+      "v"(u.y), "v"(u.z), "v"(u.w), "n"(QR), "n"(QR + 1), "n"(QR + 2), "n"(QR + 3)
+      : TSP_AGPRS);
+}
+// a[R .. R+63] *= alpha (one query block's O^T), after the MFMAs that wrote them (16 wait
+// states), 2 wait states before an MFMA reads them again.
+template <int R>
+__device__ __forceinline__ void rescale_agprs(float alpha) {
+  float t;
+  asm volatile(
+      "s_nop 7\n\ts_nop 7\n\t"
+      ".set tsp_rr, %2\n\t"
+      ".rept 64\n\t"
+      "v_accvgpr_read_b32 %0, a[tsp_rr]\n\t"
+      "v_mul_f32 %0, %0, %1\n\t"
+      "v_accvgpr_write_b32 a[tsp_rr], %0\n\t"
+      ".set tsp_rr, tsp_rr + 1\n\t"
+      ".endr\n\t"
+      "s_nop 1"
+      : "=&v"(t)
+      : "v"(alpha), "n"(R)
+      : TSP_AGPRS);
+}
+// One O^T accumulator a[R .. R+15] read out (after the 16 wait states the caller provides).
+template <int R>
+__device__ __forceinline__ f32x16 read_agprs16(void) {
+  float x0, x1, x2, x3, x4, x5, x6, x7, x8, x9, x10, x11, x12, x13, x14, x15;
+  asm volatile(
+      "v_accvgpr_read_b32 %0, a[%16]\n\tv_accvgpr_read_b32 %1, a[%17]\n\tv_accvgpr_read_b32 %2, a[%18]\n\t"
+      "v_accvgpr_read_b32 %3, a[%19]\n\tv_accvgpr_read_b32 %4, a[%20]\n\tv_accvgpr_read_b32 %5, a[%21]\n\t"
+      "v_accvgpr_read_b32 %6, a[%22]\n\tv_accvgpr_read_b32 %7, a[%23]\n\tv_accvgpr_read_b32 %8, a[%24]\n\t"
+      "v_accvgpr_read_b32 %9, a[%25]\n\tv_accvgpr_read_b32 %10, a[%26]\n\tv_accvgpr_read_b32 %11, a[%27]\n\t"
+      "v_accvgpr_read_b32 %12, a[%28]\n\tv_accvgpr_read_b32 %13, a[%29]\n\tv_accvgpr_read_b32 %14, a[%30]\n\t"
+      "v_accvgpr_read_b32 %15, a[%31]"
+      : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3), "=v"(x4), "=v"(x5), "=v"(x6), "=v"(x7), "=v"(x8), "=v"(x9),
+        "=v"(x10), "=v"(x11), "=v"(x12), "=v"(x13), "=v"(x14), "=v"(x15)
+      : "n"(R), "n"(R + 1), "n"(R + 2), "n"(R + 3), "n"(R + 4), "n"(R + 5), "n"(R + 6), "n"(R + 7), "n"(R + 8),
+        "n"(R + 9), "n"(R + 10), "n"(R + 11), "n"(R + 12), "n"(R + 13), "n"(R + 14), "n"(R + 15)
+      : TSP_AGPRS);
+  return f32x16{x0, x1, x2, x3, x4, x5, x6, x7, x8, x9, x10, x11, x12, x13, x14, x15};
+}
+#define TSP_SB() __builtin_amdgcn_sched_barrier(0)
+
+template <bool PART>
+__global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_fwd_w64(AttnArgs a) {
+  constexpr int HD = w64::HD, QB = w64::QB, NW = w64::NW, OR = w64::kOReg, QR = w64::kQReg;
+  using L = w64::L;
+  constexpr int KS = L::KS, DB = L::DB, ROWB = L::ROWB, CPR = L::CPR, TILEB = L::TILEB, NDMA = L::NDMA;
+  __shared__ __attribute__((aligned(1024))) char kring[RING * TILEB];
+  __shared__ __attribute__((aligned(1024))) char vring[RING * TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+
+  const TileSel t = select_tile<PART>(a);
+  const int b = t.b, h = t.h, key_lo = t.key_lo, key_hi = t.key_hi;
+  const int row0 = t.qt * BR;
+  int kv_end = (int)zigzag_pos(min(row0 + BR, a.rows) - 1, a.C, a.rank, a.D) + 1;
+  int k_base = 0;  // position of the first key of stage 0
+  if constexpr (PART) {
+    kv_end = min(kv_end, key_hi);
+    k_base = (key_lo / BC) * BC;
+  }
+  const int n_kt = (kv_end - k_base + BC - 1) / BC;
+
+  const int wrow0 = row0 + wave * (32 * QB);
+  const int wmin_pos = wrow0 < a.rows ? (int)zigzag_pos(wrow0, a.C, a.rank, a.D) : 0;
+  const int64_t tok = (int64_t)a.H * HD;
+
+  // This lane's query rows; their Q fragments (dims 16s + 8hl .. +7), times scale*log2(e) and
+  // rounded to bf16 so that S comes out in log2 units, go to a[QR ..].
+  int qi[QB], qpos[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    inv[qb] = PART ? (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) : 1.0f / l_tot;
-    l_run[qb] = l_tot;
+    qi[qb] = wrow0 + 32 * qb + l32;
+    qpos[qb] = (int)zigzag_pos(qi[qb] < a.rows ? qi[qb] : a.rows - 1, a.C, a.rank, a.D);
   }
   if constexpr (PART) {
+    if (kv_end <= key_lo) {  // the whole workgroup returns here, before any barrier
+      store_no_keys<HD, QB>(a, t, qi, hl);
+      return;
+    }
+  }
+  {
+    bf16x8 qf[QB][KS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (qi[qb] >= a.rows) continue;
-      const int64_t ro = ((int64_t)b * a.rows + qi[qb]) * tok + (int64_t)h * HD;
-      float* op = o32 + ((int64_t)b * a.prows + (qi[qb] - a.prow0)) * otok + (int64_t)oh * HD;
-      float* lp = lse32 + ((int64_t)b * a.oH + oh) * a.prows + (qi[qb] - a.prow0);
-      const float lse_b = l_run[qb] > 0.0f ? (m_s[qb] + __log2f(l_run[qb])) * 0.69314718055994531f : -INFINITY;
-      // Overwrite: weights (0, 1). Accumulate: the log-sum-exp merge with what the
-      // accumulator holds (both lanes of the row read it before lane hl == 0 writes).
-      float wa = 0.0f, wb = 1.0f, lse_new = lse_b;
-      if (a.accumulate) {
-        const float lse_a = *lp;
-        const float mm = fmaxf(lse_a, lse_b);
-        wb = 0.0f;
-        if (mm != -INFINITY) {
-          wa = __expf(lse_a - mm);
-          wb = __expf(lse_b - mm);
-          const float z = wa + wb;
-          lse_new = mm + __logf(z);
-          wa /= z;
-          wb /= z;
-        }
-      }
+      const bool valid = qi[qb] < a.rows;
+      const bf16_t* qp = a.q + ((int64_t)b * a.rows + (valid ? qi[qb] : a.rows - 1)) * tok + (int64_t)h * HD + 8 * hl;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+      for (int s = 0; s < KS; ++s) {
+        qf[qb][s] = valid ? as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s)) : bf16x8{};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int dim = db * 32 + 8 * g + 4 * hl;
-          const f32x16& o = oacc[qb][db];
-          const float s = wb * inv[qb];
-          f32x4 val = {o[4 * g] * s, o[4 * g + 1] * s, o[4 * g + 2] * s, o[4 * g + 3] * s};
-          if (a.accumulate) val += wa * *reinterpret_cast<const f32x4*>(op + dim);
-          *reinterpret_cast<f32x4*>(op + dim) = val;
-          if (a.o != nullptr) *reinterpret_cast<uint2*>(a.o + ro + dim) = pack_bf16x4(val[0], val[1], val[2], val[3]);
-        }
+        for (int e = 0; e < 8; ++e) qf[qb][s][e] = (__bf16)((float)qf[qb][s][e] * a.scale_log2);
       }
-      if (hl == 0) *lp = lse_new;
     }
-    return;
+#define TSP_QW(qb, s) q_to_agpr<QR + 4 * (8 * (qb) + (s))>(qf[qb][s]);
+    TSP_QW(0, 0) TSP_QW(0, 1) TSP_QW(0, 2) TSP_QW(0, 3) TSP_QW(0, 4) TSP_QW(0, 5) TSP_QW(0, 6) TSP_QW(0, 7)
+    TSP_QW(1, 0) TSP_QW(1, 1) TSP_QW(1, 2) TSP_QW(1, 3) TSP_QW(1, 4) TSP_QW(1, 5) TSP_QW(1, 6) TSP_QW(1, 7)
+#undef TSP_QW
   }
+  // O^T = 0
+  asm volatile(
+      ".set tsp_rr, %0\n\t"
+      ".rept 128\n\t"
+      "v_accvgpr_write_b32 a[tsp_rr], 0\n\t"
+      ".set tsp_rr, tsp_rr + 1\n\t"
+      ".endr" ::"n"(OR)
+      : TSP_AGPRS);
+
+  // ---- stage loads (as in attn_fwd): global -> LDS, 16 bytes per lane; load p of this wave
+  // covers linear chunks (NW p + wave) * 64 + lane of a tile.
+  const char* kseq = reinterpret_cast<const char*>(a.k + (int64_t)b * a.S * tok + (int64_t)h * HD);
+  const char* vseq = reinterpret_cast<const char*>(a.v + (int64_t)b * a.S * tok + (int64_t)h * HD);
+  int drow[NDMA], dck[NDMA], dcv[NDMA];
+#pragma unroll
+  for (int p = 0; p < NDMA; ++p) {
+    const int lin = (NW * p + wave) * 64 + lane;
+    drow[p] = lin / CPR;
+    const int pc = lin % CPR;
+    dck[p] = 16 * (pc ^ L::fk(drow[p]));
+    dcv[p] = 16 * (pc ^ L::fv(drow[p]));
+  }
+  const uint32_t tokb = (uint32_t)(tok * 2);
+  auto issue = [&] __device__(int st, int tt) {
+    const int key0 = k_base + tt * BC;
+    const int lim = kv_end - 1 - key0;         // rows past the tile's last key repeat it (masked)
+    const int low = PART ? key_lo - key0 : 0;  // a key range's rows before key_lo repeat key_lo
+    const char* kb = kseq + (int64_t)key0 * tok * 2;
+    const char* vb = vseq + (int64_t)key0 * tok * 2;
+    const uint32_t lk = lds_addr(kring) + st * TILEB + wave * 1024;
+    const uint32_t lv = lds_addr(vring) + st * TILEB + wave * 1024;
+#pragma unroll
+    for (int p = 0; p < NDMA; ++p) {
+      const uint32_t roff = (uint32_t)(PART ? max(min(drow[p], lim), low) : min(drow[p], lim)) * tokb;
+      dma16_sbase(kb, roff + dck[p], lk + NW * p * 1024);
+      dma16_sbase(vb, roff + dcv[p], lv + NW * p * 1024);
+    }
+  };
+  // Stage u's buffer is read by the K fragment reads of body u-1 and the V^T fragment reads
+  // of body u, which the first pass of body u+1 consumes; so the barrier at the start of body
+  // u+2 is the first point where every wave is done with it, and body t refills the buffer of
+  // stage t-2 with stage t+2 (4-stage ring, loads one body ahead). At that barrier the only
+  // loads in flight are stage t+1's.
+  auto sync_all = [&] __device__(int in_flight_stages) {
+    if (in_flight_stages >= 1) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NDMA));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS read moves above the barrier
+  };
+
+  // ---- fragment addresses (as in attn_fwd)
+  int kaddr[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) kaddr[s] = l32 * ROWB + 16 * ((2 * s + hl) ^ L::fk(l32));
+  const int G = lane >> 4, j16 = lane & 15;
+  const lds_s16x4* vbase[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int r = 4 * hl + (j16 >> 2);
+    const int c = 4 * db + 2 * (G & 1) + ((j16 & 3) >> 1);
+    vbase[db] = (const lds_s16x4*)(vring + r * ROWB + 16 * (c ^ L::fv(r)) + 8 * (j16 & 1));
+  }
+  auto load_k1 = [&] __device__(int st, int kb, int s) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(kring + st * TILEB + kaddr[s] + kb * 32 * ROWB));
+  };
+  auto load_v1 = [&] __device__(int st, int kb, int half, int db) {
+    const lds_s16x4* vr = vbase[db] + (st * TILEB + (32 * kb + 16 * half) * ROWB) / 8;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vr);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr + ROWB));
+    const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+    return as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+  };
+
+  // Online softmax state in log2 units: m_s the running max, l_run this half-wave's share of
+  // the row sum, m_cm the value every newly started S chain subtracts (its start value is
+  // -m_cm), m_at the m_cm a buffer's chain started from.
+  float m_s[QB], l_run[QB], m_cm[QB], m_at_a[QB], m_at_b[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    if (qi[qb] >= a.rows) continue;
-    bf16_t* op = a.o + ((int64_t)b * a.rows + qi[qb]) * tok + (int64_t)h * HD;
+    m_s[qb] = -INFINITY;
+    l_run[qb] = 0.0f;
+    m_cm[qb] = m_at_a[qb] = m_at_b[qb] = 0.0f;
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto mask = [&] __device__(f32x16 (&sacc)[QB], int kstart) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dim = db * 32 + 8 * g + 4 * hl;
-        const f32x16& o = oacc[qb][db];
-        *reinterpret_cast<uint2*>(op + dim) =
-            pack_bf16x4(o[4 * g] * inv[qb], o[4 * g + 1] * inv[qb], o[4 * g + 2] * inv[qb], o[4 * g + 3] * inv[qb]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = kstart + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (key > qpos[qb] || (PART && (key < key_lo || key >= key_hi))) sacc[qb][r] = -INFINITY;
+      }
+  };
+
+  // MFMA slot i (0..31): even i is S of the next block, step ks = i / 4, query block
+  // (i / 2) % 2; odd i is PV of the previous block, half i / 16, dims block (i / 4) % 4, query
+  // block (i / 2) % 2. K (V^T) fragments are read again once both query blocks used them.
+#define TSP_MMA_S(i)                                                              \
+  if ((i) / 4 == 0) {                                                            \
+    mma_s_first<QR + 4 * (8 * (((i) / 2) % 2) + (i) / 4)>(sn[((i) / 2) % 2], kf[(i) / 4]); \
+  } else {                                                                       \
+    mma_s<QR + 4 * (8 * (((i) / 2) % 2) + (i) / 4)>(sn[((i) / 2) % 2], kf[(i) / 4]);       \
+  }                                                                              \
+  TSP_SB();
+#define TSP_MMA_PV(i)                                                                        \
+  mma_pv<OR + 16 * (4 * (((i) / 2) % 2) + ((i) / 4) % 4)>(vf[(i) / 16][((i) / 4) % 4],       \
+                                                         pp[((i) / 2) % 2][(i) / 16]);         \
+  TSP_SB();
+#define TSP_LOAD_K(i) kf[(i) / 4] = load_k1(kst, kkb, (i) / 4);
+#define TSP_LOAD_V(i) vf[(i) / 16][((i) / 4) % 4] = load_v1(vst, vkb, (i) / 16, ((i) / 4) % 4);
+
+  // ---- prologue: stages 0 and 1 in flight; S of block 0 once stage 0 has landed; K
+  // fragments of block 1.
+  issue(0, 0);
+  if (n_kt > 1) issue(1, 1);
+  sync_all(n_kt > 1 ? 1 : 0);
+  f32x16 sa[QB], sb[QB];        // S chains of alternate blocks
+  bf16x8 pa[QB][2], pb[QB][2];  // P of alternate blocks (two 16-key halves each)
+  bf16x8 kf[KS];                // K fragments of the block whose S the next pass computes
+  bf16x8 vf[2][DB];             // V^T fragments of the block whose PV the next pass computes
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    sa[qb] = f32x16{};
+    sb[qb] = f32x16{};
+    pb[qb][0] = pb[qb][1] = bf16x8{};  // the first pass's PV adds 0 (no block before block 0)
+  }
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vf[hh][db] = bf16x8{};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) kf[s] = load_k1(0, 0, s);
+  {
+    f32x16 (&sn)[QB] = sa;
+    TSP_MMA_S(0) TSP_MMA_S(2) TSP_MMA_S(4) TSP_MMA_S(6) TSP_MMA_S(8) TSP_MMA_S(10) TSP_MMA_S(12) TSP_MMA_S(14)
+    TSP_MMA_S(16) TSP_MMA_S(18) TSP_MMA_S(20) TSP_MMA_S(22) TSP_MMA_S(24) TSP_MMA_S(26) TSP_MMA_S(28) TSP_MMA_S(30)
+  }
+#pragma unroll
+  for (int s = 0; s < KS; ++s) kf[s] = load_k1(0, 1, s);
+
+  // ---- one pass: softmax of block j (S in sc, chain started from -m_at), S of block j+1
+  // into sn from kf, PV of block j-1 from vf and pp; kf <- K of block j+2 (stage kst, block
+  // kkb), vf <- V^T of block j (stage vst, block vkb); P of block j -> pc; then sc restarts
+  // as the chain of block j+2 from -m_cm.
+  auto pass = [&] __device__(int k0, f32x16 (&sc)[QB], f32x16 (&sn)[QB], float (&m_at)[QB],
+                             const bf16x8 (&pp)[QB][2], bf16x8 (&pc)[QB][2], int kst, int kkb, int vst,
+                             int vkb) __attribute__((always_inline)) {
+    TSP_SB();
+    asm volatile("s_nop 11");  // the MFMAs that wrote sc: 12 wait states before a VALU read
+    TSP_SB();
+    // causal mask where a key may follow a row; in a key range also at its two ends
+    if (k0 + 31 > wmin_pos || (PART && (k0 < key_lo || k0 + 32 > key_hi))) mask(sc, k0);
+    TSP_SB();
+    float tm[QB][5], mx[QB], alpha[QB], lsum[QB];
+    bool need = false, any = false;
+    uint32_t w[QB][2][4];
+    // slots 0-3: row max, three-way maxima
+    TSP_MMA_S(0)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      tm[qb][0] = fmaxf(fmaxf(sc[qb][0], sc[qb][1]), sc[qb][2]);
+      tm[qb][1] = fmaxf(fmaxf(sc[qb][3], sc[qb][4]), sc[qb][5]);
+    }
+    TSP_SB();
+    TSP_MMA_PV(1)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      tm[qb][2] = fmaxf(fmaxf(sc[qb][6], sc[qb][7]), sc[qb][8]);
+      tm[qb][3] = fmaxf(fmaxf(sc[qb][9], sc[qb][10]), sc[qb][11]);
+    }
+    TSP_SB();
+    TSP_MMA_S(2)
+    TSP_LOAD_K(2)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      tm[qb][4] = fmaxf(fmaxf(sc[qb][12], sc[qb][13]), sc[qb][14]);
+      tm[qb][0] = fmaxf(fmaxf(tm[qb][0], tm[qb][1]), tm[qb][2]);
+    }
+    TSP_SB();
+    TSP_MMA_PV(3)
+    TSP_LOAD_V(3)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = fmaxf(tm[qb][0], fmaxf(fmaxf(tm[qb][3], tm[qb][4]), sc[qb][15]));
+    asm volatile("" ::"v"(mx[0]), "v"(mx[1]));
+    TSP_SB();
+    // slots 4-5: the other half-wave's 16 keys of each row
+    TSP_MMA_S(4)
+    mx[0] = max_swap32(mx[0]);
+    TSP_SB();
+    TSP_MMA_PV(5)
+    mx[1] = max_swap32(mx[1]);
+    TSP_SB();
+    // slot 6: does the reference move? (lazy: only when the max grows by more than kLazy, or
+    // when the chain started from an older reference)
+    TSP_MMA_S(6)
+    TSP_LOAD_K(6)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float d = m_s[qb] - m_at[qb];
+      need |= (mx[qb] - d > kLazy) | (d != 0.0f);
+      alpha[qb] = 1.0f;
+      lsum[qb] = 0.0f;
+    }
+    TSP_SB();
+    TSP_MMA_PV(7)
+    TSP_LOAD_V(7)
+    TSP_SB();
+    if (__ballot(need)) {  // rare: shift the scores to the new reference
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float d = m_s[qb] - m_at[qb];
+        const bool upd = mx[qb] - d > kLazy;
+        const float m_new = upd ? m_at[qb] + mx[qb] : m_s[qb];
+        alpha[qb] = upd ? __builtin_amdgcn_exp2f(m_s[qb] - m_new) : 1.0f;  // 0 on the first block
+        // a row with no visible key so far keeps its scores (-inf) and reference
+        const float shift = m_new == -INFINITY ? 0.0f : m_new - m_at[qb];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[qb][r] -= shift;
+        l_run[qb] *= alpha[qb];
+        m_s[qb] = m_new;
+        if (upd) m_cm[qb] = m_new;
+        any |= upd;
       }
     }
-    if (a.lse != nullptr && hl == 0)
-      a.lse[((int64_t)b * a.H + h) * a.rows + qi[qb]] = (m_s[qb] + __log2f(l_run[qb])) * 0.69314718055994531f;
+    TSP_SB();
+    // slots 8-23: exponentials, bf16 P and the row sums, one key pair of one query block each
+#define TSP_EXP(i)                                                                           \
+  {                                                                                          \
+    constexpr int k_ = (i) - 8, qb_ = k_ % 2, hh_ = (k_ / 2) / 4, e_ = (k_ / 2) % 4;         \
+    const float p0 = __builtin_amdgcn_exp2f(sc[qb_][8 * hh_ + 2 * e_]);                     \
+    const float p1 = __builtin_amdgcn_exp2f(sc[qb_][8 * hh_ + 2 * e_ + 1]);                 \
+    w[qb_][hh_][e_] = pack_bf16x2(p0, p1);                                                   \
+    lsum[qb_] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[qb_][hh_][e_]), ones, lsum[qb_], false); \
+    asm volatile("" ::"v"(w[qb_][hh_][e_]), "v"(lsum[qb_]));  /* computed in this slot */    \
+  }                                                                                          \
+  TSP_SB();
+    TSP_MMA_S(8)   TSP_EXP(8)
+    TSP_MMA_PV(9)  TSP_EXP(9)
+    TSP_MMA_S(10)  TSP_LOAD_K(10) TSP_EXP(10)
+    TSP_MMA_PV(11) TSP_LOAD_V(11) TSP_EXP(11)
+    TSP_MMA_S(12)  TSP_EXP(12)
+    TSP_MMA_PV(13) TSP_EXP(13)
+    TSP_MMA_S(14)  TSP_LOAD_K(14) TSP_EXP(14)
+    TSP_MMA_PV(15) TSP_LOAD_V(15) TSP_EXP(15)
+    TSP_MMA_S(16)  TSP_EXP(16)
+    TSP_MMA_PV(17) TSP_EXP(17)
+    TSP_MMA_S(18)  TSP_LOAD_K(18) TSP_EXP(18)
+    TSP_MMA_PV(19) TSP_LOAD_V(19) TSP_EXP(19)
+    TSP_MMA_S(20)  TSP_EXP(20)
+    TSP_MMA_PV(21) TSP_EXP(21)
+    TSP_MMA_S(22)  TSP_LOAD_K(22) TSP_EXP(22)
+    TSP_MMA_PV(23) TSP_LOAD_V(23) TSP_EXP(23)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) pc[qb][hh] = as_bf16x8(make_uint4(w[qb][hh][0], w[qb][hh][1], w[qb][hh][2], w[qb][hh][3]));
+      l_run[qb] += lsum[qb];
+    }
+    // slots 24-31: sc restarts as the chain of block j+2, from -m_cm (4 values per slot)
+#define TSP_INIT(i)                                                                \
+  if ((i) == 24 || (i) == 28) {                                                    \
+    constexpr int q_ = ((i) - 24) / 4;                                             \
+    float start = -m_cm[q_];                                                       \
+    asm volatile("" : "+v"(start));  /* defined here, so the copies cannot rise */ \
+    for (int r = 0; r < 16; ++r) sc[q_][r] = start;                                \
+    asm volatile("" : "+v"(sc[q_]));  /* materialised in this slot */              \
+  }                                                                                \
+  TSP_SB();
+    TSP_MMA_S(24)  TSP_INIT(24)
+    TSP_MMA_PV(25) TSP_INIT(25)
+    TSP_MMA_S(26)  TSP_LOAD_K(26) TSP_INIT(26)
+    TSP_MMA_PV(27) TSP_LOAD_V(27) TSP_INIT(27)
+    TSP_MMA_S(28)  TSP_INIT(28)
+    TSP_MMA_PV(29) TSP_INIT(29)
+    TSP_MMA_S(30)  TSP_LOAD_K(30) TSP_INIT(30)
+    TSP_MMA_PV(31) TSP_LOAD_V(31) TSP_INIT(31)
+#undef TSP_EXP
+#undef TSP_INIT
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_at[qb] = m_cm[qb];
+    // O^T now holds the blocks before j: rescale it for block j's reference (rare)
+    if (__ballot(any)) {
+      rescale_agprs<OR>(alpha[0]);
+      rescale_agprs<OR + 64>(alpha[1]);
+    }
+    TSP_SB();
+  };
+
+  // ---- main loop: stage t holds blocks 2t and 2t+1; unrolled by the ring depth so every
+  // stage buffer is named statically.
+  auto body = [&] __device__(int tt, int cur, int nxt, int refill) __attribute__((always_inline)) {
+    sync_all(0);  // stage tt+1 landed; every wave is done with the buffer of stage tt-2
+    if (tt + 2 < n_kt) issue(refill, tt + 2);
+    const int k0 = k_base + tt * BC;
+    // block 2tt: S of 2tt+1 (kf: stage tt block 1), kf <- stage tt+1 block 0, vf <- stage tt block 0
+    pass(k0, sa, sb, m_at_a, pb, pa, nxt, 0, cur, 0);
+    // block 2tt+1: S of 2tt+2 (kf: stage tt+1 block 0, stale after the last stage: unused)
+    pass(k0 + 32, sb, sa, m_at_b, pa, pb, nxt, 1, cur, 1);
+  };
+  for (int tt = 0; tt < n_kt; tt += 4) {
+    body(tt, 0, 1, 2);
+    if (tt + 1 < n_kt) body(tt + 1, 1, 2, 3);
+    if (tt + 2 < n_kt) body(tt + 2, 2, 3, 0);
+    if (tt + 3 < n_kt) body(tt + 3, 3, 0, 1);
   }
+  // PV of the last block (its P in pb, its V^T fragments in vf)
+  {
+    const bf16x8 (&pp)[QB][2] = pb;
+    TSP_MMA_PV(1) TSP_MMA_PV(3) TSP_MMA_PV(5) TSP_MMA_PV(7) TSP_MMA_PV(9) TSP_MMA_PV(11) TSP_MMA_PV(13)
+    TSP_MMA_PV(15) TSP_MMA_PV(17) TSP_MMA_PV(19) TSP_MMA_PV(21) TSP_MMA_PV(23) TSP_MMA_PV(25) TSP_MMA_PV(27)
+    TSP_MMA_PV(29) TSP_MMA_PV(31)
+  }
+#undef TSP_MMA_S
+#undef TSP_MMA_PV
+#undef TSP_LOAD_K
+#undef TSP_LOAD_V
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // 16 wait states before O^T is read out
+  TSP_SB();
+  f32x16 oacc[QB][DB];
+  oacc[0][0] = read_agprs16<OR + 0>();
+  oacc[0][1] = read_agprs16<OR + 16>();
+  oacc[0][2] = read_agprs16<OR + 32>();
+  oacc[0][3] = read_agprs16<OR + 48>();
+  oacc[1][0] = read_agprs16<OR + 64>();
+  oacc[1][1] = read_agprs16<OR + 80>();
+  oacc[1][2] = read_agprs16<OR + 96>();
+  oacc[1][3] = read_agprs16<OR + 112>();
+  store_rows<HD, QB, PART>(a, t, qi, oacc, m_s, l_run, hl);
 }
+#undef TSP_SB
 
 }  // namespace
 
@@ -694,7 +1181,7 @@ hipError_t launch(const AttnArgs& a_in, int hd, hipStream_t stream) {
   AttnArgs a = a_in;
   a.lpt = !a.strided && a.split == 0 && a.items <= kLptMaxItems && a.items % (kNumXcd * (a.qt_hi - a.qt_lo)) == 0;
   if (hd == 128) {
-    hipLaunchKernelGGL((attn_fwd<128, PART>), dim3(a.items), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_w64<PART>), dim3(a.items), dim3(w64::THREADS), 0, stream, a);
   } else {
     hipLaunchKernelGGL((attn_fwd<64, PART>), dim3(a.items), dim3(kThreads), 0, stream, a);
   }
