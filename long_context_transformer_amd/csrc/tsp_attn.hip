@@ -663,8 +663,8 @@ __device__ __forceinline__ void mma_s(f32x16& s, const bf16x8& k) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, a[%2:%3], %0" : "+v"(s) : "v"(k), "n"(QR), "n"(QR + 3) : TSP_AGPRS);
 }
 template <int QR>
-__device__ __forceinline__ void mma_s_first(f32x16& s, const bf16x8& k) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, a[%2:%3], %0" : "+v"(s) : "v"(k), "n"(QR), "n"(QR + 3)
+__device__ __forceinline__ void mma_s_first(f32x16& s, const bf16x8& k, const f32x16& start) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, a[%2:%3], %4" : "=&v"(s) : "v"(k), "n"(QR), "n"(QR + 3), "v"(start)
                : TSP_AGPRS);
 }
 // O^T in a[OR .. OR+15] += V^T-fragment x P-fragment.
@@ -868,6 +868,11 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     l_run[qb] = 0.0f;
     m_cm[qb] = m_at_a[qb] = m_at_b[qb] = 0.0f;
   }
+  // Start value of every S chain: -m_cm in all 16 registers (the first MFMA of a chain reads it
+  // as its accumulator input; rewritten only when m_cm moves).
+  f32x16 start_t[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) start_t[qb] = f32x16{};
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   auto mask = [&] __device__(f32x16 (&sacc)[QB], int kstart) {
 #pragma unroll
@@ -884,7 +889,7 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
   // block (i / 2) % 2. K (V^T) fragments are read again once both query blocks used them.
 #define TSP_MMA_S(i)                                                              \
   if ((i) / 4 == 0) {                                                            \
-    mma_s_first<QR + 4 * (8 * (((i) / 2) % 2) + (i) / 4)>(sn[((i) / 2) % 2], kf[(i) / 4]); \
+    mma_s_first<QR + 4 * (8 * (((i) / 2) % 2) + (i) / 4)>(sn[((i) / 2) % 2], kf[(i) / 4], start_t[((i) / 2) % 2]); \
   } else {                                                                       \
     mma_s<QR + 4 * (8 * (((i) / 2) % 2) + (i) / 4)>(sn[((i) / 2) % 2], kf[(i) / 4]);       \
   }                                                                              \
@@ -1006,6 +1011,8 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
         l_run[qb] *= alpha[qb];
         m_s[qb] = m_new;
         if (upd) m_cm[qb] = m_new;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) start_t[qb][r] = -m_cm[qb];
         any |= upd;
       }
     }
@@ -1044,15 +1051,7 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
       l_run[qb] += lsum[qb];
     }
     // slots 24-31: sc restarts as the chain of block j+2, from -m_cm (4 values per slot)
-#define TSP_INIT(i)                                                                \
-  if ((i) == 24 || (i) == 28) {                                                    \
-    constexpr int q_ = ((i) - 24) / 4;                                             \
-    float start = -m_cm[q_];                                                       \
-    asm volatile("" : "+v"(start));  /* defined here, so the copies cannot rise */ \
-    for (int r = 0; r < 16; ++r) sc[q_][r] = start;                                \
-    asm volatile("" : "+v"(sc[q_]));  /* materialised in this slot */              \
-  }                                                                                \
-  TSP_SB();
+#define TSP_INIT(i) TSP_SB();
     TSP_MMA_S(24)  TSP_INIT(24)
     TSP_MMA_PV(25) TSP_INIT(25)
     TSP_MMA_S(26)  TSP_LOAD_K(26) TSP_INIT(26)
