@@ -208,20 +208,21 @@ __device__ __forceinline__ void store_no_keys(const AttnArgs& a, const TileSel& 
 
 // Normalise and store one wave's rows: QB blocks of 32 rows with O^T accumulators oacc[qb][db]
 // (lane l32 + 32 hl: query l32 of block qb, dims 32 db + 8 (r / 4) + 4 hl + r % 4 in register
-// r), running max m_s (log2 units) and this half-wave's share of the row sum in l_run.
+// r), running max m_s (log2 units) and the row sum in l_in: this half-wave's share, or with
+// L_WHOLE the whole row's sum in both half-waves.
 //   PART = false: bf16 O, and the log-sum-exp if a.lse is set.
 //   PART = true:  fp32 O and log-sum-exp of the range (overwrite), or their log-sum-exp merge
 //                 into the accumulator (accumulate); bf16 O too if a.o is set.
-template <int HD, int QB, bool PART>
+template <int HD, int QB, bool PART, bool L_WHOLE = false>
 __device__ __forceinline__ void store_rows(const AttnArgs& a, const TileSel& t, const int (&qi)[QB],
                                            const f32x16 (&oacc)[QB][HD / 32], const float (&m_s)[QB],
-                                           const float (&l_half)[QB], int hl) {
+                                           const float (&l_in)[QB], int hl) {
   constexpr int DB = HD / 32;
   const int64_t tok = (int64_t)a.H * HD;
   float inv[QB], l_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_half[qb] + __shfl_xor(l_half[qb], 32);
+    const float l_tot = L_WHOLE ? l_in[qb] : l_in[qb] + __shfl_xor(l_in[qb], 32);
     inv[qb] = PART ? (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) : 1.0f / l_tot;
     l_run[qb] = l_tot;
   }
@@ -631,11 +632,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 // out of them. S of two key blocks, P of two key blocks and the K / V^T fragments stay in
 // VGPRs.
 // Per 32-key block j one pass issues 32 MFMAs, alternating the 16 of S_{j+1} = K Q^T with the
-// 16 of O^T += V^T P_{j-1}^T, and puts the softmax of S_j (row max, exponentials, bf16 P_j,
-// row sums) and the LDS reads of the next K and V^T fragments in fixed slots between them, so
-// the matrix core and the VALU work side by side within the one wave. P_{j-1} meets V_{j-1}
-// one pass late: the rescale of O^T for block j (when its max moved) follows the pass's last
-// PV MFMA, which is exactly when O^T holds blocks < j.
+// 16 of O^T += V^T P_{j-1}^T, and puts the softmax of S_j (row max, exponentials, bf16 P_j)
+// and the LDS reads of the next K and V^T fragments in fixed slots between them, so the
+// matrix core and the VALU work side by side within the one wave. The row sums of P_{j-1}
+// come from four small MFMAs beside its PV (mma_rowsum), not from the VALU. P_{j-1} meets
+// V_{j-1} one pass late: the rescale of O^T and the row sums for block j (when its max moved)
+// follows the pass's last PV MFMA, which is exactly when both hold blocks < j.
 // The compiler's hazard checks do not see into inline assembly, so the waits are explicit:
 // 2 wait states between a VALU write and an MFMA reading it (the S chains' start values, AGPR
 // writes before an MFMA), 12 between an MFMA and a VALU read of its result (S before the
@@ -646,15 +648,16 @@ constexpr int HD = 128, QB = 2, NW = 4, THREADS = 64 * NW;
 using L = Lay<HD, THREADS>;
 constexpr int kOReg = 0;    // O^T[qb][db] in a[kOReg + 16 (4 qb + db) .. +15]
 constexpr int kQReg = 128;  // Q[qb][ks] in a[kQReg + 4 (8 qb + ks) .. +3]
+constexpr int kLReg = 192;  // row sums of query block qb in a[kLReg + 4 qb] (a[.. + 1 .. 3] stay 0)
 }  // namespace w64
 
 #define TSP_STR(x) #x
 #define TSP_A10(p) TSP_STR(a##p##0), TSP_STR(a##p##1), TSP_STR(a##p##2), TSP_STR(a##p##3), TSP_STR(a##p##4), \
     TSP_STR(a##p##5), TSP_STR(a##p##6), TSP_STR(a##p##7), TSP_STR(a##p##8), TSP_STR(a##p##9)
-// a0 .. a191
+// a0 .. a199
 #define TSP_AGPRS "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", TSP_A10(1), TSP_A10(2), TSP_A10(3), \
     TSP_A10(4), TSP_A10(5), TSP_A10(6), TSP_A10(7), TSP_A10(8), TSP_A10(9), TSP_A10(10), TSP_A10(11), TSP_A10(12), \
-    TSP_A10(13), TSP_A10(14), TSP_A10(15), TSP_A10(16), TSP_A10(17), TSP_A10(18), "a190", "a191"
+    TSP_A10(13), TSP_A10(14), TSP_A10(15), TSP_A10(16), TSP_A10(17), TSP_A10(18), TSP_A10(19)
 
 // s += K-fragment x Q-fragment (Q in a[QR .. QR+3]); the first step of a chain also waits for
 // the VALU write of its start value.
@@ -672,6 +675,48 @@ template <int OR>
 __device__ __forceinline__ void mma_pv(const bf16x8& v, const bf16x8& p) {
   asm volatile("v_mfma_f32_32x32x16_bf16 a[%2:%3], %0, %1, a[%2:%3]" ::"v"(v), "v"(p), "n"(OR), "n"(OR + 15)
                : TSP_AGPRS);
+}
+// Row sums on the matrix core: a[LR .. LR+3] += Sel x P-fragment with a 16x16x32 MFMA. P's
+// B-operand layout for the 32x32x16 MFMA puts query l % 32, keys of group l / 32, in lane l;
+// read as the B operand of the 16x16x32 MFMA, column n gathers lanes n, n+16, n+32, n+48, that
+// is query n (k groups 0 and 2) and query n+16 (k groups 1 and 3). Sel (lane_sel) holds ones
+// in rows 0 and 8 over k groups 0, 2 and in rows 4 and 12 over k groups 1, 3, zeros elsewhere;
+// so output row 4 g of column n, which lane 16 g + n holds in its first register, is the sum
+// of that lane's own query's 16 P values, and the other three registers stay zero. The
+// products are exact (P times 1 or 0), so this adds the same bf16 values that enter O^T.
+template <int LR>
+__device__ __forceinline__ void mma_rowsum(const bf16x8& sel, const bf16x8& p) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 a[%2:%3], %0, %1, a[%2:%3]" ::"v"(sel), "v"(p), "n"(LR), "n"(LR + 3)
+               : TSP_AGPRS);
+}
+__device__ __forceinline__ bf16x8 lane_sel(int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  const bool on = (g & 1) ? (r == 4 || r == 12) : (r == 0 || r == 8);
+  const uint32_t w = on ? 0x3f803f80u : 0u;
+  return as_bf16x8(make_uint4(w, w, w, w));
+}
+// Both query blocks' row sums a[LR], a[LR + 4] times their alpha; for use after the O^T
+// rescale (which provides the wait after the MFMAs), 2 wait states before an MFMA reads them.
+template <int LR>
+__device__ __forceinline__ void rescale_rowsums(float alpha0, float alpha1) {
+  float t0, t1;
+  asm volatile(
+      "v_accvgpr_read_b32 %0, a[%4]\n\t"
+      "v_accvgpr_read_b32 %1, a[%5]\n\t"
+      "v_mul_f32 %0, %0, %2\n\t"
+      "v_mul_f32 %1, %1, %3\n\t"
+      "v_accvgpr_write_b32 a[%4], %0\n\t"
+      "v_accvgpr_write_b32 a[%5], %1\n\t"
+      "s_nop 1"
+      : "=&v"(t0), "=&v"(t1)
+      : "v"(alpha0), "v"(alpha1), "n"(LR), "n"(LR + 4)
+      : TSP_AGPRS);
+}
+template <int R>
+__device__ __forceinline__ float read_agpr(void) {
+  float x;
+  asm volatile("v_accvgpr_read_b32 %0, a[%1]" : "=v"(x) : "n"(R) : TSP_AGPRS);
+  return x;
 }
 // Q fragment into a[QR .. QR+3].
 template <int QR>
@@ -724,7 +769,7 @@ __device__ __forceinline__ f32x16 read_agprs16(void) {
 
 template <bool PART>
 __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_fwd_w64(AttnArgs a) {
-  constexpr int HD = w64::HD, QB = w64::QB, NW = w64::NW, OR = w64::kOReg, QR = w64::kQReg;
+  constexpr int HD = w64::HD, QB = w64::QB, NW = w64::NW, OR = w64::kOReg, QR = w64::kQReg, LR = w64::kLReg;
   using L = w64::L;
   constexpr int KS = L::KS, DB = L::DB, ROWB = L::ROWB, CPR = L::CPR, TILEB = L::TILEB, NDMA = L::NDMA;
   __shared__ __attribute__((aligned(1024))) char kring[RING * TILEB];
@@ -782,14 +827,20 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     TSP_QW(1, 0) TSP_QW(1, 1) TSP_QW(1, 2) TSP_QW(1, 3) TSP_QW(1, 4) TSP_QW(1, 5) TSP_QW(1, 6) TSP_QW(1, 7)
 #undef TSP_QW
   }
-  // O^T = 0
+  // O^T = 0, row sums = 0
   asm volatile(
       ".set tsp_rr, %0\n\t"
       ".rept 128\n\t"
       "v_accvgpr_write_b32 a[tsp_rr], 0\n\t"
       ".set tsp_rr, tsp_rr + 1\n\t"
-      ".endr" ::"n"(OR)
+      ".endr\n\t"
+      ".set tsp_rr, %1\n\t"
+      ".rept 8\n\t"
+      "v_accvgpr_write_b32 a[tsp_rr], 0\n\t"
+      ".set tsp_rr, tsp_rr + 1\n\t"
+      ".endr" ::"n"(OR), "n"(LR)
       : TSP_AGPRS);
+  const bf16x8 lsel = lane_sel(lane);
 
   // ---- stage loads (as in attn_fwd): global -> LDS, 16 bytes per lane; load p of this wave
   // covers linear chunks (NW p + wave) * 64 + lane of a tile.
@@ -858,14 +909,13 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     return as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
   };
 
-  // Online softmax state in log2 units: m_s the running max, l_run this half-wave's share of
-  // the row sum, m_cm the value every newly started S chain subtracts (its start value is
-  // -m_cm), m_at the m_cm a buffer's chain started from.
-  float m_s[QB], l_run[QB], m_cm[QB], m_at_a[QB], m_at_b[QB];
+  // Online softmax state in log2 units: m_s the running max (the row sums, relative to it,
+  // live in a[LR ..]), m_cm the value every newly started S chain subtracts (its start value
+  // is -m_cm), m_at the m_cm a buffer's chain started from.
+  float m_s[QB], m_cm[QB], m_at_a[QB], m_at_b[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_s[qb] = -INFINITY;
-    l_run[qb] = 0.0f;
     m_cm[qb] = m_at_a[qb] = m_at_b[qb] = 0.0f;
   }
   // Start value of every S chain: -m_cm in all 16 registers (the first MFMA of a chain reads it
@@ -873,7 +923,6 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
   f32x16 start_t[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) start_t[qb] = f32x16{};
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   auto mask = [&] __device__(f32x16 (&sacc)[QB], int kstart) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -897,6 +946,10 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
 #define TSP_MMA_PV(i)                                                                        \
   mma_pv<OR + 16 * (4 * (((i) / 2) % 2) + ((i) / 4) % 4)>(vf[(i) / 16][((i) / 4) % 4],       \
                                                          pp[((i) / 2) % 2][(i) / 16]);         \
+  TSP_SB();
+// Row sums of the previous block, with its PV: query block qb, key half hh.
+#define TSP_MMA_L(qb, hh)                       \
+  mma_rowsum<LR + 4 * (qb)>(lsel, pp[qb][hh]); \
   TSP_SB();
 #define TSP_LOAD_K(i) kf[(i) / 4] = load_k1(kst, kkb, (i) / 4);
 #define TSP_LOAD_V(i) vf[(i) / 16][((i) / 4) % 4] = load_v1(vst, vkb, (i) / 16, ((i) / 4) % 4);
@@ -943,7 +996,7 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     // causal mask where a key may follow a row; in a key range also at its two ends
     if (k0 + 31 > wmin_pos || (PART && (k0 < key_lo || k0 + 32 > key_hi))) mask(sc, k0);
     TSP_SB();
-    float tm[QB][5], mx[QB], alpha[QB], lsum[QB];
+    float tm[QB][5], mx[QB], alpha[QB];
     bool need = false, any = false;
     uint32_t w[QB][2][4];
     // slots 0-3: row max, three-way maxima
@@ -991,12 +1044,11 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
       const float d = m_s[qb] - m_at[qb];
       need |= (mx[qb] - d > kLazy) | (d != 0.0f);
       alpha[qb] = 1.0f;
-      lsum[qb] = 0.0f;
     }
     TSP_SB();
     TSP_MMA_PV(7)
     TSP_LOAD_V(7)
-    TSP_SB();
+    TSP_MMA_L(0, 0)
     if (__ballot(need)) {  // rare: shift the scores to the new reference
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -1008,7 +1060,6 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
         const float shift = m_new == -INFINITY ? 0.0f : m_new - m_at[qb];
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[qb][r] -= shift;
-        l_run[qb] *= alpha[qb];
         m_s[qb] = m_new;
         if (upd) m_cm[qb] = m_new;
 #pragma unroll
@@ -1017,16 +1068,15 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
       }
     }
     TSP_SB();
-    // slots 8-23: exponentials, bf16 P and the row sums, one key pair of one query block each
-#define TSP_EXP(i)                                                                           \
-  {                                                                                          \
-    constexpr int k_ = (i) - 8, qb_ = k_ % 2, hh_ = (k_ / 2) / 4, e_ = (k_ / 2) % 4;         \
-    const float p0 = __builtin_amdgcn_exp2f(sc[qb_][8 * hh_ + 2 * e_]);                     \
-    const float p1 = __builtin_amdgcn_exp2f(sc[qb_][8 * hh_ + 2 * e_ + 1]);                 \
-    w[qb_][hh_][e_] = pack_bf16x2(p0, p1);                                                   \
-    lsum[qb_] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[qb_][hh_][e_]), ones, lsum[qb_], false); \
-    asm volatile("" ::"v"(w[qb_][hh_][e_]), "v"(lsum[qb_]));  /* computed in this slot */    \
-  }                                                                                          \
+    // slots 8-23: exponentials and bf16 P, one key pair of one query block each
+#define TSP_EXP(i)                                                                   \
+  {                                                                                  \
+    constexpr int k_ = (i) - 8, qb_ = k_ % 2, hh_ = (k_ / 2) / 4, e_ = (k_ / 2) % 4; \
+    const float p0 = __builtin_amdgcn_exp2f(sc[qb_][8 * hh_ + 2 * e_]);             \
+    const float p1 = __builtin_amdgcn_exp2f(sc[qb_][8 * hh_ + 2 * e_ + 1]);         \
+    w[qb_][hh_][e_] = pack_bf16x2(p0, p1);                                           \
+    asm volatile("" ::"v"(w[qb_][hh_][e_])); /* computed in this slot */             \
+  }                                                                                  \
   TSP_SB();
     TSP_MMA_S(8)   TSP_EXP(8)
     TSP_MMA_PV(9)  TSP_EXP(9)
@@ -1035,7 +1085,7 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     TSP_MMA_S(12)  TSP_EXP(12)
     TSP_MMA_PV(13) TSP_EXP(13)
     TSP_MMA_S(14)  TSP_LOAD_K(14) TSP_EXP(14)
-    TSP_MMA_PV(15) TSP_LOAD_V(15) TSP_EXP(15)
+    TSP_MMA_PV(15) TSP_LOAD_V(15) TSP_MMA_L(1, 0) TSP_EXP(15)
     TSP_MMA_S(16)  TSP_EXP(16)
     TSP_MMA_PV(17) TSP_EXP(17)
     TSP_MMA_S(18)  TSP_LOAD_K(18) TSP_EXP(18)
@@ -1043,12 +1093,11 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     TSP_MMA_S(20)  TSP_EXP(20)
     TSP_MMA_PV(21) TSP_EXP(21)
     TSP_MMA_S(22)  TSP_LOAD_K(22) TSP_EXP(22)
-    TSP_MMA_PV(23) TSP_LOAD_V(23) TSP_EXP(23)
+    TSP_MMA_PV(23) TSP_LOAD_V(23) TSP_MMA_L(0, 1) TSP_EXP(23)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) pc[qb][hh] = as_bf16x8(make_uint4(w[qb][hh][0], w[qb][hh][1], w[qb][hh][2], w[qb][hh][3]));
-      l_run[qb] += lsum[qb];
     }
     // slots 24-31: sc restarts as the chain of block j+2, from -m_cm (4 values per slot)
 #define TSP_INIT(i) TSP_SB();
@@ -1059,7 +1108,7 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     TSP_MMA_S(28)  TSP_INIT(28)
     TSP_MMA_PV(29) TSP_INIT(29)
     TSP_MMA_S(30)  TSP_LOAD_K(30) TSP_INIT(30)
-    TSP_MMA_PV(31) TSP_LOAD_V(31) TSP_INIT(31)
+    TSP_MMA_PV(31) TSP_LOAD_V(31) TSP_MMA_L(1, 1) TSP_INIT(31)
 #undef TSP_EXP
 #undef TSP_INIT
 #pragma unroll
@@ -1068,6 +1117,7 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     if (__ballot(any)) {
       rescale_agprs<OR>(alpha[0]);
       rescale_agprs<OR + 64>(alpha[1]);
+      rescale_rowsums<LR>(alpha[0], alpha[1]);
     }
     TSP_SB();
   };
@@ -1095,9 +1145,11 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     TSP_MMA_PV(1) TSP_MMA_PV(3) TSP_MMA_PV(5) TSP_MMA_PV(7) TSP_MMA_PV(9) TSP_MMA_PV(11) TSP_MMA_PV(13)
     TSP_MMA_PV(15) TSP_MMA_PV(17) TSP_MMA_PV(19) TSP_MMA_PV(21) TSP_MMA_PV(23) TSP_MMA_PV(25) TSP_MMA_PV(27)
     TSP_MMA_PV(29) TSP_MMA_PV(31)
+    TSP_MMA_L(0, 0) TSP_MMA_L(1, 0) TSP_MMA_L(0, 1) TSP_MMA_L(1, 1)
   }
 #undef TSP_MMA_S
 #undef TSP_MMA_PV
+#undef TSP_MMA_L
 #undef TSP_LOAD_K
 #undef TSP_LOAD_V
   asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // 16 wait states before O^T is read out
@@ -1111,7 +1163,8 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
   oacc[1][1] = read_agprs16<OR + 80>();
   oacc[1][2] = read_agprs16<OR + 96>();
   oacc[1][3] = read_agprs16<OR + 112>();
-  store_rows<HD, QB, PART>(a, t, qi, oacc, m_s, l_run, hl);
+  const float l_row[QB] = {read_agpr<LR>(), read_agpr<LR + 4>()};
+  store_rows<HD, QB, PART, true>(a, t, qi, oacc, m_s, l_row, hl);
 }
 #undef TSP_SB
 
