@@ -177,6 +177,24 @@ __device__ __forceinline__ TileSel select_tile(const AttnArgs& a) {
   return t;
 }
 
+// A TileSel with every field read from the first lane (all lanes hold the same values).
+__device__ __forceinline__ TileSel uniform_tile(const TileSel& v) {
+  auto u = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  auto up = [&](float* p) {
+    const uint64_t x = (uint64_t)(uintptr_t)p;
+    return (float*)(uintptr_t)(((uint64_t)(uint32_t)u((int)(uint32_t)(x >> 32)) << 32) | (uint32_t)u((int)(uint32_t)x));
+  };
+  TileSel t;
+  t.b = u(v.b);
+  t.h = u(v.h);
+  t.qt = u(v.qt);
+  t.key_lo = u(v.key_lo);
+  t.key_hi = u(v.key_hi);
+  t.o32 = up(v.o32);
+  t.lse32 = up(v.lse32);
+  return t;
+}
+
 // Key-range attention, a tile whose keys all lie outside the range: O = 0 and lse = -inf for
 // its rows (accumulate: the range adds nothing; only the bf16 O is written if asked).
 template <int HD, int QB>
@@ -780,10 +798,13 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
 
-  const TileSel t = select_tile<PART>(a);
+  // The tile's indices come out of integer divisions, which the compiler leaves in VGPRs;
+  // they are the same in every lane, so they are moved to SGPRs: the per-stage addresses,
+  // loop bounds and mask tests then run on the scalar unit.
+  const TileSel t = uniform_tile(select_tile<PART>(a));
   const int b = t.b, h = t.h, key_lo = t.key_lo, key_hi = t.key_hi;
   const int row0 = t.qt * BR;
-  int kv_end = (int)zigzag_pos(min(row0 + BR, a.rows) - 1, a.C, a.rank, a.D) + 1;
+  int kv_end = __builtin_amdgcn_readfirstlane((int)zigzag_pos(min(row0 + BR, a.rows) - 1, a.C, a.rank, a.D) + 1);
   int k_base = 0;  // position of the first key of stage 0
   if constexpr (PART) {
     kv_end = min(kv_end, key_hi);
@@ -792,7 +813,8 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
   const int n_kt = (kv_end - k_base + BC - 1) / BC;
 
   const int wrow0 = row0 + wave * (32 * QB);
-  const int wmin_pos = wrow0 < a.rows ? (int)zigzag_pos(wrow0, a.C, a.rank, a.D) : 0;
+  const int wmin_pos =
+      __builtin_amdgcn_readfirstlane(wrow0 < a.rows ? (int)zigzag_pos(wrow0, a.C, a.rank, a.D) : 0);
   const int64_t tok = (int64_t)a.H * HD;
 
   // This lane's query rows; their Q fragments (dims 16s + 8hl .. +7), times scale*log2(e) and
@@ -846,16 +868,24 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
   // covers linear chunks (NW p + wave) * 64 + lane of a tile.
   const char* kseq = reinterpret_cast<const char*>(a.k + (int64_t)b * a.S * tok + (int64_t)h * HD);
   const char* vseq = reinterpret_cast<const char*>(a.v + (int64_t)b * a.S * tok + (int64_t)h * HD);
-  int drow[NDMA], dck[NDMA], dcv[NDMA];
+  // Load p of a lane covers tile row drow, 16-byte column chunk pc (stored swizzled); in a
+  // tile whose rows are all keys of the range its source offsets are fixed (voffk, voffv).
+  const uint32_t tokb = (uint32_t)(tok * 2);
+  auto dma_slot = [&] __device__(int p, int& drow, int& dck, int& dcv) {
+    const int lin = (NW * p + wave) * 64 + lane;
+    drow = lin / CPR;
+    const int pc = lin % CPR;
+    dck = 16 * (pc ^ L::fk(drow));
+    dcv = 16 * (pc ^ L::fv(drow));
+  };
+  uint32_t voffk[NDMA], voffv[NDMA];
 #pragma unroll
   for (int p = 0; p < NDMA; ++p) {
-    const int lin = (NW * p + wave) * 64 + lane;
-    drow[p] = lin / CPR;
-    const int pc = lin % CPR;
-    dck[p] = 16 * (pc ^ L::fk(drow[p]));
-    dcv[p] = 16 * (pc ^ L::fv(drow[p]));
+    int drow, dck, dcv;
+    dma_slot(p, drow, dck, dcv);
+    voffk[p] = (uint32_t)drow * tokb + dck;
+    voffv[p] = (uint32_t)drow * tokb + dcv;
   }
-  const uint32_t tokb = (uint32_t)(tok * 2);
   auto issue = [&] __device__(int st, int tt) {
     const int key0 = k_base + tt * BC;
     const int lim = kv_end - 1 - key0;         // rows past the tile's last key repeat it (masked)
@@ -864,11 +894,21 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     const char* vb = vseq + (int64_t)key0 * tok * 2;
     const uint32_t lk = lds_addr(kring) + st * TILEB + wave * 1024;
     const uint32_t lv = lds_addr(vring) + st * TILEB + wave * 1024;
+    if (lim >= BC - 1 && low <= 0) {
 #pragma unroll
-    for (int p = 0; p < NDMA; ++p) {
-      const uint32_t roff = (uint32_t)(PART ? max(min(drow[p], lim), low) : min(drow[p], lim)) * tokb;
-      dma16_sbase(kb, roff + dck[p], lk + NW * p * 1024);
-      dma16_sbase(vb, roff + dcv[p], lv + NW * p * 1024);
+      for (int p = 0; p < NDMA; ++p) {
+        dma16_sbase(kb, voffk[p], lk + NW * p * 1024);
+        dma16_sbase(vb, voffv[p], lv + NW * p * 1024);
+      }
+    } else {  // the last tile, or the first of a key range: clamp the rows
+#pragma unroll
+      for (int p = 0; p < NDMA; ++p) {
+        int drow, dck, dcv;
+        dma_slot(p, drow, dck, dcv);
+        const uint32_t roff = (uint32_t)(PART ? max(min(drow, lim), low) : min(drow, lim)) * tokb;
+        dma16_sbase(kb, roff + dck, lk + NW * p * 1024);
+        dma16_sbase(vb, roff + dcv, lv + NW * p * 1024);
+      }
     }
   };
   // Stage u's buffer is read by the K fragment reads of body u-1 and the V^T fragment reads
