@@ -953,6 +953,11 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
   // live in a[LR ..]), m_cm the value every newly started S chain subtracts (its start value
   // is -m_cm), m_at the m_cm a buffer's chain started from.
   float m_s[QB], m_cm[QB], m_at_a[QB], m_at_b[QB];
+  // Wave-wide flags: some row has seen no key yet (its m_s is -inf while its chains start from
+  // 0), and the block about to be processed was started before the last reference move. When
+  // both are clear, every row's chain started from its current reference, so the scores of a
+  // block are already relative to m_s and the lazy test is just "a score above kLazy".
+  bool unseen = true, stale = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_s[qb] = -INFINITY;
@@ -1039,57 +1044,54 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     float tm[QB][5], mx[QB], alpha[QB];
     bool need = false, any = false;
     uint32_t w[QB][2][4];
-    // slots 0-3: row max, three-way maxima
+    // slots 0-5: this half-wave's max of each row (16 of its 32 keys), three-way maxima
     TSP_MMA_S(0)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      tm[qb][0] = fmaxf(fmaxf(sc[qb][0], sc[qb][1]), sc[qb][2]);
-      tm[qb][1] = fmaxf(fmaxf(sc[qb][3], sc[qb][4]), sc[qb][5]);
-    }
+    tm[0][0] = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
+    tm[0][1] = fmaxf(fmaxf(sc[0][3], sc[0][4]), sc[0][5]);
+    tm[0][2] = fmaxf(fmaxf(sc[0][6], sc[0][7]), sc[0][8]);
     TSP_SB();
     TSP_MMA_PV(1)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      tm[qb][2] = fmaxf(fmaxf(sc[qb][6], sc[qb][7]), sc[qb][8]);
-      tm[qb][3] = fmaxf(fmaxf(sc[qb][9], sc[qb][10]), sc[qb][11]);
-    }
+    tm[0][3] = fmaxf(fmaxf(sc[0][9], sc[0][10]), sc[0][11]);
+    tm[0][4] = fmaxf(fmaxf(sc[0][12], sc[0][13]), sc[0][14]);
+    tm[1][0] = fmaxf(fmaxf(sc[1][0], sc[1][1]), sc[1][2]);
     TSP_SB();
     TSP_MMA_S(2)
     TSP_LOAD_K(2)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      tm[qb][4] = fmaxf(fmaxf(sc[qb][12], sc[qb][13]), sc[qb][14]);
-      tm[qb][0] = fmaxf(fmaxf(tm[qb][0], tm[qb][1]), tm[qb][2]);
-    }
+    tm[1][1] = fmaxf(fmaxf(sc[1][3], sc[1][4]), sc[1][5]);
+    tm[1][2] = fmaxf(fmaxf(sc[1][6], sc[1][7]), sc[1][8]);
+    tm[1][3] = fmaxf(fmaxf(sc[1][9], sc[1][10]), sc[1][11]);
     TSP_SB();
     TSP_MMA_PV(3)
     TSP_LOAD_V(3)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mx[qb] = fmaxf(tm[qb][0], fmaxf(fmaxf(tm[qb][3], tm[qb][4]), sc[qb][15]));
-    asm volatile("" ::"v"(mx[0]), "v"(mx[1]));
+    tm[1][4] = fmaxf(fmaxf(sc[1][12], sc[1][13]), sc[1][14]);
+    tm[0][0] = fmaxf(fmaxf(tm[0][0], tm[0][1]), tm[0][2]);
+    tm[0][3] = fmaxf(fmaxf(tm[0][3], tm[0][4]), sc[0][15]);
+    asm volatile("" ::"v"(tm[1][4]), "v"(tm[0][0]), "v"(tm[0][3]));
     TSP_SB();
-    // slots 4-5: the other half-wave's 16 keys of each row
     TSP_MMA_S(4)
-    mx[0] = max_swap32(mx[0]);
+    tm[1][0] = fmaxf(fmaxf(tm[1][0], tm[1][1]), tm[1][2]);
+    tm[1][3] = fmaxf(fmaxf(tm[1][3], tm[1][4]), sc[1][15]);
+    mx[0] = fmaxf(tm[0][0], tm[0][3]);
+    asm volatile("" ::"v"(tm[1][0]), "v"(tm[1][3]), "v"(mx[0]));
     TSP_SB();
     TSP_MMA_PV(5)
-    mx[1] = max_swap32(mx[1]);
+    mx[1] = fmaxf(tm[1][0], tm[1][3]);
+    asm volatile("" ::"v"(mx[1]));
     TSP_SB();
-    // slot 6: does the reference move? (lazy: only when the max grows by more than kLazy, or
-    // when the chain started from an older reference)
+    // slot 6: does some row's reference move? With unseen and stale clear, only when one of
+    // its scores exceeds kLazy (the half-wave maxima suffice: the row max exceeds kLazy iff
+    // one half does); otherwise the branch takes the exact per-row test.
     TSP_MMA_S(6)
     TSP_LOAD_K(6)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float d = m_s[qb] - m_at[qb];
-      need |= (mx[qb] - d > kLazy) | (d != 0.0f);
-      alpha[qb] = 1.0f;
-    }
+    need = (mx[0] > kLazy) | (mx[1] > kLazy);
+    alpha[0] = alpha[1] = 1.0f;
     TSP_SB();
     TSP_MMA_PV(7)
     TSP_LOAD_V(7)
     TSP_MMA_L(0, 0)
-    if (__ballot(need)) {  // rare: shift the scores to the new reference
+    if (__ballot(need) | unseen | stale) {  // rare: shift the scores to the new reference
+      mx[0] = max_swap32(mx[0]);  // the row max over both half-waves
+      mx[1] = max_swap32(mx[1]);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float d = m_s[qb] - m_at[qb];
@@ -1106,18 +1108,26 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
         for (int r = 0; r < 16; ++r) start_t[qb][r] = -m_cm[qb];
         any |= upd;
       }
+      unseen = __ballot((m_s[0] == -INFINITY) | (m_s[1] == -INFINITY)) != 0;
     }
     TSP_SB();
-    // slots 8-23: exponentials and bf16 P, one key pair of one query block each
-#define TSP_EXP(i)                                                                   \
-  {                                                                                  \
-    constexpr int k_ = (i) - 8, qb_ = k_ % 2, hh_ = (k_ / 2) / 4, e_ = (k_ / 2) % 4; \
-    const float p0 = __builtin_amdgcn_exp2f(sc[qb_][8 * hh_ + 2 * e_]);             \
-    const float p1 = __builtin_amdgcn_exp2f(sc[qb_][8 * hh_ + 2 * e_ + 1]);         \
-    w[qb_][hh_][e_] = pack_bf16x2(p0, p1);                                           \
-    asm volatile("" ::"v"(w[qb_][hh_][e_])); /* computed in this slot */             \
-  }                                                                                  \
-  TSP_SB();
+    // slots 8-31: exponentials and bf16 P, two operations per slot (spread evenly: the MFMA
+    // pipe stays fed only while each gap between MFMAs holds a few instructions). Operation n
+    // (0..47) is exp, exp, convert of key pair n / 3, which is query block pr % 2, half
+    // (pr / 2) / 4, register pair (pr / 2) % 4.
+    float pv_[16][2];
+#define TSP_OP(n)                                                                                    \
+  {                                                                                                  \
+    constexpr int pr_ = (n) / 3, op_ = (n) % 3, qb_ = pr_ % 2, hh_ = (pr_ / 2) / 4, e_ = (pr_ / 2) % 4; \
+    if (op_ < 2) {                                                                                   \
+      pv_[pr_][op_ % 2] = __builtin_amdgcn_exp2f(sc[qb_][8 * hh_ + 2 * e_ + op_ % 2]);               \
+      asm volatile("" ::"v"(pv_[pr_][op_ % 2])); /* computed in this slot */                         \
+    } else {                                                                                         \
+      w[qb_][hh_][e_] = pack_bf16x2(pv_[pr_][0], pv_[pr_][1]);                                        \
+      asm volatile("" ::"v"(w[qb_][hh_][e_]));                                                       \
+    }                                                                                                \
+  }
+#define TSP_EXP(i) TSP_OP(2 * ((i) - 8)) TSP_OP(2 * ((i) - 8) + 1) TSP_SB();
     TSP_MMA_S(8)   TSP_EXP(8)
     TSP_MMA_PV(9)  TSP_EXP(9)
     TSP_MMA_S(10)  TSP_LOAD_K(10) TSP_EXP(10)
@@ -1134,27 +1144,27 @@ __global__ __launch_bounds__(w64::THREADS) __attribute__((amdgpu_waves_per_eu(1,
     TSP_MMA_PV(21) TSP_EXP(21)
     TSP_MMA_S(22)  TSP_LOAD_K(22) TSP_EXP(22)
     TSP_MMA_PV(23) TSP_LOAD_V(23) TSP_MMA_L(0, 1) TSP_EXP(23)
+    TSP_MMA_S(24)  TSP_EXP(24)
+    TSP_MMA_PV(25) TSP_EXP(25)
+    TSP_MMA_S(26)  TSP_LOAD_K(26) TSP_EXP(26)
+    TSP_MMA_PV(27) TSP_LOAD_V(27) TSP_EXP(27)
+    TSP_MMA_S(28)  TSP_EXP(28)
+    TSP_MMA_PV(29) TSP_EXP(29)
+    TSP_MMA_S(30)  TSP_LOAD_K(30) TSP_EXP(30)
+    TSP_MMA_PV(31) TSP_LOAD_V(31) TSP_MMA_L(1, 1) TSP_EXP(31)
+#undef TSP_EXP
+#undef TSP_OP
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) pc[qb][hh] = as_bf16x8(make_uint4(w[qb][hh][0], w[qb][hh][1], w[qb][hh][2], w[qb][hh][3]));
     }
-    // slots 24-31: sc restarts as the chain of block j+2, from -m_cm (4 values per slot)
-#define TSP_INIT(i) TSP_SB();
-    TSP_MMA_S(24)  TSP_INIT(24)
-    TSP_MMA_PV(25) TSP_INIT(25)
-    TSP_MMA_S(26)  TSP_LOAD_K(26) TSP_INIT(26)
-    TSP_MMA_PV(27) TSP_LOAD_V(27) TSP_INIT(27)
-    TSP_MMA_S(28)  TSP_INIT(28)
-    TSP_MMA_PV(29) TSP_INIT(29)
-    TSP_MMA_S(30)  TSP_LOAD_K(30) TSP_INIT(30)
-    TSP_MMA_PV(31) TSP_LOAD_V(31) TSP_MMA_L(1, 1) TSP_INIT(31)
-#undef TSP_EXP
-#undef TSP_INIT
+
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) m_at[qb] = m_cm[qb];
     // O^T now holds the blocks before j: rescale it for block j's reference (rare)
-    if (__ballot(any)) {
+    stale = __ballot(any) != 0;  // block j+1 was started from the old reference
+    if (stale) {
       rescale_agprs<OR>(alpha[0]);
       rescale_agprs<OR + 64>(alpha[1]);
       rescale_rowsums<LR>(alpha[0], alpha[1]);
