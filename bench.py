@@ -547,7 +547,7 @@ def main():
                    "d_model": w.d_model, "n_heads": w.n_heads, "head_dim": w.head_dim,
                    "ffn": w.ffn, "flops_per_step": flops},
         "phases_ms": {k: round(v, 4) for k, v in phases.items()},
-        "roofline": {"kernel": "attention (attn_fwd<128>)", "bound": "mfma",
+        "roofline": {"kernel": "attention (attn_fwd_w64)", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "avg_launch_ms": round(attn_ms, 4),
