@@ -122,13 +122,52 @@ def build(verbose=False, resource_usage=False):
     return LIB
 
 
+SAN_BUILD = os.path.join(PKG, "_build_san")
+SAN_LIB = os.path.join(SAN_BUILD, "libtsp.so")
+# Host-side sanitizers for the C ABI's host code (argument checks, workspace layout, launch
+# order). Each flag applies to the host compilation only: the gfx950 code is built as usual.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+
+
+def asan_runtime():
+    """Path of the AddressSanitizer runtime that a host process must preload to use SAN_LIB."""
+    out = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], check=True, text=True,
+                         stdout=subprocess.PIPE, stderr=subprocess.DEVNULL).stdout.strip()
+    if not os.path.isabs(out) or not os.path.exists(out):
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return out
+
+
+def build_sanitized(verbose=False):
+    """libtsp.so with tsp_api.hip's host code built under AddressSanitizer and
+    UndefinedBehaviorSanitizer (the other objects as in `build`, which must have run).
+    Returns the library path."""
+    hipcc = _hipcc()
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "tsp_api.hip"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"run build() first: {missing}")
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    api = os.path.join(SAN_BUILD, "tsp_api.o")
+    _run([hipcc, *HIPCC_FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, "tsp_api.hip"), "-o", api], verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+          "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", SAN_LIB, api, *objs], verbose)
+    return SAN_LIB
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--resource-usage", action="store_true")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="also build the host-sanitized library (ASan + UBSan) under _build_san/")
     args = ap.parse_args(argv)
     path = build(verbose=args.verbose, resource_usage=args.resource_usage)
     print(path)
+    if args.sanitize:
+        print(build_sanitized(verbose=args.verbose))
 
 
 if __name__ == "__main__":

@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libtsp.so")
+# TSP_LIBRARY selects another build of the same library (the sanitized host build of the CPU
+# tests); by default the in-tree libtsp.so.
+LIB_PATH = os.environ.get("TSP_LIBRARY") or os.path.join(_PKG, "libtsp.so")
 
 TSP_OK = 0
 STATUS_NAMES = {0: "TSP_OK", 1: "TSP_ERR_NULL", 2: "TSP_ERR_SHAPE", 3: "TSP_ERR_RANK",
