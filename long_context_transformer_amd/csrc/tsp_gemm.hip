@@ -674,6 +674,26 @@ bool fast_ok(const Operands& op, bool dual) {
 // the chip busy. Operands that cannot take 16-byte chunks (odd K or strides: only tiny
 // shapes) use the register-staged kernel with element-wise loads.
 constexpr int64_t kBigTileMin = 256;
+// Single-weight GEMMs also have a 256 x 128 tile (64 x 64 per wave: one LDS fragment per MFMA
+// against 0.75 for the 256 x 256 tile's 128 x 64 waves). Each tile fills one CU, so a launch
+// runs in rounds of kCUs tiles; where the 256 x 256 tiles leave much of the last round idle
+// (few row tiles: M of a few thousand) the 256 x 128 tile fills the rounds better.
+constexpr int64_t kCUs = 256;
+constexpr double kMidTileRate = 0.68;  // its per-CU rate relative to the 256 x 256 tile (measured)
+enum class Tile { k256x256, k256x128, k128x128 };
+
+double round_fill(int64_t tiles) {
+  const int64_t rounds = (tiles + kCUs - 1) / kCUs;
+  return (double)tiles / (double)(rounds * kCUs);
+}
+
+Tile choose_tile(int M, int N) {
+  const int64_t tm = (M + 255) / 256;
+  const int64_t t256 = tm * ((N + 255) / 256), t_mid = tm * ((N + 127) / 128);
+  if (t256 >= kBigTileMin && round_fill(t256) >= kMidTileRate * round_fill(t_mid)) return Tile::k256x256;
+  if (t_mid >= kCUs) return Tile::k256x128;
+  return Tile::k128x128;
+}
 
 template <class Epi>
 hipError_t run_single(const Operands& op, const Epi& epi, hipStream_t s) {
@@ -681,9 +701,11 @@ hipError_t run_single(const Operands& op, const Epi& epi, hipStream_t s) {
     const bool vec = (op.K % 8 == 0) && (op.lda % 8 == 0) && (op.ldb % 8 == 0) && aligned16(op.a) && aligned16(op.b);
     return vec ? run_tiles<128, 128, false, true>(op, epi, s) : run_tiles<128, 128, false, false>(op, epi, s);
   }
-  const int64_t big = (int64_t)((op.M + 255) / 256) * ((op.N + 255) / 256);
-  if (big >= kBigTileMin) return run_fast<256, 256, 128, 64, false>(op, epi, s);
-  return run_fast<128, 128, 64, 64, false>(op, epi, s);
+  switch (choose_tile(op.M, op.N)) {
+    case Tile::k256x256: return run_fast<256, 256, 128, 64, false>(op, epi, s);
+    case Tile::k256x128: return run_fast<256, 128, 64, 64, false>(op, epi, s);
+    default: return run_fast<128, 128, 64, 64, false>(op, epi, s);
+  }
 }
 
 template <class Epi>
@@ -794,9 +816,11 @@ hipError_t launch_down_ring(const void* h, int64_t ldh, int64_t ldseg, const voi
   }
   sg.count = D;
   op.b = sg.b[0];
-  const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= kBigTileMin) return run_fast<256, 256, 128, 64, false, SEG_K>(op, epi, stream, sg);
-  return run_fast<128, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
+  switch (choose_tile(M, N)) {
+    case Tile::k256x256: return run_fast<256, 256, 128, 64, false, SEG_K>(op, epi, stream, sg);
+    case Tile::k256x128: return run_fast<256, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
+    default: return run_fast<128, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
+  }
 }
 
 }  // namespace tsp

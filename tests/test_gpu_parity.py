@@ -141,6 +141,9 @@ MLP_CASES = [  # M, d, Fs, ld_w2 (0 = Fs)
     # the large-tile kernels: gate/up 256 x 128 per weight (512 tiles), down 256 x 256 (256 tiles)
     (4096, 4096, 4096, 0),
     (4000, 4096, 4104, 0),   # ragged: M tail 160, gate/up N tail 8, down K tail 8
+    # down 256 x 128 (M = 2048, N = 4096: 256 x 256 tiles would fill half the CUs)
+    (2048, 4096, 1376, 0),
+    (1900, 4096, 1000, 0),   # ragged: M tail 108, down K tail 40
 ]
 
 
