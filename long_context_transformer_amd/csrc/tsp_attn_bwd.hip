@@ -46,7 +46,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // `lds` + 4 i (M0 holds `lds`). Like the 16-byte forms it is issued from inline assembly
 // and ordered by explicit s_waitcnt vmcnt and s_barrier.
 __device__ __forceinline__ void dma4_vaddr(const void* addr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "s"(lds) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "s"(lds) : "memory");
 }
 
 // s_waitcnt vmcnt(n) for a wave-uniform n known only at run time (s_waitcnt takes an

@@ -54,7 +54,8 @@ __device__ __forceinline__ bf16_t to_bf16(float x) {
 // Issued from inline assembly on purpose: the compiler then neither tracks these writes
 // nor inserts its own conservative waits before LDS reads; callers order them with
 // explicit s_waitcnt vmcnt (loads retire in order) and s_barrier. Nothing else in these
-// kernels uses M0.
+// kernels uses M0. A scalar write of M0 needs one wait state before an LDS DMA reads it
+// (the compiler puts an s_nop 0 there for its own global_load_lds), hence the s_nop.
 //   dma16_sbase: address = uniform 64-bit base + per-lane 32-bit byte offset
 //   dma16_vaddr: address = per-lane 64-bit pointer
 __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t voff, uint32_t lds) {
@@ -65,10 +66,10 @@ __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t voff, uin
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
   const uint64_t ps = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ps), "s"(lds) : "memory");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ps), "s"(lds) : "memory");
 }
 __device__ __forceinline__ void dma16_vaddr(const void* addr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds) : "memory");
 }
 // LDS byte address of a pointer into a __shared__ array, made wave-uniform.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
