@@ -24,6 +24,29 @@ LSE_MEAN_ABS = 3e-3
 BF16_NAN = 0x7FC0
 
 
+# Softmax scale 1/(8 log2 e): the kernel's pre-scaled Q (q / 8) is then exact in bf16, so its
+# scores differ from the oracle's only by fp32 rounding even where they reach thousands.
+RAMP_SCALE = float(1.0 / (8.0 * np.log2(np.e)))
+
+
+def ramp_inputs(B, S, rows, H, hd, seed):
+    """Per head, scores (log2 units) that rise by 12 per key position (the running max moves
+    at every 32-key block, so every block takes the reference-move path and the next block's
+    scores were started from the old reference), rise by 0.2 per key (a move every few
+    blocks), fall by 0.5 per key (no move after the first block), or are random (head 3)."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(hd).astype(np.float32)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((B, rows, H, hd)).astype(np.float32)
+    k = rng.standard_normal((B, S, H, hd)).astype(np.float32)
+    v = rng.standard_normal((B, S, H, hd)).astype(np.float32)
+    pos = np.arange(S, dtype=np.float32)[:, None]
+    for h, slope in ((0, 12.0), (1, 0.2), (2, -0.5)):
+        q[:, :, h] = u + 0.05 * q[:, :, h]
+        k[:, :, h] = 8.0 * slope * pos * u + 0.05 * k[:, :, h]
+    return tuple(synth.round_bf16_bits(x) for x in (q, k, v))
+
+
 def dev_bf16(bits):
     return synth.to_torch(bits).cuda()
 

@@ -17,7 +17,7 @@ import torch
 from long_context_transformer_amd import synth, tsp
 from oracle import tsp_oracle as O
 
-from _gpu_helpers import check_close, check_lse, dev_bf16, host_f64
+from _gpu_helpers import RAMP_SCALE, check_close, check_lse, dev_bf16, host_f64, ramp_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +74,33 @@ def check_range(name, o, lse, ref_o, ref_lse):
     if np.any(~empty):
         check_close(f"{name} O", o_h[~rows_empty], ref_o[~rows_empty])
         check_lse(f"{name} lse", l_h[~empty], ref_lse[~empty])
+
+
+RAMP_RANGE_CASES = [  # B, S, D, rank, H, hd, ranges
+    (1, 2048, 2, 1, 4, 128, [(0, 2048), (700, 1500), (1500, 2048), (33, 1000)]),
+    (1, 1200, 3, 2, 4, 64, [(100, 900), (0, 1200)]),
+]
+
+
+@pytest.mark.parametrize("B,S,D,rank,H,hd,ranges", RAMP_RANGE_CASES)
+def test_attn_range_reference_moves(B, S, D, rank, H, hd, ranges):
+    """Key ranges over scores that climb, creep, fall or wander along the keys (see
+    ramp_inputs): rows that see no key of the range until late, or at all, next to rows
+    whose reference moves at every block."""
+    print(f"range attention, reference moves B={B} S={S} D={D} rank={rank} H={H} hd={hd}", flush=True)
+    R = S // D
+    q, k, v = ramp_inputs(B, S, R, H, hd, 7400 + S + rank)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    idx = O.zigzag_index(S, D, rank)
+    for lo, hi in ranges:
+        o = torch.full((B, R, H, hd), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((B, H, R), float("nan"), dtype=torch.float32, device="cuda")
+        tsp.attn_fwd_range(qd, nan_outside(kd, lo, hi), nan_outside(vd, lo, hi), o, lse, B, S, D, rank, H, hd,
+                           lo, hi, scale=RAMP_SCALE)
+        torch.cuda.synchronize()
+        ref_o, ref_lse = O.attention_range(synth.to_f64(q), idx, synth.to_f64(k), synth.to_f64(v), lo, hi,
+                                           scale=RAMP_SCALE)
+        check_range(f"[{lo},{hi})", o, lse, ref_o, ref_lse)
 
 
 RANGE_CASES = [  # B, S, D, rank, H, hd, ranges

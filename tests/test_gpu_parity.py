@@ -14,7 +14,7 @@ import torch
 from long_context_transformer_amd import synth, tsp
 from oracle import tsp_oracle as O
 
-from _gpu_helpers import (BF16_NAN, check_close, check_lse, dev_bf16, fill_peer_kv, host_bits, host_f64,
+from _gpu_helpers import (RAMP_SCALE, BF16_NAN, ramp_inputs, check_close, check_lse, dev_bf16, fill_peer_kv, host_bits, host_f64,
                           nan_bf16, shard_rows)
 
 pytestmark = pytest.mark.gpu
@@ -102,6 +102,34 @@ def test_attn_parity(B, S, D, rank, H, hd):
     for c0 in (0, C):
         for h in range(H):
             check_close(f"o chunk{c0 // C} head{h}", got[:, c0:c0 + C, h], ref_o[:, c0:c0 + C, h])
+
+
+RAMP_CASES = [  # B, S, D, rank, H, hd
+    (1, 2048, 2, 1, 4, 128),
+    (2, 1024, 4, 2, 4, 128),
+    (1, 512, 1, 0, 4, 128),    # D = 1: plain causal attention
+    (1, 1200, 3, 1, 4, 64),
+]
+
+
+@pytest.mark.parametrize("B,S,D,rank,H,hd", RAMP_CASES)
+def test_attn_reference_moves(B, S, D, rank, H, hd):
+    """Scores that climb, creep, fall or wander along the keys: the online softmax's
+    reference moves at every block, every few blocks or never, and each case must still
+    match the oracle (O per head, and the log-sum-exp)."""
+    print(f"attn reference moves B={B} S={S} D={D} rank={rank} H={H} hd={hd}", flush=True)
+    rows = S // D
+    q, k, v = ramp_inputs(B, S, rows, H, hd, 7300 + S + rank)
+    o = torch.empty((B, rows, H, hd), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, rows), dtype=torch.float32, device="cuda")
+    tsp.attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), o, lse, B, S, D, rank, H, hd, scale=RAMP_SCALE)
+    torch.cuda.synchronize()
+    idx = O.zigzag_index(S, D, rank)
+    ref_o, ref_lse = O.causal_attention(synth.to_f64(q), idx, synth.to_f64(k), synth.to_f64(v), scale=RAMP_SCALE)
+    got = host_f64(o)
+    for h in range(H):
+        check_close(f"o head{h}", got[:, :, h], ref_o[:, :, h])
+    check_lse("lse", host_f64(lse), ref_lse)
 
 
 def test_attn_scale_argument():
