@@ -378,7 +378,7 @@ struct SegArgOf<SEG_NONE> {
 template <int SEG>
 using SegArg = typename SegArgOf<SEG>::type;
 
-template <int BM, int BN, int WM, int WN, bool DUAL, int SEG, int KB, class Epi>
+template <int BM, int BN, int WM, int WN, bool DUAL, int SEG, int KB, int GM, class Epi>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN) / 4, (BM / WM) * (BN / WN) / 4)))
 void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
@@ -407,9 +407,9 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
   const int l32 = lane & 31, hl = lane >> 5;
 
   const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-  const int span = kGroupM * tiles_n;
-  const int first_m = (t / span) * kGroupM;
-  const int gsz = min(tiles_m - first_m, kGroupM);
+  const int span = GM * tiles_n;
+  const int first_m = (t / span) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
   const int in_g = t - (t / span) * span;
   const int m0 = (first_m + in_g % gsz) * BM;
   int n0 = (in_g / gsz) * BN;
@@ -643,7 +643,7 @@ hipError_t run_tiles(const Operands& op, const Epi& epi, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, bool DUAL, int SEG = SEG_NONE, class Epi>
+template <int BM, int BN, int WM, int WN, bool DUAL, int SEG = SEG_NONE, int GM = kGroupM, class Epi>
 hipError_t run_fast(const Operands& op, const Epi& epi, hipStream_t s, SegArg<SEG> sg = {}) {
   constexpr int KB = 64;
   const int tm = (op.M + BM - 1) / BM;
@@ -654,7 +654,7 @@ hipError_t run_fast(const Operands& op, const Epi& epi, hipStream_t s, SegArg<SE
   }
   if constexpr (SEG == SEG_K) sg.nks = (op.K + KB - 1) / KB;
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  hipLaunchKernelGGL((gemm_fast<BM, BN, WM, WN, DUAL, SEG, KB, Epi>), dim3(tm * tn), dim3(threads), 0, s, op, epi, tm,
+  hipLaunchKernelGGL((gemm_fast<BM, BN, WM, WN, DUAL, SEG, KB, GM, Epi>), dim3(tm * tn), dim3(threads), 0, s, op, epi, tm,
                      tn, sg);
   return hipGetLastError();
 }
@@ -816,8 +816,12 @@ hipError_t launch_down_ring(const void* h, int64_t ldh, int64_t ldseg, const voi
   }
   sg.count = D;
   op.b = sg.b[0];
+  // Tiles in groups of 2 row tiles (16 column tiles of the 7B width run together on an XCD):
+  // the hidden activation (361 MB at 7B S=128K) does not fit the 256 MB MALL, so each of its
+  // row panels is read from HBM about once per group; the weights, which fit, are re-read
+  // from the MALL instead (8-row groups: 3.76 ms of MLP, 2-row groups: 3.68 ms).
   switch (choose_tile(M, N)) {
-    case Tile::k256x256: return run_fast<256, 256, 128, 64, false, SEG_K>(op, epi, stream, sg);
+    case Tile::k256x256: return run_fast<256, 256, 128, 64, false, SEG_K, 2>(op, epi, stream, sg);
     case Tile::k256x128: return run_fast<256, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
     default: return run_fast<128, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
   }
