@@ -780,43 +780,58 @@ int tsp_layer_fwd_streamed(const tsp_layer_desc* desc, const void* x_shard, cons
   for (int t = 0; t < 2 && t < D; ++t)
     if (int rc = fill_mlp(t)) return rc;
 
-  // Head group t: QKV and attention on comp[t % 2], the W_O partial on s_wo (in order of t,
-  // so the fp32 sum takes the groups in order). A slot's QKV rows are refilled once its QKV
-  // launch is done, its W_o columns once its W_O launch is done.
-  for (int t = 0; t < D; ++t) {
-    const int sl = t & 1;
-    hipStream_t st = comp[sl];
-    if (int rc = wait(st, q_full[sl])) return rc;
-    if (int rc = hip_status(tsp::launch_qkv_group(x_shard, slot_a[sl], t, D, q, k_full, v_full, B, S, D, r, d, st),
-                            "group qkv launch"))
-      return rc;
-    if (t + 2 < D) {
-      if (int rc = rec(q_free[sl], st)) return rc;
-      if (int rc = fill_qkv(t + 2)) return rc;
+  // Head groups in pairs (t, t+1), one group per slot: the pair's QKV launches, then its
+  // attention as one launch over both groups' heads, on comp[(t / 2) % 2]; then one W_O
+  // partial over both groups on s_wo (pairs in order, so the fp32 sum takes the groups in
+  // order). A slot's QKV rows are refilled once its QKV launch is done, its W_o columns once
+  // the pair's W_O launch is done. With D odd the last group runs alone, its attention split
+  // into two key halves (one group is about one query tile per CU, and a tile of the later
+  // zigzag chunk sees up to S keys) merged by log-sum-exp.
+  for (int t = 0; t < D; t += 2) {
+    const bool pair = t + 1 < D;
+    const int pi = (t / 2) & 1;
+    hipStream_t st = comp[pi];
+    for (int u = t; u < t + (pair ? 2 : 1); ++u) {
+      const int sl = u & 1;
+      if (int rc = wait(st, q_full[sl])) return rc;
+      if (int rc = hip_status(tsp::launch_qkv_group(x_shard, slot_a[sl], u, D, q, k_full, v_full, B, S, D, r, d, st),
+                              "group qkv launch"))
+        return rc;
+      if (u + 2 < D) {
+        if (int rc = rec(q_free[sl], st)) return rc;
+        if (int rc = fill_qkv(u + 2)) return rc;
+      }
     }
-    // Causal attention of the group's heads, every query tile's keys split at S/2 into two
-    // work items (one group has about one tile per CU, and a tile of the later zigzag
-    // chunk sees up to S keys), then the halves merged by log-sum-exp into bf16 O.
-    if (int rc = hip_status(tsp::launch_attn_split(q, k_full, v_full, part[sl], part_lse[sl], B, S, D, r, H, hd,
-                                                   desc->scale, t * hg, hg, (int)(S / 2), st),
-                            "group attention launch"))
-      return rc;
-    if (int rc = hip_status(tsp::launch_attn_merge_halves(part[sl], part_lse[sl], o, B, (int)(S / D), H, hd, t * hg,
-                                                          hg, st),
-                            "group attention merge launch"))
-      return rc;
-    if (int rc = rec(attn_done[sl], st)) return rc;
-    if (int rc = wait(s_wo, attn_done[sl])) return rc;
-    if (int rc = wait(s_wo, o_full[sl])) return rc;
-    if (int rc = hip_status(tsp::launch_wo_group(o, slot_a[sl] + qkv_part, t, D, mlp_out, attn_out, M, d, t, D, s_wo),
-                            "group W_O launch"))
-      return rc;
-    if (t + 2 < D)
-      if (int rc = rec(o_free[sl], s_wo)) return rc;
-    // The W_o columns of group t+1 were released by W_O step t-1; queued here, behind the
-    // QKV rows of group t+2, so that no copy waits behind one that is needed later.
-    if (t + 1 >= 2 && t + 1 < D)
-      if (int rc = fill_wo(t + 1)) return rc;
+    if (pair) {
+      if (int rc = hip_status(tsp::launch_attn_heads(q, k_full, v_full, o, B, S, D, r, H, hd, desc->scale, t * hg,
+                                                     2 * hg, st),
+                              "group pair attention launch"))
+        return rc;
+    } else {
+      if (int rc = hip_status(tsp::launch_attn_split(q, k_full, v_full, part[0], part_lse[0], B, S, D, r, H, hd,
+                                                     desc->scale, t * hg, hg, (int)(S / 2), st),
+                              "group attention launch"))
+        return rc;
+      if (int rc = hip_status(tsp::launch_attn_merge_halves(part[0], part_lse[0], o, B, (int)(S / D), H, hd, t * hg,
+                                                            hg, st),
+                              "group attention merge launch"))
+        return rc;
+    }
+    if (int rc = rec(attn_done[pi], st)) return rc;
+    if (int rc = wait(s_wo, attn_done[pi])) return rc;
+    if (int rc = wait(s_wo, o_full[0])) return rc;
+    if (pair)
+      if (int rc = wait(s_wo, o_full[1])) return rc;
+    const hipError_t e = pair ? tsp::launch_wo_pair(o, slot_a[0] + qkv_part, slot_a[1] + qkv_part, t, D, mlp_out,
+                                                    attn_out, M, d, t == 0 ? 1 : 0, t + 2 >= D ? 1 : 0, s_wo)
+                              : tsp::launch_wo_group(o, slot_a[0] + qkv_part, t, D, mlp_out, attn_out, M, d, t == 0 ? 0 : 1,
+                                                     t == 0 ? 1 : 2, s_wo);
+    if (int rc = hip_status(e, "group W_O launch")) return rc;
+    for (int u = t; u < t + (pair ? 2 : 1); ++u)
+      if (u + 2 < D) {
+        if (int rc = rec(o_free[u & 1], s_wo)) return rc;
+        if (int rc = fill_wo(u + 2)) return rc;
+      }
   }
   if (int rc = rec(wo_last, s_wo)) return rc;
   if (int rc = wait(s0, wo_last)) return rc;

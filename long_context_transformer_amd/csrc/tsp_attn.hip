@@ -1322,6 +1322,14 @@ hipError_t launch_attn_range(const void* q, const void* k_full, const void* v_fu
   return launch<true>(a, hd, stream);
 }
 
+hipError_t launch_attn_heads(const void* q, const void* k_full, const void* v_full, void* o, int B, int64_t S, int D,
+                             int rank, int H, int hd, float scale, int h0, int h_run, hipStream_t stream) {
+  AttnArgs a = base_args(q, k_full, v_full, B, S, D, rank, H, hd, scale);
+  if (!set_heads(a, B, h0, h_run)) return hipErrorInvalidValue;
+  a.o = static_cast<bf16_t*>(o);
+  return launch<false>(a, hd, stream);
+}
+
 hipError_t launch_attn_split(const void* q, const void* k_full, const void* v_full, float* o32, float* lse, int B,
                              int64_t S, int D, int rank, int H, int hd, float scale, int h0, int h_run, int split,
                              hipStream_t stream) {

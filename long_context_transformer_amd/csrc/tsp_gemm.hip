@@ -752,6 +752,33 @@ hipError_t launch_wo_group(const void* o, const void* w_o_g, int group, int grou
   return run_single(op, EpiAcc{acc, d, step > 0 ? 1 : 0}, stream);
 }
 
+hipError_t launch_wo_pair(const void* o, const void* w_o_a, const void* w_o_b, int group, int groups, float* acc,
+                          void* out, int M, int d, int first, int last, hipStream_t stream) {
+  const int dg = d / groups;
+  Operands op{static_cast<const bf16_t*>(o), d, static_cast<const bf16_t*>(w_o_a), nullptr, dg, M, d, dg};
+  Shards sg{};
+  sg.b[0] = static_cast<const bf16_t*>(w_o_a);
+  sg.b[1] = static_cast<const bf16_t*>(w_o_b);
+  sg.a_col[0] = (int64_t)group * dg;
+  sg.a_col[1] = (int64_t)(group + 1) * dg;
+  sg.count = 2;
+  // Operands the 16-byte path cannot take run as two single-group launches.
+  Operands chk = op;
+  chk.a = op.a + sg.a_col[0];
+  if (!fast_ok(chk, false) || !aligned16(w_o_b) || (dg * 2) % 16 != 0) {
+    if (hipError_t e = launch_wo_group(o, w_o_a, group, groups, acc, out, M, d, first ? 0 : 1, 3, stream)) return e;
+    return launch_wo_group(o, w_o_b, group + 1, groups, acc, out, M, d, last ? 2 : 1, 3, stream);
+  }
+  if (last) {
+    const EpiAccBf16 epi{acc, static_cast<bf16_t*>(out), d, first};
+    if (choose_tile(M, d) == Tile::k256x256) return run_fast<256, 256, 128, 64, false, SEG_K>(op, epi, stream, sg);
+    return run_fast<128, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
+  }
+  const EpiAcc epi{acc, d, first ? 0 : 1};
+  if (choose_tile(M, d) == Tile::k256x256) return run_fast<256, 256, 128, 64, false, SEG_K>(op, epi, stream, sg);
+  return run_fast<128, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
+}
+
 hipError_t launch_proj_bf16(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc, int M, int N,
                             int K, hipStream_t stream) {
   Operands op{static_cast<const bf16_t*>(a), lda, static_cast<const bf16_t*>(w), nullptr, ldw, M, N, K};

@@ -23,6 +23,11 @@ hipError_t launch_qkv_group(const void* x, const void* w_qkv_g, int group, int g
 // stored as bf16 to out instead.
 hipError_t launch_wo_group(const void* o, const void* w_o_g, int group, int groups, float* acc, void* out, int M, int d,
                            int step, int steps, hipStream_t stream);
+// The same for head groups `group` and `group + 1` in one launch (their W_o columns w_o_a and
+// w_o_b held apart), the two products summed in fp32 registers: acc (= when first, else +=);
+// when last, out = bf16(acc + the pair's partial) instead (acc not written).
+hipError_t launch_wo_pair(const void* o, const void* w_o_a, const void* w_o_b, int group, int groups, float* acc,
+                          void* out, int M, int d, int first, int last, hipStream_t stream);
 
 // Plain projection C[M, N] = A[M, K] W[N, K]^T, bf16 out (step a4, W_O).
 hipError_t launch_proj_bf16(const void* a, int64_t lda, const void* w, int64_t ldw, void* c,
@@ -64,6 +69,10 @@ hipError_t launch_attn(const void* q, const void* k_full, const void* v_full, vo
 // log-sum-exp; half 0 at o32 / lse, half 1 at o32 + B rows h_run hd / lse + B h_run rows,
 // in the group's [B, rows, h_run, hd] / [B, h_run, rows] layout. Every item covers at most
 // max(split, S - split) keys; launch_attn_merge_halves then writes bf16 O.
+// Causal attention of heads [h0, h0 + h_run) only, bf16 O into the full-width o (the other
+// heads' columns untouched).
+hipError_t launch_attn_heads(const void* q, const void* k_full, const void* v_full, void* o, int B, int64_t S, int D,
+                             int rank, int H, int hd, float scale, int h0, int h_run, hipStream_t stream);
 hipError_t launch_attn_split(const void* q, const void* k_full, const void* v_full, float* o32, float* lse, int B,
                              int64_t S, int D, int rank, int H, int hd, float scale, int h0, int h_run, int split,
                              hipStream_t stream);
