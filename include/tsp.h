@@ -296,12 +296,15 @@ TSP_API int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const
  *                 slot is refilled in two parts: its QKV rows once the QKV launch that read
  *                 them is done, its W_o columns once the W_O launch that read them is done.
  *                 The MLP shards 0 and 1 are copied right after the attention shards 0, 1.
- *   attention     head group t (t = j = 0 .. D-1) runs on streams[t % 2]: QKV of the
- *                 group (its Q columns, its columns of the rank's K/V rows), then causal
- *                 attention of its heads with every query tile's keys split at S/2 into
- *                 two work items, merged by log-sum-exp into O. Two groups overlap.
- *   W_O stream    O_group W_o,group^T added to an fp32 accumulator, in order of t; the
- *                 last step stores the sum as bf16 attn_out.
+ *   attention     head groups t = j = 0 .. D-1 in pairs (t, t+1), one per attention slot;
+ *                 pair p runs on streams[p % 2]: the QKV of each group (its Q columns, its
+ *                 columns of the rank's K/V rows), then causal attention of the pair's
+ *                 heads as one launch. With D odd the last group runs alone, every query
+ *                 tile's keys split at S/2 into two work items merged by log-sum-exp into
+ *                 O. Two pairs overlap.
+ *   W_O stream    per pair, O_pair W_o,pair^T (both groups' partials summed in fp32
+ *                 registers) added to an fp32 accumulator, pairs in order; the last step
+ *                 stores the sum as bf16 attn_out.
  *   streams[0]    the MLP ring after the last W_O step, t = 0 .. D-1 on shard
  *                 j = (r - t) mod D: the gated hidden of shard j, then its down projection
  *                 added to mlp_out.
@@ -317,8 +320,8 @@ TSP_API int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const
  * threads are not supported.
  * Workspace (tsp_layer_streamed_workspace_size; 0 if desc is invalid): Q and O bf16
  * [B 2C, d] each, the gated hidden of one shard bf16 [B 2C, Fp], two attention slots, two
- * MLP slots, and per attention stream the fp32 O and log-sum-exp of a group's attention
- * over keys [0, S/2) and [S/2, S) (merged into O after each group).
+ * MLP slots and, when D is odd, the fp32 O and log-sum-exp of the last group's attention
+ * over keys [0, S/2) and [S/2, S) (merged into O).
  * Errors: as tsp_layer_fwd; TSP_ERR_SHAPE if H % D != 0 or n_streams is not 1 or 4.
  */
 TSP_API size_t tsp_layer_streamed_workspace_size(const tsp_layer_desc* desc);

@@ -635,7 +635,7 @@ int stream_events(hipEvent_t** out, int n) {
 }
 
 struct StreamedCarve {
-  size_t q_off, o_off, h_off, slot_a[2], slot_m[2], part[2], total;
+  size_t q_off, o_off, h_off, slot_a[2], slot_m[2], part, total;
   size_t attn_shard, mlp_shard;  // elements of one packed shard
   int64_t fp;                    // W2 row stride / hidden row stride in a packed MLP shard
 };
@@ -665,13 +665,12 @@ StreamedCarve carve_streamed(const tsp_layer_desc* d) {
     c.slot_m[i] = at;
     at += round_up(c.mlp_shard * 2, kAlign);
   }
-  // Per attention stream: the two key halves of a head group's attention, fp32 O
-  // [2, M, dg] and log-sum-exp [2, M * heads per group].
+  // With D odd, the last head group runs alone and its attention is split into two key
+  // halves: fp32 O [2, M, dg] and log-sum-exp [2, M * heads per group]. Pairs of groups
+  // write O directly.
   const size_t hg = (size_t)(d->n_heads / d->fold);
-  for (int i = 0; i < 2; ++i) {
-    c.part[i] = at;
-    at += round_up(2 * M * dg * 4, kAlign) + round_up(2 * M * hg * 4, kAlign);
-  }
+  c.part = at;
+  if (d->fold % 2) at += round_up(2 * M * dg * 4, kAlign) + round_up(2 * M * hg * 4, kAlign);
   c.total = at;
   return c;
 }
@@ -727,12 +726,8 @@ int tsp_layer_fwd_streamed(const tsp_layer_desc* desc, const void* x_shard, cons
                             reinterpret_cast<tsp::bf16_t*>(base + c.slot_a[1])};
   tsp::bf16_t* slot_m[2] = {reinterpret_cast<tsp::bf16_t*>(base + c.slot_m[0]),
                             reinterpret_cast<tsp::bf16_t*>(base + c.slot_m[1])};
-  float* part[2];
-  float* part_lse[2];
-  for (int i = 0; i < 2; ++i) {
-    part[i] = reinterpret_cast<float*>(base + c.part[i]);
-    part_lse[i] = reinterpret_cast<float*>(base + c.part[i] + round_up(2 * (size_t)M * dg * 4, kAlign));
-  }
+  float* part = reinterpret_cast<float*>(base + c.part);
+  float* part_lse = reinterpret_cast<float*>(base + c.part + round_up(2 * (size_t)M * dg * 4, kAlign));
   hipStream_t s0 = static_cast<hipStream_t>(streams[0]);
   auto pick = [&](int i) { return n_streams == 4 && streams[i] ? static_cast<hipStream_t>(streams[i]) : s0; };
   hipStream_t comp[2] = {s0, pick(1)};
@@ -808,11 +803,11 @@ int tsp_layer_fwd_streamed(const tsp_layer_desc* desc, const void* x_shard, cons
                               "group pair attention launch"))
         return rc;
     } else {
-      if (int rc = hip_status(tsp::launch_attn_split(q, k_full, v_full, part[0], part_lse[0], B, S, D, r, H, hd,
+      if (int rc = hip_status(tsp::launch_attn_split(q, k_full, v_full, part, part_lse, B, S, D, r, H, hd,
                                                      desc->scale, t * hg, hg, (int)(S / 2), st),
                               "group attention launch"))
         return rc;
-      if (int rc = hip_status(tsp::launch_attn_merge_halves(part[0], part_lse[0], o, B, (int)(S / D), H, hd, t * hg,
+      if (int rc = hip_status(tsp::launch_attn_merge_halves(part, part_lse, o, B, (int)(S / D), H, hd, t * hg,
                                                             hg, st),
                               "group attention merge launch"))
         return rc;

@@ -213,17 +213,19 @@ def test_layer_bwd_errors():
 
 
 def test_streamed_layer_workspace_and_errors():
-    good = _desc()
-    M, d, Fs, dg = 64, 256, 172, 64
-    fp = 176
-    act = M * d * 2
     rup = lambda x: (x + 255) // 256 * 256
-    hg = 1  # heads per group
-    part = rup(2 * M * dg * 4) + rup(2 * M * hg * 4)  # two key halves: fp32 O and lse
-    want = (2 * rup(act) + rup(M * fp * 2) + 2 * rup(4 * dg * d * 2) + 2 * rup((2 * Fs + fp) * d * 2)
-            + 2 * part)
+
+    def want(M, d, Fs, fp, dg, hg, odd):
+        act = M * d * 2
+        # the lone last head group of an odd D: two key halves, fp32 O and lse
+        part = rup(2 * M * dg * 4) + rup(2 * M * hg * 4) if odd else 0
+        return (2 * rup(act) + rup(M * fp * 2) + 2 * rup(4 * dg * d * 2) + 2 * rup((2 * Fs + fp) * d * 2)
+                + part)
+
+    good = _desc()
     ws = tsp.layer_streamed_workspace_size(good)
-    assert ws == want
+    assert ws == want(64, 256, 172, 176, 64, 1, False)   # D = 4: pairs of groups only
+    assert tsp.layer_streamed_workspace_size(_desc(D=1, rank=0)) == want(256, 256, 688, 688, 256, 4, True)
     # H % D != 0: a head group must hold whole heads
     assert tsp.layer_streamed_workspace_size(_desc(n_heads=2, head_dim=128)) == 0
     sh = [A] * 4
