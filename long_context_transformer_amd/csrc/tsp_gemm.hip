@@ -10,9 +10,11 @@
 //   EpiSwiGLU   two weights at once (W1, W3); stores silu(G) * U as bf16
 //   EpiAcc      fp32 accumulator, overwrite or add (the down projection of a shard)
 //
-// Two kernels share the epilogues. gemm_fast (below, "fast path") serves every operand
-// that takes 16-byte chunks, i.e. every layer shape but the tiny one's odd shard width;
-// gemm_nt, register-staged, serves the rest:
+// Three kernels share the epilogues. gemm_p (the persistent path, below) takes the large
+// shapes: 256 x 256 tiles, one wave per SIMD, the 16 x 16 x 32 MFMA, one workgroup per CU
+// walking its tiles. gemm_fast (the "fast path") serves the other operands that take
+// 16-byte chunks, with smaller tiles or k extents gemm_p does not take; gemm_nt,
+// register-staged, serves the rest (only the tiny workload's odd shard width):
 // Tiling of gemm_nt: 256 threads = 4 waves in a 2 x 2 grid over a BM x BN output tile;
 // each wave owns a (BM/2) x (BN/2) block made of 32 x 32 MFMA tiles
 // (v_mfma_f32_32x32x16_bf16). K advances in stages of 64 through a double-buffered LDS
@@ -29,6 +31,9 @@
 // walked column-major so tiles running together on one XCD share A and B in its L2.
 #include "tsp_device.h"
 #include "tsp_internal.h"
+
+#include <type_traits>
+#include <utility>
 
 namespace tsp {
 namespace {
@@ -633,6 +638,407 @@ void gemm_fast(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
   }
 }
 
+// ------------------------------------------------------ persistent path (one wave per SIMD)
+// 256 x 256 output tiles (256 x 128 per weight for the gated pair) computed by 4 waves, one
+// per SIMD, each owning 128 x 128 outputs (128 x 64 per weight), on the 16 x 16 x 32 bf16
+// MFMA: per 32-wide k step a wave reads 8 weight and 8 activation fragments (16 bytes per
+// lane each) for its 64 MFMAs. Of the two bf16 MFMA shapes this one moves half the
+// accumulator data per flop (k = 32 instead of 16), and on random data the matrix cores run
+// at a clock some 15% higher with it than with 32 x 32 x 16 at the same issue rate.
+// Registers: the 64 accumulators (64 x 4 fp32) fill a0..a255, fixed AGPRs named only in
+// inline assembly (the MFMAs and the epilogue's read-out); every such statement lists them
+// as clobbered, so the compiler keeps its own values out of them and never moves them. The
+// fragments (two sets of 16) and everything else live in VGPRs.
+// The grid holds one workgroup per CU (the two 64 KB stage buffers fill its LDS); workgroup
+// b computes the tiles v = b, b + gridDim.x, ... (each XCD still walks a contiguous range of
+// the grouped tile order, 32 tiles at a time). The k stages (64 wide) of consecutive tiles
+// form one software pipeline over the two buffers: the workgroup's stage g lives in buffer
+// g % 2, and the loads of stage g + 2 go into buffer g % 2 during stage g's second k step,
+// whether g + 2 belongs to this tile or the next, so the next tile's first two stages load
+// while this tile's epilogue runs.
+// Stage g: k step 0 runs on fragments read during stage g-1 and reads those of step 1; then
+// this wave waits for its reads and for its loads of stage g+1 and meets the other waves at
+// the barrier (every wave has read stage g and every load of stage g+1 has landed); k step
+// 1 then issues the 16 loads of stage g+2 and the 16 reads of stage g+1's step 0, one of
+// each per four MFMAs. Scheduling barriers pin that placement.
+// A k extent that is an odd multiple of 32 ends with a half stage (one k step): its loads
+// take chunks 0..3 twice (in bounds; the copy is never read) and the barrier falls in the
+// middle of its k step.
+#define TSP_STR(x) #x
+#define TSP_G10(p) TSP_STR(a##p##0), TSP_STR(a##p##1), TSP_STR(a##p##2), TSP_STR(a##p##3), TSP_STR(a##p##4), \
+    TSP_STR(a##p##5), TSP_STR(a##p##6), TSP_STR(a##p##7), TSP_STR(a##p##8), TSP_STR(a##p##9)
+// a0 .. a255
+#define TSP_ACC_AGPRS "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", TSP_G10(1), TSP_G10(2), TSP_G10(3), \
+    TSP_G10(4), TSP_G10(5), TSP_G10(6), TSP_G10(7), TSP_G10(8), TSP_G10(9), TSP_G10(10), TSP_G10(11), TSP_G10(12),   \
+    TSP_G10(13), TSP_G10(14), TSP_G10(15), TSP_G10(16), TSP_G10(17), TSP_G10(18), TSP_G10(19), TSP_G10(20),         \
+    TSP_G10(21), TSP_G10(22), TSP_G10(23), TSP_G10(24), "a250", "a251", "a252", "a253", "a254", "a255"
+
+// a[R .. R+3] (+)= A-fragment x B-fragment (16 x 16 x 32). Lane l supplies row l % 16 of A
+// and column l % 16 of B, each with k = 8 (l / 16) .. + 7; the result holds rows
+// 4 (l / 16) .. + 3 of column l % 16 in lane l.
+template <int R>
+__device__ __forceinline__ void gmma(const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 a[%2:%3], %0, %1, a[%2:%3]" ::"v"(a), "v"(b), "n"(R), "n"(R + 3)
+               : TSP_ACC_AGPRS);
+}
+template <int R>
+__device__ __forceinline__ void gmma0(const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 a[%2:%3], %0, %1, 0" ::"v"(a), "v"(b), "n"(R), "n"(R + 3)
+               : TSP_ACC_AGPRS);
+}
+// a[R .. R+3] into VGPRs.
+template <int R>
+__device__ __forceinline__ f32x4 acc_read(void) {
+  float x0, x1, x2, x3;
+  asm volatile(
+      "v_accvgpr_read_b32 %0, a[%4]\n\tv_accvgpr_read_b32 %1, a[%5]\n\tv_accvgpr_read_b32 %2, a[%6]\n\t"
+      "v_accvgpr_read_b32 %3, a[%7]"
+      : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3)
+      : "n"(R), "n"(R + 1), "n"(R + 2), "n"(R + 3)
+      : TSP_ACC_AGPRS);
+  return f32x4{x0, x1, x2, x3};
+}
+// Lanes 16..31 of x trade places with lanes 0..15 of y, and lanes 48..63 of x with lanes
+// 32..47 of y (v_permlane16_swap), with the wait states around the permute.
+__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+template <bool DUAL>
+struct PGeom {
+  static constexpr int KB = 64, ROWB = KB * 2, CPR = KB / 8, RPI = 1024 / ROWB;
+  static constexpr int BM = 256, BN = DUAL ? 128 : 256, WM = 128, WN = DUAL ? 64 : 128;
+  static constexpr int NWN = BN / WN, NWAVE = 4;
+  static constexpr int NB = DUAL ? 2 : 1;
+  static constexpr int MB = WM / 16, NBK = WN / 16, NW = NB * NBK;  // activation / weight blocks of 16
+  static constexpr int ATILE = BM * KB * 2, BTILE = BN * KB * 2;
+  static constexpr int STAGE = ATILE + NB * BTILE;
+  static constexpr int AINS = ATILE / 1024 / NWAVE, BINS = BTILE / 1024 / NWAVE;
+  static_assert(MB * NW == 64 && MB + NW == 16 && AINS + NB * BINS == 16, "64 MFMAs, 16 reads, 16 loads per step");
+  // MFMA i of a k step: activation block mb = i / NW, weight block w = i % NW = (nb, nbk);
+  // its accumulator a[4 (w MB + mb) ..].
+  static constexpr int mb_of(int i) { return i / NW; }
+  static constexpr int w_of(int i) { return i % NW; }
+  static constexpr int acc_of(int i) { return 4 * (w_of(i) * MB + mb_of(i)); }
+};
+
+// Logical 16-byte chunk c of tile row r sits at physical chunk c ^ (r % 8): the 8 rows that
+// 8 consecutive lanes of a fragment read hit 8 distinct bank groups.
+__device__ __forceinline__ int swz8(int r) { return r & 7; }
+
+template <bool DUAL, int SEG, int GM, class Epi>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
+  using G = PGeom<DUAL>;
+  constexpr int KB = G::KB, ROWB = G::ROWB, CPR = G::CPR, RPI = G::RPI;
+  constexpr int BM = G::BM, BN = G::BN, WM = G::WM, WN = G::WN, NWN = G::NWN, NWAVE = G::NWAVE;
+  constexpr int NB = G::NB, MB = G::MB, NBK = G::NBK, NW = G::NW;
+  constexpr int ATILE = G::ATILE, BTILE = G::BTILE, STAGE = G::STAGE, AINS = G::AINS, BINS = G::BINS;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int total = tiles_m * tiles_n;
+  // Stages per k segment (the whole reduction, or one shard under SEG_K) and segments.
+  const int nks = (op.K + KB - 1) / KB;
+  int nseg = 1;
+  if constexpr (SEG == SEG_K) nseg = sg.count;
+  const bool khalf = (op.K % KB) != 0;
+  if ((int)blockIdx.x >= total) return;
+
+  // Tile v of the grouped order: row tile, column tile and (SEG_N) shard.
+  struct TileAt {
+    int m0, n0, j;
+  };
+  auto tile_at = [&](int v) {
+    const int t = xcd_remap(v, total);
+    const int span = GM * tiles_n;
+    const int first_m = (t / span) * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    const int in_g = t - (t / span) * span;
+    TileAt r;
+    r.m0 = (first_m + in_g % gsz) * BM;
+    int nt = in_g / gsz;
+    r.j = 0;
+    if constexpr (SEG == SEG_N) {
+      r.j = nt / sg.tn;
+      nt -= r.j * sg.tn;
+    }
+    r.n0 = nt * BN;
+    return r;
+  };
+
+  // ---- load side. Per-lane byte offsets of the load instructions for the rows of the tile
+  // the loads are working on: the current tile, or from the stage whose loads first reach
+  // into the workgroup's next tile on, that one. The k position and the operand bases are
+  // scalar. DMA instruction p of this wave covers tile rows RPI (p NWAVE + wave) + lane / CPR
+  // at physical chunk lane % CPR, i.e. logical chunk (lane % CPR) ^ swz8(row), which is the
+  // same chunk for every p (rows of one instruction step by RPI NWAVE, a multiple of 8).
+  // Rows past M or N repeat the last row.
+  auto row_of = [&](int p) { return RPI * (p * NWAVE + wave) + lane / CPR; };
+  const int lc = (lane % CPR) ^ swz8(row_of(0));
+  const uint32_t hsub = lc >= 4 ? 64u : 0u;  // bytes back to chunk c - 4 (half stages)
+  uint32_t oa[AINS], ob[BINS];
+  auto offsets = [&](int v) {
+    const TileAt tl = tile_at(v);
+#pragma unroll
+    for (int p = 0; p < AINS; ++p)
+      oa[p] = (uint32_t)min(tl.m0 + row_of(p), op.M - 1) * (uint32_t)(op.lda * 2) + 16 * lc;
+#pragma unroll
+    for (int p = 0; p < BINS; ++p)
+      ob[p] = (uint32_t)min(tl.n0 + row_of(p), op.N - 1) * (uint32_t)(op.ldb * 2) + 16 * lc;
+  };
+  const char* const abase = reinterpret_cast<const char*>(op.a);
+  // Weight bases of tile v (SEG_N: its shard's).
+  auto wbase = [&](int v, int w) -> const char* {
+    if constexpr (SEG == SEG_N) {
+      const int j = tile_at(v).j;
+      return reinterpret_cast<const char*>(w ? sg.b2[j] : sg.b[j]);
+    }
+    return reinterpret_cast<const char*>(w && DUAL ? op.b2 : op.b);
+  };
+  const char* wb = wbase(blockIdx.x, 0);
+  const char* wb2 = wbase(blockIdx.x, 1);
+  // Loads of stage kt of segment s of the loads' tile, instruction by instruction
+  // (p = 0 .. 15), into the stage buffer at LDS address la + 1 KB x wave.
+  struct Ld {
+    const char *a, *b, *b2;
+    uint32_t hm;  // ~0 for a half stage
+  };
+  auto ld_of = [&](int s, int kt) {
+    Ld l;
+    const int k0 = kt * KB;
+    const char* a = abase;
+    const char* b = wb;
+    if constexpr (SEG == SEG_K) {
+      a = abase + sg.a_col[s] * 2;
+      b = reinterpret_cast<const char*>(sg.b[s]);
+    }
+    l.a = a + (size_t)k0 * 2;
+    l.b = b + (size_t)k0 * 2;
+    l.b2 = wb2 + (size_t)k0 * 2;
+    l.hm = k0 + KB <= op.K ? 0u : 0xffffffffu;
+    return l;
+  };
+  auto dma = [&](int p, uint32_t la, const Ld& l) {
+    const uint32_t back = hsub & l.hm;
+    if (p < AINS) {
+      dma16_sbase(l.a, oa[p] - back, la + p * NWAVE * 1024);
+    } else {
+      const int q = p - AINS;
+      const int nb = q / BINS, pb = q % BINS;
+      dma16_sbase(nb ? l.b2 : l.b, ob[pb] - back, la + ATILE + nb * BTILE + pb * NWAVE * 1024);
+    }
+  };
+
+  // ---- compute side
+  // Fragment byte offsets within a stage for each 32-wide k step: row l % 16 of a 16-row
+  // block (every block starts at a multiple of 8, so the swizzle depends on l % 8 alone),
+  // logical chunk 4 ks + l / 16.
+  int fo[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) fo[ks] = l16 * ROWB + 16 * ((4 * ks + lg) ^ swz8(l16));
+  bf16x8 fa[2][MB];  // activation fragments (MFMA B operand)
+  bf16x8 fw[2][NW];  // weight fragments (MFMA A operand)
+  // Read r (0..15) of k step ks from the stage at st into register set `set`: activation
+  // block 0, the weight blocks, then activation blocks 1..7 (the order the MFMAs use them).
+  auto rd = [&](int set, const char* st, int ks, int r) {
+    if (r == 0 || r > NW) {
+      const int mb = r == 0 ? 0 : r - NW;
+      fa[set][mb] = as_bf16x8(*reinterpret_cast<const uint4*>(st + (wm * WM + 16 * mb) * ROWB + fo[ks]));
+    } else {
+      const int w = r - 1, nb = w / NBK, k = w % NBK;
+      fw[set][w] = as_bf16x8(
+          *reinterpret_cast<const uint4*>(st + ATILE + nb * BTILE + (wn * WN + 16 * k) * ROWB + fo[ks]));
+    }
+  };
+  // MFMAs lo .. hi-1 of a k step on register set `set` (zero: the tile's first step, C = 0),
+  // with, every rs-th MFMA from the first, read number (i - lo) / rs of k step rks of the
+  // stage at rst into set rset (when rs != 0), and every ds-th MFMA from the (ds / 2)-th,
+  // load number (i - lo) / ds of the stage *ld into the buffer at LDS address la (ds != 0).
+  auto step = [&](const int set, const bool zero, auto LO, auto HI, const int rs, const char* rst, const int rset,
+                  const int rks, const int ds, const Ld* ld, const uint32_t la) __attribute__((always_inline)) {
+    static_for<64>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i >= decltype(LO)::value && i < decltype(HI)::value) {
+        constexpr int j = i - decltype(LO)::value;
+        if (zero)
+          gmma0<G::acc_of(i)>(fw[set][G::w_of(i)], fa[set][G::mb_of(i)]);
+        else
+          gmma<G::acc_of(i)>(fw[set][G::w_of(i)], fa[set][G::mb_of(i)]);
+        if (rs && j % rs == 0 && j / rs < 16) rd(rset, rst, rks, j / rs);
+        if (ds && j % ds == ds / 2 && j / ds < 16) dma(j / ds, la, *ld);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I32 = std::integral_constant<int, 32>;
+  using I64 = std::integral_constant<int, 64>;
+
+  // Prologue: stages 0 and 1 of the first tile (every tile has at least two), then the
+  // first step's fragments.
+  offsets(blockIdx.x);
+  {
+    const uint32_t base = lds_addr(smem) + wave * 1024;
+    const Ld l0 = ld_of(0, 0);
+    const Ld l1 = ld_of(0, 1);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) dma(p, base, l0);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) dma(p, base + STAGE, l1);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 16; ++r) rd(0, smem, 0, r);
+
+  // Waits for this wave's reads of the stage and its loads of the next one, then meets the
+  // other waves: past it every wave has read the stage and every load of the next has landed.
+  auto sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  int g = 0;  // stages computed so far
+  for (int v = blockIdx.x; v < total; v += gridDim.x) {
+    const bool has_next = v + (int)gridDim.x < total;
+    bool moved = false;  // the load offsets point at the next tile
+    for (int s = 0; s < nseg; ++s) {
+      for (int kt = 0; kt < nks; ++kt, ++g) {
+        const char* cur = smem + (g & 1) * STAGE;
+        const char* nxt = smem + ((g + 1) & 1) * STAGE;
+        const bool first = s == 0 && kt == 0;
+        // The stage two ahead: (s2, k2) of this tile or of the next; past the workgroup's
+        // last stage, this stage again (into its own buffer, which nobody reads again).
+        int s2 = s, k2 = kt + 2;
+        bool nx = false;
+        if (k2 >= nks) {
+          k2 -= nks;
+          if (++s2 == nseg) {
+            s2 = 0;
+            nx = true;
+          }
+        }
+        if (nx && !has_next) {
+          s2 = s;
+          k2 = kt;
+          nx = false;
+        }
+        if (nx && !moved) {
+          offsets(v + gridDim.x);
+          wb = wbase(v + gridDim.x, 0);
+          wb2 = wbase(v + gridDim.x, 1);
+          moved = true;
+        }
+        const Ld l2 = ld_of(s2, k2);
+        const uint32_t la = lds_addr(cur) + wave * 1024;
+        // Settle the scalar bookkeeping here, ahead of the MFMAs, not between a barrier and
+        // the MFMAs that follow it.
+        asm volatile("" ::"s"(l2.a), "s"(l2.b), "s"(l2.b2), "s"(l2.hm), "s"(la));
+        if (kt + 1 < nks || !khalf) {
+          if (first) step(0, true, I0{}, I64{}, 4, cur, 1, 1, 0, nullptr, 0u);
+          else step(0, false, I0{}, I64{}, 4, cur, 1, 1, 0, nullptr, 0u);
+          sync();
+          step(1, false, I0{}, I64{}, 4, nxt, 0, 0, 4, &l2, la);
+        } else {  // half stage: one k step, the barrier in its middle
+          // Its second half still uses every weight fragment of set 0, so the next stage's
+          // first fragments go to set 1 and move to set 0 afterwards.
+          step(0, false, I0{}, I32{}, 0, cur, 0, 0, 0, nullptr, 0u);
+          sync();
+          step(0, false, I32{}, I64{}, 2, nxt, 1, 0, 2, &l2, la);
+#pragma unroll
+          for (int w = 0; w < NW; ++w) fw[0][w] = fw[1][w];
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) fa[0][mb] = fa[1][mb];
+        }
+      }
+    }
+    // Epilogue: the accumulators of the last MFMAs are read many slots later; the nops
+    // cover the read-after-write wait of the first ones read.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: TSP_ACC_AGPRS);
+    const TileAt tl = tile_at(v);
+    Epi e = epi;
+    if constexpr (SEG == SEG_N) e.shift_cols(tl.j * sg.out_col);
+    const int m0 = tl.m0, n0 = tl.n0;
+    // Activation block mb, weight blocks 2 q and 2 q + 1 of each weight: lane l holds outputs
+    // (m = l % 16, n = 4 (l / 16) .. + 3) of each block.
+    auto block = [&](auto I) __attribute__((always_inline)) {
+      constexpr int mb = decltype(I)::value / (NBK / 2), q = decltype(I)::value % (NBK / 2);
+      constexpr int k0 = 2 * q, k1 = 2 * q + 1;
+      const int m = m0 + wm * WM + 16 * mb + l16;
+      const f32x4 g0 = acc_read<4 * (k0 * MB + mb)>();
+      const f32x4 g1 = acc_read<4 * (k1 * MB + mb)>();
+      f32x4 u0 = g0, u1 = g1;
+      if constexpr (DUAL) {
+        u0 = acc_read<4 * ((NBK + k0) * MB + mb)>();
+        u1 = acc_read<4 * ((NBK + k1) * MB + mb)>();
+      }
+      const int nblk = n0 + wn * WN + 16 * k0;  // first column of the block pair
+      if constexpr (Epi::kWide) {
+        // Pack each block's 4 columns to bf16, then trade halves between lane groups so
+        // that lane group g holds columns 8 g' .. 8 g' + 7 of the pair (g' = 2 (g % 2) +
+        // g / 2 ... see below) for one 16-byte store.
+        uint2 p0, p1;
+        if constexpr (DUAL) {
+          p0 = Epi::pack(g0, u0);
+          p1 = Epi::pack(g1, u1);
+        } else {
+          p0 = Epi::pack(g0);
+          p1 = Epi::pack(g1);
+        }
+        // After the swaps: group 0 holds block 0 columns 0..7, group 1 block 1 columns
+        // 0..7, group 2 block 0 columns 8..15, group 3 block 1 columns 8..15.
+        uint32_t x0 = p0.x, x1 = p0.y, y0 = p1.x, y1 = p1.y;
+        swap16(x0, y0);
+        swap16(x1, y1);
+        // x now holds the lower 4 columns and y the upper 4 of the lane's 8.
+        const uint4 w = make_uint4(x0, x1, y0, y1);
+        const int col = nblk + 16 * (lg & 1) + 8 * (lg >> 1);
+        e.store8(m, col, w, op.M, op.N);
+      } else {
+        const int n = nblk + 4 * lg;
+        if constexpr (DUAL) {
+          e(m, n, g0, u0, op.M, op.N);
+          e(m, n + 16, g1, u1, op.M, op.N);
+        } else {
+          e(m, n, g0, op.M, op.N);
+          e(m, n + 16, g1, op.M, op.N);
+        }
+      }
+    };
+    static_for<MB * NBK / 2>(block);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the last stage's extra loads land before the LDS is freed
+}
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <int BM, int BN, bool DUAL, bool VEC, class Epi>
@@ -656,6 +1062,26 @@ hipError_t run_fast(const Operands& op, const Epi& epi, hipStream_t s, SegArg<SE
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
   hipLaunchKernelGGL((gemm_fast<BM, BN, WM, WN, DUAL, SEG, KB, GM, Epi>), dim3(tm * tn), dim3(threads), 0, s, op, epi, tm,
                      tn, sg);
+  return hipGetLastError();
+}
+
+// The persistent kernel takes k extents (per shard under SEG_K) that are multiples of 32 and
+// hold at least two 64-wide stages.
+inline bool persist_ok(const Operands& op) { return op.K % 32 == 0 && op.K > 64; }
+
+template <bool DUAL, int SEG = SEG_NONE, int GM = kGroupM, class Epi>
+hipError_t run_persist(const Operands& op, const Epi& epi, hipStream_t s, SegArg<SEG> sg = {}) {
+  constexpr int BM = 256, BN = DUAL ? 128 : 256, KB = 64;
+  const int tm = (op.M + BM - 1) / BM;
+  int tn = (op.N + BN - 1) / BN;
+  if constexpr (SEG == SEG_N) {
+    sg.tn = tn;
+    tn *= sg.count;
+  }
+  if constexpr (SEG == SEG_K) sg.nks = (op.K + KB - 1) / KB;
+  const int total = tm * tn;
+  const int grid = total < device_cus() ? total : device_cus();
+  hipLaunchKernelGGL((gemm_p<DUAL, SEG, GM, Epi>), dim3(grid), dim3(256), 0, s, op, epi, tm, tn, sg);
   return hipGetLastError();
 }
 
@@ -702,7 +1128,9 @@ hipError_t run_single(const Operands& op, const Epi& epi, hipStream_t s) {
     return vec ? run_tiles<128, 128, false, true>(op, epi, s) : run_tiles<128, 128, false, false>(op, epi, s);
   }
   switch (choose_tile(op.M, op.N)) {
-    case Tile::k256x256: return run_fast<256, 256, 128, 64, false>(op, epi, s);
+    case Tile::k256x256:
+      if (persist_ok(op)) return run_persist<false>(op, epi, s);
+      return run_fast<256, 256, 128, 64, false>(op, epi, s);
     case Tile::k256x128: return run_fast<256, 128, 64, 64, false>(op, epi, s);
     default: return run_fast<128, 128, 64, 64, false>(op, epi, s);
   }
@@ -716,7 +1144,10 @@ hipError_t run_dual(const Operands& op, const Epi& epi, hipStream_t s) {
     return vec ? run_tiles<128, 64, true, true>(op, epi, s) : run_tiles<128, 64, true, false>(op, epi, s);
   }
   const int64_t big = (int64_t)((op.M + 255) / 256) * ((op.N + 127) / 128);
-  if (big >= kBigTileMin) return run_fast<256, 128, 128, 32, true>(op, epi, s);
+  if (big >= kBigTileMin) {
+    if (persist_ok(op)) return run_persist<true>(op, epi, s);
+    return run_fast<256, 128, 128, 32, true>(op, epi, s);
+  }
   return run_fast<128, 64, 64, 32, true>(op, epi, s);
 }
 
@@ -769,13 +1200,16 @@ hipError_t launch_wo_pair(const void* o, const void* w_o_a, const void* w_o_b, i
     if (hipError_t e = launch_wo_group(o, w_o_a, group, groups, acc, out, M, d, first ? 0 : 1, 3, stream)) return e;
     return launch_wo_group(o, w_o_b, group + 1, groups, acc, out, M, d, last ? 2 : 1, 3, stream);
   }
+  const bool big = choose_tile(M, d) == Tile::k256x256;
   if (last) {
     const EpiAccBf16 epi{acc, static_cast<bf16_t*>(out), d, first};
-    if (choose_tile(M, d) == Tile::k256x256) return run_fast<256, 256, 128, 64, false, SEG_K>(op, epi, stream, sg);
+    if (big && persist_ok(op)) return run_persist<false, SEG_K>(op, epi, stream, sg);
+    if (big) return run_fast<256, 256, 128, 64, false, SEG_K>(op, epi, stream, sg);
     return run_fast<128, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
   }
   const EpiAcc epi{acc, d, first ? 0 : 1};
-  if (choose_tile(M, d) == Tile::k256x256) return run_fast<256, 256, 128, 64, false, SEG_K>(op, epi, stream, sg);
+  if (big && persist_ok(op)) return run_persist<false, SEG_K>(op, epi, stream, sg);
+  if (big) return run_fast<256, 256, 128, 64, false, SEG_K>(op, epi, stream, sg);
   return run_fast<128, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
 }
 
@@ -827,7 +1261,10 @@ hipError_t launch_gate_up_ring(const void* x, const void* const* w1, const void*
   op.b = sg.b[0];
   op.b2 = sg.b2[0];
   const int64_t big = (int64_t)((M + 255) / 256) * D * ((Fs + 127) / 128);
-  if (big >= kBigTileMin) return run_fast<256, 128, 128, 32, true, SEG_N>(op, epi, stream, sg);
+  if (big >= kBigTileMin) {
+    if (persist_ok(op)) return run_persist<true, SEG_N>(op, epi, stream, sg);
+    return run_fast<256, 128, 128, 32, true, SEG_N>(op, epi, stream, sg);
+  }
   return run_fast<128, 64, 64, 32, true, SEG_N>(op, epi, stream, sg);
 }
 
@@ -848,7 +1285,9 @@ hipError_t launch_down_ring(const void* h, int64_t ldh, int64_t ldseg, const voi
   // row panels is read from HBM about once per group; the weights, which fit, are re-read
   // from the MALL instead (8-row groups: 3.76 ms of MLP, 2-row groups: 3.68 ms).
   switch (choose_tile(M, N)) {
-    case Tile::k256x256: return run_fast<256, 256, 128, 64, false, SEG_K, 2>(op, epi, stream, sg);
+    case Tile::k256x256:
+      if (persist_ok(op)) return run_persist<false, SEG_K, 2>(op, epi, stream, sg);
+      return run_fast<256, 256, 128, 64, false, SEG_K, 2>(op, epi, stream, sg);
     case Tile::k256x128: return run_fast<256, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
     default: return run_fast<128, 128, 64, 64, false, SEG_K>(op, epi, stream, sg);
   }
