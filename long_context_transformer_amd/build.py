@@ -122,6 +122,13 @@ def build(verbose=False, resource_usage=False):
     return LIB
 
 
+def device_asm(src, out_path, verbose=False):
+    """gfx950 assembly of one source's device code, compiled with the library's own flags."""
+    flags = [*HIPCC_FLAGS, *SOURCE_FLAGS.get(src, [])]
+    _run([_hipcc(), *flags, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out_path], verbose)
+    return out_path
+
+
 SAN_BUILD = os.path.join(PKG, "_build_san")
 SAN_LIB = os.path.join(SAN_BUILD, "libtsp.so")
 # Host-side sanitizers for the C ABI's host code (argument checks, workspace layout, launch

@@ -16,6 +16,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace tsp {
 
 typedef uint16_t bf16_t;  // storage type of a bfloat16 in global memory
@@ -86,6 +89,22 @@ __device__ __forceinline__ float max_swap32(float v) {
   uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1" : "+v"(x), "+v"(y));
   return __builtin_bit_cast(float, x);
+}
+
+// Lanes 16..31 of x trade places with lanes 0..15 of y, and lanes 48..63 of x with lanes
+// 32..47 of y (v_permlane16_swap), with the wait states around the permute.
+__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // s_waitcnt immediate that waits until at most `vm` vector-memory loads of this wave are

@@ -32,9 +32,6 @@
 #include "tsp_device.h"
 #include "tsp_internal.h"
 
-#include <type_traits>
-#include <utility>
-
 namespace tsp {
 namespace {
 
@@ -697,21 +694,6 @@ __device__ __forceinline__ f32x4 acc_read(void) {
       : "n"(R), "n"(R + 1), "n"(R + 2), "n"(R + 3)
       : TSP_ACC_AGPRS);
   return f32x4{x0, x1, x2, x3};
-}
-// Lanes 16..31 of x trade places with lanes 0..15 of y, and lanes 48..63 of x with lanes
-// 32..47 of y (v_permlane16_swap), with the wait states around the permute.
-__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
-}
-
-// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 int device_cus() {
