@@ -87,10 +87,22 @@ __device__ __forceinline__ void store8_bf16(bf16_t* p, const uint4& w, int valid
   }
 }
 
+// Unchecked stores for whole tiles (the persistent kernel): row(m) does the per-row address
+// work once, put8 / put4 store 8 bf16 or 4 fp32 columns at n without bounds or alignment
+// tests; vec_ok says whether the destination takes 16-byte (bf16) or 16-byte fp32 stores at
+// every multiple of 8 (4) columns.
 struct EpiBf16 {
   static constexpr bool kWide = true;
   bf16_t* c;
   int64_t ldc;
+  struct Row {
+    bf16_t* p;
+  };
+  __device__ __forceinline__ bool vec_ok() const { return ((reinterpret_cast<uintptr_t>(c) & 15u) == 0) && ldc % 8 == 0; }
+  __device__ __forceinline__ Row row(int m) const { return Row{c + (int64_t)m * ldc}; }
+  __device__ __forceinline__ void put8(const Row& r, int n, const uint4& w) const {
+    *reinterpret_cast<uint4*>(r.p + n) = w;
+  }
   __device__ __forceinline__ static uint2 pack(const f32x4& v) { return pack_bf16x4(v[0], v[1], v[2], v[3]); }
   __device__ __forceinline__ void store8(int m, int n, const uint4& w, int M, int N) const {
     if (m >= M || n >= N) return;
@@ -119,6 +131,23 @@ struct EpiQKV {
   int64_t C;   // zigzag chunk length
   int rank, D;
   int64_t S;
+  struct Row {
+    bf16_t *q, *k, *v;  // row m's Q row and its K/V rows, at column col0
+  };
+  __device__ __forceinline__ bool vec_ok() const {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v);
+    return (a & 15u) == 0 && d % 8 == 0 && col0 % 8 == 0 && dg % 8 == 0;
+  }
+  __device__ __forceinline__ Row row(int m) const {
+    const int b = m / R;
+    const int64_t kv = ((int64_t)b * S + zigzag_pos(m - b * R, C, rank, D)) * d + col0;
+    return Row{q ? q + (int64_t)m * d + col0 : nullptr, k + kv, v + kv};
+  }
+  __device__ __forceinline__ void put8(const Row& r, int n, const uint4& w) const {
+    const int which = (n >= dg) + (n >= 2 * dg);
+    bf16_t* p = which == 0 ? r.q : which == 1 ? r.k : r.v;
+    if (p) *reinterpret_cast<uint4*>(p + (n - which * dg)) = w;
+  }
   __device__ __forceinline__ void operator()(int m, int n, const f32x4& val, int M, int N) const {
     if (m >= M || n >= N) return;
     const int which = n / dg;
@@ -155,6 +184,14 @@ struct EpiSwiGLU {
   static constexpr bool kWide = true;
   bf16_t* h;
   int64_t ldh;
+  struct Row {
+    bf16_t* p;
+  };
+  __device__ __forceinline__ bool vec_ok() const { return ((reinterpret_cast<uintptr_t>(h) & 15u) == 0) && ldh % 8 == 0; }
+  __device__ __forceinline__ Row row(int m) const { return Row{h + (int64_t)m * ldh}; }
+  __device__ __forceinline__ void put8(const Row& r, int n, const uint4& w) const {
+    *reinterpret_cast<uint4*>(r.p + n) = w;
+  }
   __device__ __forceinline__ void shift_cols(int64_t c) { h += c; }
   __device__ __forceinline__ static float silu(float g) { return g / (1.0f + __expf(-g)); }
   __device__ __forceinline__ static uint2 pack(const f32x4& g, const f32x4& u) {
@@ -187,6 +224,19 @@ struct EpiAccBf16 {
   bf16_t* out;
   int64_t ld;
   int first;
+  struct Row {
+    const float* a;
+    bf16_t* o;
+  };
+  __device__ __forceinline__ bool vec_ok() const {
+    return ((reinterpret_cast<uintptr_t>(acc) & 15u) == 0) && ((reinterpret_cast<uintptr_t>(out) & 7u) == 0) && ld % 4 == 0;
+  }
+  __device__ __forceinline__ Row row(int m) const { return Row{acc + (int64_t)m * ld, out + (int64_t)m * ld}; }
+  __device__ __forceinline__ void put4(const Row& r, int n, const f32x4& v) const {
+    f32x4 o = v;
+    if (!first) o += *reinterpret_cast<const f32x4*>(r.a + n);
+    *reinterpret_cast<uint2*>(r.o + n) = pack_bf16x4(o[0], o[1], o[2], o[3]);
+  }
   __device__ __forceinline__ void operator()(int m, int n, const f32x4& v, int M, int N) const {
     if (m >= M || n >= N) return;
     f32x4 o = v;
@@ -200,6 +250,16 @@ struct EpiAcc {
   float* c;
   int64_t ldc;
   int accumulate;
+  struct Row {
+    float* p;
+  };
+  __device__ __forceinline__ bool vec_ok() const { return ((reinterpret_cast<uintptr_t>(c) & 15u) == 0) && ldc % 4 == 0; }
+  __device__ __forceinline__ Row row(int m) const { return Row{c + (int64_t)m * ldc}; }
+  __device__ __forceinline__ void put4(const Row& r, int n, const f32x4& v) const {
+    f32x4 o = v;
+    if (accumulate) o += *reinterpret_cast<const f32x4*>(r.p + n);
+    *reinterpret_cast<f32x4*>(r.p + n) = o;
+  }
   __device__ __forceinline__ void operator()(int m, int n, const f32x4& v, int M, int N) const {
     if (m >= M || n >= N) return;
     float* p = c + (int64_t)m * ldc + n;
@@ -971,52 +1031,65 @@ void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
     if constexpr (SEG == SEG_N) e.shift_cols(tl.j * sg.out_col);
     const int m0 = tl.m0, n0 = tl.n0;
     // Activation block mb, weight blocks 2 q and 2 q + 1 of each weight: lane l holds outputs
-    // (m = l % 16, n = 4 (l / 16) .. + 3) of each block.
-    auto block = [&](auto I) __attribute__((always_inline)) {
-      constexpr int mb = decltype(I)::value / (NBK / 2), q = decltype(I)::value % (NBK / 2);
-      constexpr int k0 = 2 * q, k1 = 2 * q + 1;
-      const int m = m0 + wm * WM + 16 * mb + l16;
-      const f32x4 g0 = acc_read<4 * (k0 * MB + mb)>();
-      const f32x4 g1 = acc_read<4 * (k1 * MB + mb)>();
-      f32x4 u0 = g0, u1 = g1;
-      if constexpr (DUAL) {
-        u0 = acc_read<4 * ((NBK + k0) * MB + mb)>();
-        u1 = acc_read<4 * ((NBK + k1) * MB + mb)>();
-      }
-      const int nblk = n0 + wn * WN + 16 * k0;  // first column of the block pair
-      if constexpr (Epi::kWide) {
-        // Pack each block's 4 columns to bf16, then trade halves between lane groups so
-        // that lane group g holds columns 8 g' .. 8 g' + 7 of the pair (g' = 2 (g % 2) +
-        // g / 2 ... see below) for one 16-byte store.
-        uint2 p0, p1;
-        if constexpr (DUAL) {
-          p0 = Epi::pack(g0, u0);
-          p1 = Epi::pack(g1, u1);
-        } else {
-          p0 = Epi::pack(g0);
-          p1 = Epi::pack(g1);
-        }
-        // After the swaps: group 0 holds block 0 columns 0..7, group 1 block 1 columns
-        // 0..7, group 2 block 0 columns 8..15, group 3 block 1 columns 8..15.
-        uint32_t x0 = p0.x, x1 = p0.y, y0 = p1.x, y1 = p1.y;
-        swap16(x0, y0);
-        swap16(x1, y1);
-        // x now holds the lower 4 columns and y the upper 4 of the lane's 8.
-        const uint4 w = make_uint4(x0, x1, y0, y1);
-        const int col = nblk + 16 * (lg & 1) + 8 * (lg >> 1);
-        e.store8(m, col, w, op.M, op.N);
-      } else {
-        const int n = nblk + 4 * lg;
-        if constexpr (DUAL) {
-          e(m, n, g0, u0, op.M, op.N);
-          e(m, n + 16, g1, u1, op.M, op.N);
-        } else {
-          e(m, n, g0, op.M, op.N);
-          e(m, n + 16, g1, op.M, op.N);
-        }
-      }
+    // (m = l % 16, n = 4 (l / 16) .. + 3) of each block. A tile wholly inside C whose
+    // destination takes vector stores (FAST) does each row's address work once and stores
+    // without per-store tests.
+    auto tile = [&](auto FAST) __attribute__((always_inline)) {
+      constexpr bool fast = decltype(FAST)::value;
+      static_for<MB>([&](auto MBI) __attribute__((always_inline)) {
+        constexpr int mb = decltype(MBI)::value;
+        const int m = m0 + wm * WM + 16 * mb + l16;
+        typename Epi::Row r{};
+        if constexpr (fast) r = e.row(m);
+        static_for<NBK / 2>([&](auto QI) __attribute__((always_inline)) {
+          constexpr int q = decltype(QI)::value;
+          constexpr int k0 = 2 * q, k1 = 2 * q + 1;
+          const f32x4 g0 = acc_read<4 * (k0 * MB + mb)>();
+          const f32x4 g1 = acc_read<4 * (k1 * MB + mb)>();
+          f32x4 u0 = g0, u1 = g1;
+          if constexpr (DUAL) {
+            u0 = acc_read<4 * ((NBK + k0) * MB + mb)>();
+            u1 = acc_read<4 * ((NBK + k1) * MB + mb)>();
+          }
+          const int nblk = n0 + wn * WN + 16 * k0;  // first column of the block pair
+          if constexpr (Epi::kWide) {
+            // Pack each block's 4 columns to bf16, then trade halves between lane groups:
+            // after the swaps group 0 holds block 0 columns 0..7, group 1 block 1 columns
+            // 0..7, group 2 block 0 columns 8..15, group 3 block 1 columns 8..15, with x the
+            // lower 4 and y the upper 4 of the lane's 8: one 16-byte store each.
+            uint2 p0, p1;
+            if constexpr (DUAL) {
+              p0 = Epi::pack(g0, u0);
+              p1 = Epi::pack(g1, u1);
+            } else {
+              p0 = Epi::pack(g0);
+              p1 = Epi::pack(g1);
+            }
+            uint32_t x0 = p0.x, x1 = p0.y, y0 = p1.x, y1 = p1.y;
+            swap16(x0, y0);
+            swap16(x1, y1);
+            const uint4 w = make_uint4(x0, x1, y0, y1);
+            const int col = nblk + 16 * (lg & 1) + 8 * (lg >> 1);
+            if constexpr (fast) e.put8(r, col, w);
+            else e.store8(m, col, w, op.M, op.N);
+          } else {
+            const int n = nblk + 4 * lg;
+            if constexpr (DUAL) {
+              e(m, n, g0, u0, op.M, op.N);
+              e(m, n + 16, g1, u1, op.M, op.N);
+            } else if constexpr (fast) {
+              e.put4(r, n, g0);
+              e.put4(r, n + 16, g1);
+            } else {
+              e(m, n, g0, op.M, op.N);
+              e(m, n + 16, g1, op.M, op.N);
+            }
+          }
+        });
+      });
     };
-    static_for<MB * NBK / 2>(block);
+    if (m0 + BM <= op.M && n0 + BN <= op.N && e.vec_ok()) tile(std::true_type{});
+    else tile(std::false_type{});
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the last stage's extra loads land before the LDS is freed
 }
