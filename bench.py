@@ -2,6 +2,7 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rank R]
                 [--no-cpu-baseline] [--cpu-rows N] [--calib-copy] [--sweep PATH]
+                [--gemm-yardstick] [--streamed] [--chunked] [--memory PATH] [--attn-bwd] [--layer-bwd]
 
 A step is one tsp_layer_fwd call: QKV projection of the rank's zigzag shard, causal
 attention against the full-sequence K/V, W_O, and the D-shard SwiGLU ring accumulated in
@@ -443,6 +444,44 @@ def cpu_baseline(w, inputs, rank, rows_sample):
             "wall_s": round(dt, 2)}
 
 
+def gemm_yardstick(st, w, phases, reps=10, warmup=3):
+    """The layer's projections as plain 2-D torch.matmul calls (hipBLASLt on ROCm) on the same
+    bf16 operands, each timed alone (median of `reps`, HIP events): QKV x W_qkv^T, W_O, the
+    gate/up pair of all D shards as one [2F, d] weight, and the down projection over all F
+    columns. They do no zigzag scatter, SwiGLU or fp32 accumulation, so they are a yardstick
+    for the matrix work only, not the same computation."""
+    import torch
+    dev = st["dev"]
+    M, d, F = w.B * (w.S // w.D), w.d_model, w.ffn
+    x = st["xs"].reshape(M, d)
+    a_f = torch.randn((M, F), device="cuda").to(torch.bfloat16)
+    w13 = torch.cat([dev["w1"], dev["w3"]], 0).contiguous()
+    cases = {"qkv": (x, dev["w_qkv"]), "w_o": (x, dev["w_o"]), "gate_up": (x, w13), "down": (a_f, dev["w2"])}
+    res = {}
+    for name, (a, b) in cases.items():
+        bt = b.t()
+        for _ in range(warmup):
+            torch.matmul(a, bt)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, bt)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        fl = 2.0 * a.shape[0] * a.shape[1] * b.shape[0]
+        res[name] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                     "shape_mnk": [a.shape[0], b.shape[0], a.shape[1]]}
+    res["library_phases_ms"] = {k: round(phases[k], 4) for k in ("qkv", "w_o", "mlp")}
+    res["matmul_mlp_ms"] = round(res["gate_up"]["ms"] + res["down"]["ms"], 4)
+    del a_f, w13
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -465,6 +504,9 @@ def main():
                     help="run one 256 MiB plain copy kernel first (counter calibration)")
     ap.add_argument("--sweep", default=None, help="also time every workload (and every rank of the "
                     "S=32K one) and write one JSON line each to this file")
+    ap.add_argument("--gemm-yardstick", action="store_true",
+                    help="also time the layer's four projections as plain torch.matmul (hipBLASLt) "
+                    "on the same operands, beside this library's phases")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -518,6 +560,11 @@ def main():
         layer_bwd = time_layer_bwd(st, w, args.rank)
         print("# layer backward " + json.dumps(layer_bwd), file=sys.stderr, flush=True)
 
+    yard = None
+    if args.gemm_yardstick:
+        yard = gemm_yardstick(st, w, phases)
+        print("# gemm yardstick " + json.dumps(yard), file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, st["inputs"], args.rank, args.cpu_rows)
@@ -562,6 +609,8 @@ def main():
         out["attention_backward"] = attn_bwd
     if layer_bwd:
         out["layer_backward"] = layer_bwd
+    if yard:
+        out["gemm_yardstick"] = yard
     print(json.dumps(out), flush=True)
 
     if args.memory:
