@@ -201,7 +201,8 @@ TSP_API int tsp_attn_bwd(const void* q, const void* k_full, const void* v_full, 
                          int32_t head_dim, float scale, void* ws, size_t ws_bytes,
                          tsp_stream_t stream);
 
-/* Workspace bytes tsp_mlp_shard_accum needs for M rows and shard width Fs. */
+/* Workspace bytes tsp_mlp_shard_accum needs for M rows and shard width Fs: the gated hidden,
+ * bf16 [M, round_up(Fs, 64)]. */
 TSP_API size_t tsp_mlp_workspace_size(int64_t M, int32_t Fs);
 
 /*
@@ -232,7 +233,7 @@ TSP_API int tsp_mlp_shard_accum(const void* x, const void* w1_j, const void* w3_
  * device. A caller that must not see that happen, e.g. before a graph capture, makes one
  * call first (M = 0 does not count: it returns before any HIP call).
  *   Limit: tsp_mlp_workspace_size(M, Fs) <= tsp_mlp_noalloc_max_bytes(), e.g. at most
- *   24385 rows at the 7B shard width Fs = 1376; larger calls return TSP_ERR_WORKSPACE
+ *   23831 rows at the 7B shard width Fs = 1376; larger calls return TSP_ERR_WORKSPACE
  *   before any HIP call (the rows are independent, so a caller may split them).
  *   The stream must belong to the current device. Every call on one GPU shares that GPU's
  *   scratch: calls that overlap on one GPU (different streams, host threads or graphs
@@ -246,7 +247,7 @@ TSP_API int tsp_mlp_shard_accum_noalloc(const void* x, const void* w1_j, const v
 
 /* Workspace bytes tsp_layer_fwd needs for `desc` (0 if desc is invalid): Q and O of the
  * rank, bf16 [B, 2C, d] each, and the gated hidden of all D shards, bf16
- * [B*2C, D * round_up(F/D, 8)], in that order, each starting at a multiple of 256 bytes
+ * [B*2C, D * round_up(F/D, 64)], in that order, each starting at a multiple of 256 bytes
  * (Q at offset 0, O at round_up(B*2C*d*2, 256)). After a call O holds the rank's attention
  * output, bf16 [B, 2C, H, hd] in local row order. */
 TSP_API size_t tsp_layer_workspace_size(const tsp_layer_desc* desc);
@@ -319,7 +320,7 @@ TSP_API int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const
  * on first use, never freed); calls that overlap on the same streams from different
  * threads are not supported.
  * Workspace (tsp_layer_streamed_workspace_size; 0 if desc is invalid): Q and O bf16
- * [B 2C, d] each, the gated hidden of one shard bf16 [B 2C, Fp], two attention slots, two
+ * [B 2C, d] each, the gated hidden of one shard bf16 [B 2C, round_up(Fs, 64)], two attention slots, two
  * MLP slots and, when D is odd, the fp32 O and log-sum-exp of the last group's attention
  * over keys [0, S/2) and [S/2, S) (merged into O).
  * Errors: as tsp_layer_fwd; TSP_ERR_SHAPE if H % D != 0 or n_streams is not 1 or 4.

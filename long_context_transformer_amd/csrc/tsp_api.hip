@@ -83,7 +83,13 @@ hipEvent_t* timing_slot() {
   return &g_tm_ev[(size_t)(g_tm_used++) * (kPhases + 1)];
 }
 
-size_t mlp_ws_bytes(int64_t M, int64_t Fs) { return round_up((size_t)M * (size_t)round_up((size_t)Fs, 8) * 2, kAlign); }
+// Row stride (elements) of one shard's block of the gated hidden: F/D rounded up to 64, so
+// each row and each shard block starts on a 128-byte line and every 64-wide k stage of the
+// down projection reads whole lines (with F/D = 1376, an odd multiple of 32, every other
+// block would start mid-line; 0.1 ms of the 7B S=128K MLP).
+int64_t hidden_ld(int64_t Fs) { return (int64_t)round_up((size_t)Fs, 64); }
+
+size_t mlp_ws_bytes(int64_t M, int64_t Fs) { return round_up((size_t)M * (size_t)hidden_ld(Fs) * 2, kAlign); }
 
 // Scratch of tsp_mlp_shard_accum_noalloc: the gated hidden of one ring step. A device global,
 // so every GPU the library runs on holds its own copy from the module's load until the
@@ -126,7 +132,7 @@ int check_mlp_step(const void* x, const void* w1_j, const void* w3_j, const void
 // The two launches of one ring step: gated hidden into h, then its down projection into acc.
 int launch_mlp_step(const void* x, const void* w1_j, const void* w3_j, const void* w2_j, int64_t ld_w2, float* acc,
                     int64_t M, int32_t d, int32_t Fs, int32_t accumulate, void* h, hipStream_t s) {
-  const int64_t ldh = (int64_t)round_up((size_t)Fs, 8);
+  const int64_t ldh = hidden_ld(Fs);
   if (int rc = hip_status(tsp::launch_gate_up(x, d, w1_j, w3_j, d, h, ldh, (int)M, Fs, d, s), "gate/up launch"))
     return rc;
   if (int rc = hip_status(tsp::launch_down_acc(h, ldh, w2_j, ld_w2, acc, d, (int)M, d, Fs, accumulate ? 1 : 0, s),
@@ -357,8 +363,8 @@ LayerCarve carve(const tsp_layer_desc* d) {
   c.q_off = 0;
   c.o_off = act;
   c.h_off = 2 * act;
-  // Gated hidden of all D shards: [M, D * round_up(F/D, 8)] bf16.
-  c.total = 2 * act + mlp_ws_bytes((int64_t)M, (int64_t)d->fold * round_up((size_t)(d->ffn / d->fold), 8));
+  // Gated hidden of all D shards: [M, D * hidden_ld(F/D)] bf16.
+  c.total = 2 * act + round_up(M * (size_t)d->fold * (size_t)hidden_ld(d->ffn / d->fold) * 2, kAlign);
   return c;
 }
 
@@ -394,7 +400,7 @@ int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const void* w
   const int M = (int)(B * (S / D));
   const int Fs = desc->ffn / D;
   const int64_t ldw2 = desc->w2_ld ? desc->w2_ld : Fs;
-  const int64_t ldseg = (int64_t)round_up((size_t)Fs, 8);  // H columns per shard block
+  const int64_t ldseg = hidden_ld(Fs);  // H columns per shard block
   const int64_t ldh = ldseg * D;
   char* base = static_cast<char*>(ws);
   void* q = base + c.q_off;
@@ -637,7 +643,8 @@ int stream_events(hipEvent_t** out, int n) {
 struct StreamedCarve {
   size_t q_off, o_off, h_off, slot_a[2], slot_m[2], part, total;
   size_t attn_shard, mlp_shard;  // elements of one packed shard
-  int64_t fp;                    // W2 row stride / hidden row stride in a packed MLP shard
+  int64_t fp;                    // W2 row stride in a packed MLP shard
+  int64_t fh;                    // row stride of the gated hidden
 };
 
 StreamedCarve carve_streamed(const tsp_layer_desc* d) {
@@ -647,6 +654,7 @@ StreamedCarve carve_streamed(const tsp_layer_desc* d) {
   const size_t Fs = (size_t)(d->ffn / d->fold);
   StreamedCarve c;
   c.fp = (int64_t)round_up(Fs, 8);
+  c.fh = hidden_ld((int64_t)Fs);
   c.attn_shard = 4 * dg * dm;
   c.mlp_shard = (2 * Fs + (size_t)c.fp) * dm;
   const size_t act = round_up(M * dm * 2, kAlign);
@@ -838,9 +846,9 @@ int tsp_layer_fwd_streamed(const tsp_layer_desc* desc, const void* x_shard, cons
     const tsp::bf16_t* w3 = slot_m[sl] + (size_t)Fs * d;
     const tsp::bf16_t* w2 = slot_m[sl] + 2 * (size_t)Fs * d;
     if (int rc = wait(s0, m_full[sl])) return rc;
-    if (int rc = hip_status(tsp::launch_gate_up(attn_out, d, w1, w3, d, hbuf, c.fp, M, Fs, d, s0), "gate/up launch"))
+    if (int rc = hip_status(tsp::launch_gate_up(attn_out, d, w1, w3, d, hbuf, c.fh, M, Fs, d, s0), "gate/up launch"))
       return rc;
-    if (int rc = hip_status(tsp::launch_down_acc(hbuf, c.fp, w2, c.fp, mlp_out, d, M, d, Fs, t > 0 ? 1 : 0, s0),
+    if (int rc = hip_status(tsp::launch_down_acc(hbuf, c.fh, w2, c.fp, mlp_out, d, M, d, Fs, t > 0 ? 1 : 0, s0),
                             "down projection launch"))
       return rc;
     if (t + 2 < D) {

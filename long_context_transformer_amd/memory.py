@@ -58,8 +58,13 @@ class Shape:
 
     @property
     def Fp(self):
-        """F/D rounded up to a multiple of 8 (row stride of the gated hidden)."""
+        """F/D rounded up to a multiple of 8 (W2 row stride in a packed MLP shard)."""
         return _rup(self.Fs, 8)
+
+    @property
+    def Fh(self):
+        """F/D rounded up to a multiple of 64 (row stride of one shard's gated hidden)."""
+        return _rup(self.Fs, 64)
 
     @property
     def weight_elems(self):
@@ -75,7 +80,7 @@ def shape_of(w):
 def layer_workspace(s):
     """tsp_layer_workspace_size: Q, O bf16 [M, d]; gated hidden of all D shards."""
     act = _rup(s.M * s.d * BF16, ALIGN)
-    return 2 * act + _rup(s.M * s.D * s.Fp * BF16, ALIGN)
+    return 2 * act + _rup(s.M * s.D * s.Fh * BF16, ALIGN)
 
 
 def streamed_workspace(s):
@@ -85,7 +90,7 @@ def streamed_workspace(s):
     dg = s.d // s.D
     hg = s.H // s.D
     act = _rup(s.M * s.d * BF16, ALIGN)
-    hid = _rup(s.M * s.Fp * BF16, ALIGN)
+    hid = _rup(s.M * s.Fh * BF16, ALIGN)
     slot_a = _rup(4 * dg * s.d * BF16, ALIGN)
     slot_m = _rup((2 * s.Fs + s.Fp) * s.d * BF16, ALIGN)
     part = _rup(2 * s.M * dg * F32, ALIGN) + _rup(2 * s.M * hg * F32, ALIGN)

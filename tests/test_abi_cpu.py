@@ -135,7 +135,7 @@ def test_mlp_noalloc_errors():
     assert f(A, A, A, A, 171, A, 64, 256, 172, 0, None) == 2
     assert f(A, A, A, A, 172, A, -1, 256, 172, 0, None) == 2
     assert f(A, A, A, A, 172, MIS, 64, 256, 172, 0, None) == 6
-    rows = cap // (1376 * 2)                         # 24385 rows of the 7B shard width fit
+    rows = cap // (1408 * 2)                         # 23831 rows of the 7B shard width fit (stride 1408)
     assert tsp.mlp_workspace_size(rows, 1376) <= cap < tsp.mlp_workspace_size(rows + 1, 1376)
     assert f(A, A, A, A, 1376, A, rows + 1, 4096, 1376, 0, None) == 5
     assert b"maximum" in tsp.load().tsp_last_error()
@@ -215,17 +215,17 @@ def test_layer_bwd_errors():
 def test_streamed_layer_workspace_and_errors():
     rup = lambda x: (x + 255) // 256 * 256
 
-    def want(M, d, Fs, fp, dg, hg, odd):
+    def want(M, d, Fs, fp, fh, dg, hg, odd):
         act = M * d * 2
         # the lone last head group of an odd D: two key halves, fp32 O and lse
         part = rup(2 * M * dg * 4) + rup(2 * M * hg * 4) if odd else 0
-        return (2 * rup(act) + rup(M * fp * 2) + 2 * rup(4 * dg * d * 2) + 2 * rup((2 * Fs + fp) * d * 2)
+        return (2 * rup(act) + rup(M * fh * 2) + 2 * rup(4 * dg * d * 2) + 2 * rup((2 * Fs + fp) * d * 2)
                 + part)
 
     good = _desc()
     ws = tsp.layer_streamed_workspace_size(good)
-    assert ws == want(64, 256, 172, 176, 64, 1, False)   # D = 4: pairs of groups only
-    assert tsp.layer_streamed_workspace_size(_desc(D=1, rank=0)) == want(256, 256, 688, 688, 256, 4, True)
+    assert ws == want(64, 256, 172, 176, 192, 64, 1, False)   # D = 4: pairs of groups only
+    assert tsp.layer_streamed_workspace_size(_desc(D=1, rank=0)) == want(256, 256, 688, 688, 704, 256, 4, True)
     # H % D != 0: a head group must hold whole heads
     assert tsp.layer_streamed_workspace_size(_desc(n_heads=2, head_dim=128)) == 0
     sh = [A] * 4
