@@ -246,10 +246,11 @@ TSP_API int tsp_mlp_shard_accum_noalloc(const void* x, const void* w1_j, const v
                                         tsp_stream_t stream);
 
 /* Workspace bytes tsp_layer_fwd needs for `desc` (0 if desc is invalid): Q and O of the
- * rank, bf16 [B, 2C, d] each, and the gated hidden of all D shards, bf16
- * [B*2C, D * round_up(F/D, 64)], in that order, each starting at a multiple of 256 bytes
- * (Q at offset 0, O at round_up(B*2C*d*2, 256)). After a call O holds the rank's attention
- * output, bf16 [B, 2C, H, hd] in local row order. */
+ * rank, bf16 [B, 2C, d] each, the gated hidden of all D shards, bf16
+ * [B*2C, D * round_up(F/D, 64)], and, when D is even and ceil(B*2C/256) * ceil(d/256) <= 128
+ * (short sequences), an fp32 [B*2C, d] partial sum of the down projection, in that order,
+ * each starting at a multiple of 256 bytes (Q at offset 0, O at round_up(B*2C*d*2, 256)).
+ * After a call O holds the rank's attention output, bf16 [B, 2C, H, hd] in local row order. */
 TSP_API size_t tsp_layer_workspace_size(const tsp_layer_desc* desc);
 
 /*

@@ -353,8 +353,16 @@ int check_desc(const tsp_layer_desc* desc) {
 }
 
 struct LayerCarve {
-  size_t q_off, o_off, h_off, total;
+  size_t q_off, o_off, h_off, p_off, total;  // p_off: 0 when there is no partial-sum region
 };
+
+// Whether the layer workspace carries an fp32 [M, d] partial sum for the down projection:
+// when its 256 x 256 output tiles would fill at most half of the 256 CUs (7B S=16K: 128
+// tiles), each tile runs as two work items over the two halves of the D-shard ring, and the
+// second half's sum lands there before the two are added.
+bool down_split_region(size_t M, size_t d, int D) {
+  return D % 2 == 0 && ((M + 255) / 256) * ((d + 255) / 256) <= 128;
+}
 
 LayerCarve carve(const tsp_layer_desc* d) {
   const size_t M = (size_t)d->batch * (size_t)(d->seq_len / d->fold);
@@ -365,6 +373,11 @@ LayerCarve carve(const tsp_layer_desc* d) {
   c.h_off = 2 * act;
   // Gated hidden of all D shards: [M, D * hidden_ld(F/D)] bf16.
   c.total = 2 * act + round_up(M * (size_t)d->fold * (size_t)hidden_ld(d->ffn / d->fold) * 2, kAlign);
+  c.p_off = 0;
+  if (down_split_region(M, (size_t)d->d_model, d->fold)) {
+    c.p_off = c.total;
+    c.total += round_up(M * (size_t)d->d_model * 4, kAlign);
+  }
   return c;
 }
 
@@ -436,7 +449,8 @@ int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const void* w
     if (int rc = hip_status(tsp::launch_gate_up_ring(attn_out, w1, w3, D, hbuf, ldh, ldseg, M, Fs, d, s),
                             "gate/up launch"))
       return rc;
-    if (int rc = hip_status(tsp::launch_down_ring(hbuf, ldh, ldseg, w2, ldw2, D, r, mlp_out, d, M, d, Fs, s),
+    float* part = c.p_off ? reinterpret_cast<float*>(base + c.p_off) : nullptr;
+    if (int rc = hip_status(tsp::launch_down_ring(hbuf, ldh, ldseg, w2, ldw2, D, r, mlp_out, d, M, d, Fs, part, s),
                             "down projection launch"))
       return rc;
     if (int rc = mark(4)) return rc;

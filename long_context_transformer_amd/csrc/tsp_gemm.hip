@@ -29,6 +29,8 @@
 // stores).
 // Workgroup -> tile: XCD-contiguous ranges (xcd_remap), then groups of 8 row-tiles
 // walked column-major so tiles running together on one XCD share A and B in its L2.
+#include <algorithm>
+
 #include "tsp_device.h"
 #include "tsp_internal.h"
 
@@ -428,6 +430,12 @@ struct Shards {
   int tn;           // SEG_N: column tiles per shard
   int nks;          // SEG_K: 32-wide k stages per shard
   int count;        // number of shards
+  // SEG_K in gemm_p only: parts > 1 splits the shards of every tile into `parts` equal runs,
+  // each its own work item; run p (in ring order) writes its fp32 sum to the epilogue's output
+  // (p = 0) or to part_c + (p - 1) part_stride (EpiAcc, overwrite), summed afterwards.
+  int parts;
+  float* part_c;
+  int64_t part_stride;
 };
 template <int SEG>
 struct SegArgOf {
@@ -805,25 +813,35 @@ void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / NWN, wn = wave % NWN;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int total = tiles_m * tiles_n;
-  // Stages per k segment (the whole reduction, or one shard under SEG_K) and segments.
+  const int tiles = tiles_m * tiles_n;
+  // Stages per k segment (the whole reduction, or one shard under SEG_K), segments, and the
+  // runs of segments a tile is split into (SEG_K parts).
   const int nks = (op.K + KB - 1) / KB;
-  int nseg = 1;
-  if constexpr (SEG == SEG_K) nseg = sg.count;
+  int nseg = 1, parts = 1;
+  if constexpr (SEG == SEG_K) {
+    nseg = sg.count;
+    parts = sg.parts > 1 ? sg.parts : 1;
+  }
+  const int total = tiles * parts;
   const bool khalf = (op.K % KB) != 0;
   if ((int)blockIdx.x >= total) return;
+  auto seg_lo = [&](int p) { return p * nseg / parts; };
 
-  // Tile v of the grouped order: row tile, column tile and (SEG_N) shard.
+  // Work item v of the grouped order: row tile, column tile, (SEG_N) shard and (SEG_K) part;
+  // the part is the slowest index.
   struct TileAt {
-    int m0, n0, j;
+    int m0, n0, j, p;
   };
   auto tile_at = [&](int v) {
-    const int t = xcd_remap(v, total);
+    int t = xcd_remap(v, total);
+    const int pt = t / tiles;
+    t -= pt * tiles;
     const int span = GM * tiles_n;
     const int first_m = (t / span) * GM;
     const int gsz = min(tiles_m - first_m, GM);
     const int in_g = t - (t / span) * span;
     TileAt r;
+    r.p = pt;
     r.m0 = (first_m + in_g % gsz) * BM;
     int nt = in_g / gsz;
     r.j = 0;
@@ -948,8 +966,9 @@ void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
   offsets(blockIdx.x);
   {
     const uint32_t base = lds_addr(smem) + wave * 1024;
-    const Ld l0 = ld_of(0, 0);
-    const Ld l1 = ld_of(0, 1);
+    const int s0 = seg_lo(tile_at(blockIdx.x).p);
+    const Ld l0 = ld_of(s0, 0);
+    const Ld l1 = ld_of(s0, 1);
 #pragma unroll
     for (int p = 0; p < 16; ++p) dma(p, base, l0);
 #pragma unroll
@@ -973,19 +992,22 @@ void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
   for (int v = blockIdx.x; v < total; v += gridDim.x) {
     const bool has_next = v + (int)gridDim.x < total;
     bool moved = false;  // the load offsets point at the next tile
-    for (int s = 0; s < nseg; ++s) {
+    const int pv = tile_at(v).p;
+    const int s_lo = seg_lo(pv), s_hi = seg_lo(pv + 1);
+    const int s_next = has_next ? seg_lo(tile_at(v + gridDim.x).p) : 0;
+    for (int s = s_lo; s < s_hi; ++s) {
       for (int kt = 0; kt < nks; ++kt, ++g) {
         const char* cur = smem + (g & 1) * STAGE;
         const char* nxt = smem + ((g + 1) & 1) * STAGE;
-        const bool first = s == 0 && kt == 0;
+        const bool first = s == s_lo && kt == 0;
         // The stage two ahead: (s2, k2) of this tile or of the next; past the workgroup's
         // last stage, this stage again (into its own buffer, which nobody reads again).
         int s2 = s, k2 = kt + 2;
         bool nx = false;
         if (k2 >= nks) {
           k2 -= nks;
-          if (++s2 == nseg) {
-            s2 = 0;
+          if (++s2 == s_hi) {
+            s2 = s_next;
             nx = true;
           }
         }
@@ -1029,6 +1051,8 @@ void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
     const TileAt tl = tile_at(v);
     Epi e = epi;
     if constexpr (SEG == SEG_N) e.shift_cols(tl.j * sg.out_col);
+    if constexpr (SEG == SEG_K && std::is_same<Epi, EpiAcc>::value)
+      if (tl.p > 0) e.c = sg.part_c + (int64_t)(tl.p - 1) * sg.part_stride;
     const int m0 = tl.m0, n0 = tl.n0;
     // Activation block mb, weight blocks 2 q and 2 q + 1 of each weight: lane l holds outputs
     // (m = l % 16, n = 4 (l / 16) .. + 3) of each block. A tile wholly inside C whose
@@ -1134,7 +1158,8 @@ hipError_t run_persist(const Operands& op, const Epi& epi, hipStream_t s, SegArg
     tn *= sg.count;
   }
   if constexpr (SEG == SEG_K) sg.nks = (op.K + KB - 1) / KB;
-  const int total = tm * tn;
+  int total = tm * tn;
+  if constexpr (SEG == SEG_K) total *= sg.parts > 1 ? sg.parts : 1;
   const int grid = total < device_cus() ? total : device_cus();
   hipLaunchKernelGGL((gemm_p<DUAL, SEG, GM, Epi>), dim3(grid), dim3(256), 0, s, op, epi, tm, tn, sg);
   return hipGetLastError();
@@ -1323,8 +1348,20 @@ hipError_t launch_gate_up_ring(const void* x, const void* const* w1, const void*
   return run_fast<128, 64, 64, 32, true, SEG_N>(op, epi, stream, sg);
 }
 
+// out[m, :N] += part[m, :N]: the sum of the two halves of a split down projection.
+__global__ __launch_bounds__(256) void add_rows_kernel(float* out, int64_t ldo, const float* part, int64_t ldp, int M,
+                                                       int N4) {
+  const int64_t n = (int64_t)M * N4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t m = i / N4, c = (i - m * N4) * 4;
+    f32x4* o = reinterpret_cast<f32x4*>(out + m * ldo + c);
+    *o += *reinterpret_cast<const f32x4*>(part + m * ldp + c);
+  }
+}
+
 hipError_t launch_down_ring(const void* h, int64_t ldh, int64_t ldseg, const void* const* w2, int64_t ldw2, int D,
-                            int rank, float* out, int64_t ldout, int M, int N, int Fs, hipStream_t stream) {
+                            int rank, float* out, int64_t ldout, int M, int N, int Fs, float* part,
+                            hipStream_t stream) {
   Operands op{static_cast<const bf16_t*>(h), ldh, nullptr, nullptr, ldw2, M, N, Fs};
   EpiAcc epi{out, ldout, 0};
   Shards sg{};
@@ -1341,6 +1378,21 @@ hipError_t launch_down_ring(const void* h, int64_t ldh, int64_t ldseg, const voi
   // from the MALL instead (with the 8-wave kernel, 8-row groups: 3.76 ms of MLP, 2-row
   // groups: 3.68 ms; with the persistent kernel 1-, 2-, 4-, 8- and 16-row groups all time
   // within 2%).
+  // With at most half a round of 256 x 256 tiles (7B S=16K: 128 tiles), each tile runs as two
+  // work items over the two halves of the ring, one per CU, and a pass adds the halves
+  // (230 -> 180 us against the 256 x 128 tile over the whole ring).
+  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  if (part && D % 2 == 0 && persist_ok(op) && 2 * t256 <= device_cus() && N % 4 == 0 && ldout % 4 == 0 &&
+      aligned16(out) && aligned16(part)) {
+    sg.parts = 2;
+    sg.part_c = part;
+    sg.part_stride = 0;
+    if (hipError_t e = run_persist<false, SEG_K, 2>(op, epi, stream, sg)) return e;
+    const int64_t n4 = (int64_t)M * (N / 4);
+    const int grid = (int)std::min<int64_t>((n4 + 255) / 256, 4 * (int64_t)device_cus());
+    hipLaunchKernelGGL(add_rows_kernel, dim3(grid), dim3(256), 0, stream, out, ldout, part, ldout, M, N / 4);
+    return hipGetLastError();
+  }
   switch (choose_tile(M, N)) {
     case Tile::k256x256:
       if (persist_ok(op)) return run_persist<false, SEG_K, 2>(op, epi, stream, sg);

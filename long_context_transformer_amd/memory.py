@@ -78,9 +78,11 @@ def shape_of(w):
 
 
 def layer_workspace(s):
-    """tsp_layer_workspace_size: Q, O bf16 [M, d]; gated hidden of all D shards."""
+    """tsp_layer_workspace_size: Q, O bf16 [M, d]; gated hidden of all D shards; with D even and
+    at most 128 output tiles of 256 x 256 in the down projection, an fp32 [M, d] partial sum."""
     act = _rup(s.M * s.d * BF16, ALIGN)
-    return 2 * act + _rup(s.M * s.D * s.Fh * BF16, ALIGN)
+    split = s.D % 2 == 0 and -(-s.M // 256) * -(-s.d // 256) <= 128
+    return 2 * act + _rup(s.M * s.D * s.Fh * BF16, ALIGN) + (_rup(s.M * s.d * F32, ALIGN) if split else 0)
 
 
 def streamed_workspace(s):
