@@ -51,6 +51,8 @@
 // v_dot2, so numerator and denominator use the same p.
 #include <math.h>
 
+#include <algorithm>
+
 #include "tsp_device.h"
 #include "tsp_internal.h"
 
@@ -95,6 +97,10 @@ struct AttnArgs {
   // [0, split) and [split, S); the item of half 1 writes o32 + part_o and lse + part_l.
   int split;
   int64_t part_o, part_l;
+  // Fused split launch (split > 0, fused != 0): the key halves of the later chunk's tiles and
+  // the earlier chunk's whole tiles in one launch; fused = later-chunk tiles per XCD, or -1
+  // where heads do not divide over the XCDs.
+  int fused;
   int64_t S;
   int64_t C;
   int rows;  // 2C local rows per sequence
@@ -130,8 +136,9 @@ struct Lay {
 struct TileSel {
   int b, h, qt;
   int key_lo, key_hi;
-  float* o32;
+  float* o32;    // key-range attention: fp32 O and log-sum-exp (nullptr: not written)
   float* lse32;
+  bf16_t* o16;   // bf16 O (nullptr: not written)
 };
 
 // Item -> (sequence-head, query tile). A tile's work grows with its index (its last position
@@ -147,7 +154,54 @@ __device__ __forceinline__ TileSel select_tile(const AttnArgs& a) {
   t.key_hi = a.key_hi;
   t.o32 = a.o32;
   t.lse32 = a.lse;
+  t.o16 = a.o;
   if constexpr (PART) {
+    if (a.fused != 0) {
+      // fused > 0: XCD x receives blocks x, x + 8, ... in order. Its first 2 f blocks are the
+      // two key halves of its f later-chunk tiles (whole heads), which start together; the
+      // next f are the same heads' earlier-chunk tiles, heaviest first, each taken by the CU
+      // that frees first: the one whose half over [split, end) was shortest. A later tile t
+      // and the earlier tile n - 1 - t together see 2 D C + BR keys, so with
+      // split = D C + BR / 2 a short half and its earlier tile take about as long as a first
+      // half. fused < 0 (heads do not divide over the XCDs): the same items, halves first,
+      // then the earlier tiles heaviest first, in block order.
+      const int n_run = a.qt_hi - a.qt_lo;
+      int f, x, k;
+      if (a.fused > 0) {
+        f = a.fused;
+        x = (int)blockIdx.x % kNumXcd;
+        k = (int)blockIdx.x / kNumXcd;
+      } else {
+        f = a.items / 3;
+        x = 0;
+        k = (int)blockIdx.x;
+      }
+      const int nbh = f / n_run;  // (sequence, head) pairs per XCD (all of them when fused < 0)
+      int bh, qt;
+      if (k < 2 * f) {
+        const int half = k & 1;
+        const int L = x * f + (k >> 1);
+        bh = L / n_run;
+        qt = a.qt_hi - 1 - (L - bh * n_run);
+        t.key_lo = half ? a.split : 0;
+        t.key_hi = half ? (int)a.S : a.split;
+        t.o32 += half * a.part_o;
+        t.lse32 += half * a.part_l;
+        t.o16 = nullptr;
+      } else {
+        const int j = k - 2 * f;
+        bh = x * nbh + j % nbh;
+        qt = a.qt_lo - 1 - j / nbh;
+        t.key_lo = 0;
+        t.key_hi = (int)a.S;
+        t.o32 = nullptr;
+        t.lse32 = nullptr;
+      }
+      t.b = bh / a.Hrun;
+      t.h = a.h0 + bh - t.b * a.Hrun;
+      t.qt = qt;
+      return t;
+    }
     if (a.split > 0) {  // both halves of a tile are consecutive items
       const int half = item & 1;
       item >>= 1;
@@ -192,6 +246,7 @@ __device__ __forceinline__ TileSel uniform_tile(const TileSel& v) {
   t.key_hi = u(v.key_hi);
   t.o32 = up(v.o32);
   t.lse32 = up(v.lse32);
+  t.o16 = reinterpret_cast<bf16_t*>(up(reinterpret_cast<float*>(v.o16)));
   return t;
 }
 
@@ -199,7 +254,7 @@ __device__ __forceinline__ TileSel uniform_tile(const TileSel& v) {
 // its rows (accumulate: the range adds nothing; only the bf16 O is written if asked).
 template <int HD, int QB>
 __device__ __forceinline__ void store_no_keys(const AttnArgs& a, const TileSel& t, const int (&qi)[QB], int hl) {
-  if (a.accumulate && a.o == nullptr) return;
+  if (a.accumulate && t.o16 == nullptr) return;
   const int64_t tok = (int64_t)a.H * HD, otok = (int64_t)a.oH * HD;
   const int oh = t.h - a.oh0;
 #pragma unroll
@@ -214,10 +269,10 @@ __device__ __forceinline__ void store_no_keys(const AttnArgs& a, const TileSel& 
         const int dim = db * 32 + 8 * g + 4 * hl;
         if (a.accumulate) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(op + dim);
-          *reinterpret_cast<uint2*>(a.o + ro + dim) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<uint2*>(t.o16 + ro + dim) = pack_bf16x4(v[0], v[1], v[2], v[3]);
         } else {
           *reinterpret_cast<f32x4*>(op + dim) = f32x4{};
-          if (a.o != nullptr) *reinterpret_cast<uint2*>(a.o + ro + dim) = make_uint2(0u, 0u);
+          if (t.o16 != nullptr) *reinterpret_cast<uint2*>(t.o16 + ro + dim) = make_uint2(0u, 0u);
         }
       }
     if (!a.accumulate && hl == 0) t.lse32[((int64_t)t.b * a.oH + oh) * a.prows + (qi[qb] - a.prow0)] = -INFINITY;
@@ -251,8 +306,9 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, const TileSel& t, 
     for (int qb = 0; qb < QB; ++qb) {
       if (qi[qb] >= a.rows) continue;
       const int64_t ro = ((int64_t)t.b * a.rows + qi[qb]) * tok + (int64_t)t.h * HD;
-      float* op = t.o32 + ((int64_t)t.b * a.prows + (qi[qb] - a.prow0)) * otok + (int64_t)oh * HD;
-      float* lp = t.lse32 + ((int64_t)t.b * a.oH + oh) * a.prows + (qi[qb] - a.prow0);
+      const bool w32 = t.o32 != nullptr;
+      float* op = w32 ? t.o32 + ((int64_t)t.b * a.prows + (qi[qb] - a.prow0)) * otok + (int64_t)oh * HD : nullptr;
+      float* lp = w32 ? t.lse32 + ((int64_t)t.b * a.oH + oh) * a.prows + (qi[qb] - a.prow0) : nullptr;
       const float lse_b = l_run[qb] > 0.0f ? (m_s[qb] + __log2f(l_run[qb])) * 0.69314718055994531f : -INFINITY;
       // Overwrite: weights (0, 1). Accumulate: the log-sum-exp merge with what the
       // accumulator holds (both lanes of the row read it before lane hl == 0 writes).
@@ -279,11 +335,12 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, const TileSel& t, 
           const float s = wb * inv[qb];
           f32x4 val = {o[4 * g] * s, o[4 * g + 1] * s, o[4 * g + 2] * s, o[4 * g + 3] * s};
           if (a.accumulate) val += wa * *reinterpret_cast<const f32x4*>(op + dim);
-          *reinterpret_cast<f32x4*>(op + dim) = val;
-          if (a.o != nullptr) *reinterpret_cast<uint2*>(a.o + ro + dim) = pack_bf16x4(val[0], val[1], val[2], val[3]);
+          if (w32) *reinterpret_cast<f32x4*>(op + dim) = val;
+          if (t.o16 != nullptr)
+            *reinterpret_cast<uint2*>(t.o16 + ro + dim) = pack_bf16x4(val[0], val[1], val[2], val[3]);
         }
       }
-      if (hl == 0) *lp = lse_new;
+      if (w32 && hl == 0) *lp = lse_new;
     }
     return;
   }
@@ -1257,6 +1314,7 @@ AttnArgs base_args(const void* q, const void* k_full, const void* v_full, int B,
   a.split = 0;
   a.part_o = 0;
   a.part_l = 0;
+  a.fused = 0;
   const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)hd);
   a.scale_log2 = sc * 1.4426950408889634f;
   return a;
@@ -1443,24 +1501,27 @@ hipError_t launch_attn_merge_halves(const float* o32, const float* lse, void* o_
   return merge_halves_rows(o32, lse, o_out, B, rows, H, hd, h0, h_run, rows, 0, stream);
 }
 
-// Two-part attention for launches of at most one round of tiles (one per CU): the time is
-// then that of the heaviest tile, and the later zigzag chunk's tiles see up to (2D - r) C
-// keys against at most (r + 1) C for the earlier chunk's. The earlier chunk's tiles run as
-// they are (bf16 O); each later-chunk tile runs as two items, keys [0, split) and
-// [split, end), with split at half of that chunk's key span, into fp32 partials of the later
-// chunk's rows only, merged by log-sum-exp into bf16 O. Every later-chunk row lies at or after
-// split, so both halves see keys. Applies when chunks hold whole tiles and the later chunk's
-// span is at least twice the earlier one's (r <= (2D - 2) / 3).
+// Two-part attention for launches of at most one round of tiles (one per CU): the time of a
+// plain launch is then that of the heaviest tile, a later zigzag chunk's tile that sees up to
+// (2D - r) C keys. Instead, one launch runs each later-chunk tile as two items, keys
+// [0, split) and [split, end), into fp32 partials of the later chunk's rows, and each
+// earlier-chunk tile whole (bf16 O); the earlier tiles wait for the CUs whose second half
+// ends first (the item order is in select_tile). A later tile t and the earlier tile
+// n - 1 - t see 2 D C + BR keys together whatever the rank, so with split = D C + BR / 2 every
+// CU sees about D C + BR / 2 keys. A log-sum-exp pass merges the halves into bf16 O. Every
+// later-chunk row lies at or after split (split is clamped to the later chunk's start), so
+// both halves see keys. Applies when chunks hold whole tiles and the tiles fill at most one
+// round.
 constexpr int kCus = 256;
 
 int attn_two_part_split(int B, int64_t S, int D, int rank, int H) {
   const int64_t C = S / (2 * D);
   if (C <= 0 || C % BR != 0) return 0;
-  const int64_t n_qt = 2 * C / BR;
-  if ((int64_t)B * H * n_qt > kCus) return 0;
-  if (3 * (int64_t)rank > 2 * (int64_t)D - 2) return 0;
-  const int64_t split = ((2 * (int64_t)D - rank) * C / 2) / BC * BC;
-  if (split <= 0 || split > (2 * (int64_t)D - 1 - rank) * C) return 0;
+  const int64_t nt = C / BR;               // tiles per chunk and (sequence, head)
+  const int64_t nl = (int64_t)B * H * nt;  // tiles per chunk over every (sequence, head)
+  if (2 * nl > kCus) return 0;
+  const int64_t split = std::min((int64_t)D * C + BR / 2, (2 * (int64_t)D - 1 - rank) * C) / BC * BC;
+  if (split <= 0) return 0;
   return (int)split;
 }
 
@@ -1473,18 +1534,12 @@ hipError_t launch_attn_two_part(const void* q, const void* k_full, const void* v
                                 int64_t S, int D, int rank, int H, int hd, float scale, hipStream_t stream) {
   const int split = attn_two_part_split(B, S, D, rank, H);
   if (split <= 0) return hipErrorInvalidValue;
-  AttnArgs e = base_args(q, k_full, v_full, B, S, D, rank, H, hd, scale);
-  const int c_tiles = (int)(e.C / BR);
-  // earlier chunk: tiles [0, C / BR), bf16 O
-  e.o = static_cast<bf16_t*>(o);
-  e.qt_hi = c_tiles;
-  e.items = B * H * c_tiles;
-  if (hipError_t err = launch<false>(e, hd, stream)) return err;
-  // later chunk: tiles [C / BR, 2C / BR), two key halves each, partials of rows [C, 2C)
   AttnArgs l = base_args(q, k_full, v_full, B, S, D, rank, H, hd, scale);
+  const int c_tiles = (int)(l.C / BR);
   const int64_t units = (int64_t)B * l.C * H;
   float* o32 = static_cast<float*>(part);
-  l.o32 = o32;
+  l.o = static_cast<bf16_t*>(o);  // the earlier chunk's tiles
+  l.o32 = o32;                    // the later chunk's halves: rows [C, 2C)
   l.lse = o32 + 2 * units * hd;
   l.qt_lo = c_tiles;
   l.prow0 = (int)l.C;
@@ -1492,7 +1547,9 @@ hipError_t launch_attn_two_part(const void* q, const void* k_full, const void* v
   l.split = split;
   l.part_o = units * hd;
   l.part_l = units;
-  l.items = 2 * B * H * (l.n_qt - c_tiles);
+  const int nl = B * H * c_tiles;
+  l.fused = nl % kNumXcd == 0 && (nl / kNumXcd) % c_tiles == 0 ? nl / kNumXcd : -1;
+  l.items = 3 * nl;
   l.strided = 1;
   if (hipError_t err = launch<true>(l, hd, stream)) return err;
   return merge_halves_rows(o32, l.lse, o, B, (int)l.C, H, hd, 0, H, l.rows, (int)l.C, stream);

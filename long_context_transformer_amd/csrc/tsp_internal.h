@@ -82,10 +82,11 @@ hipError_t launch_attn_split(const void* q, const void* k_full, const void* v_fu
                              hipStream_t stream);
 hipError_t launch_attn_merge_halves(const float* o32, const float* lse, void* o_out, int B, int rows, int H, int hd,
                                     int h0, int h_run, hipStream_t stream);
-// Causal attention of all heads for launches of at most one tile per CU: the earlier zigzag
-// chunk's tiles write bf16 O directly; each later-chunk tile runs as two key halves split at
-// attn_two_part_split(...) into fp32 partials of the later chunk's rows (`part`, 16-byte
-// aligned, attn_two_part_bytes(...) bytes), then merged into bf16 O. attn_two_part_split
+// Causal attention of all heads for launches of at most one tile per CU, in one launch: the
+// earlier zigzag chunk's tiles write bf16 O directly; each later-chunk tile runs as two key
+// halves split at attn_two_part_split(...) into fp32 partials of the later chunk's rows
+// (`part`, 16-byte aligned, attn_two_part_bytes(...) bytes), then merged into bf16 O by a
+// second launch. attn_two_part_split
 // returns 0 where this does not apply (launch_attn serves those shapes).
 int attn_two_part_split(int B, int64_t S, int D, int rank, int H);
 size_t attn_two_part_bytes(int B, int64_t S, int D, int H, int hd);

@@ -297,10 +297,13 @@ LAYER_MID = [  # B, S, D, rank, H, hd, F, w2_view
     (1, 512, 8, 5, 8, 64, 2304, False),       # D = 8, ring wraps at rank 5, Fs = 288
     (1, 768, 2, 1, 4, 64, 1040, "separate"),  # Fs = 520, shards in separate allocations
     (1, 256, 4, 2, 4, 64, 696, False),        # Fs = 174: per-shard steps (Fs % 8 != 0)
-    # at most one query tile per CU: the later chunk's tiles run as two key halves
-    (1, 4096, 4, 0, 4, 64, 1024, False),      # split at 2048
-    (1, 4096, 4, 2, 4, 64, 2048, False),      # split at 1536
+    # at most one query tile per CU: the later chunk's tiles run as two key halves beside the
+    # earlier chunk's whole tiles, in one launch
+    (1, 4096, 4, 0, 4, 64, 1024, False),      # split at D C + 128 = 2176; heads do not divide over 8 XCDs
+    (1, 4096, 4, 2, 4, 64, 2048, False),      # split at 2176
     (1, 1024, 1, 0, 2, 128, 1024, False),     # D = 1: split at the chunk boundary (position C)
+    (1, 2048, 4, 1, 8, 64, 1024, False),      # one head per XCD, split at 1152
+    (1, 2048, 4, 3, 8, 128, 2048, False),     # one head per XCD, split at the later chunk's start 1024
 ]
 
 
