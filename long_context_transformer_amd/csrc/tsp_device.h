@@ -71,6 +71,15 @@ __device__ __forceinline__ void dma16_sbase(const void* base, uint32_t voff, uin
   const uint64_t ps = ((uint64_t)hi << 32) | (uint64_t)lo;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ps), "s"(lds) : "memory");
 }
+// 4-byte form of dma16_sbase (global_load_lds_dword): one lane per 128-byte line pulls lines
+// into the caches ahead of their 16-byte loads; its LDS destination is scratch nobody reads.
+__device__ __forceinline__ void dma4_sbase(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  const uint64_t ps = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(ps), "s"(lds) : "memory");
+}
 __device__ __forceinline__ void dma16_vaddr(const void* addr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds) : "memory");
 }
