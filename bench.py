@@ -97,17 +97,24 @@ def step(st):
                   st["w2"], st["kf"], st["vf"], st["attn_out"], st["mlp_out"], st["ws"])
 
 
-def time_layer(st, steps, warmup):
+def time_layer(st, steps, warmup, warmup_s=0.0):
     """Times `steps` steps, each between its own pair of HIP events on the launch stream
     (torch's current stream, which the library launches on). Returns per-step statistics
     (median, min, max, mean, and the whole timed region) in ms, the wall time, and the
-    per-phase averages from the library's events recorded inside those same steps."""
+    per-phase averages from the library's events recorded inside those same steps.
+    Untimed warmup: `warmup` steps, then more until `warmup_s` seconds have passed (the
+    GPU's clock takes some tens of ms of work to settle; short steps need more of them)."""
     import statistics
     import torch
     from long_context_transformer_amd import tsp
     for _ in range(warmup):
         step(st)
     torch.cuda.synchronize()
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < warmup_s:
+        for _ in range(5):
+            step(st)
+        torch.cuda.synchronize()
     tsp.timing_start(steps)
     ev = lambda: torch.cuda.Event(enable_timing=True)
     marks = [(ev(), ev()) for _ in range(steps)]
@@ -631,7 +638,7 @@ def main():
                 for r in ranks:
                     ww = base.with_rank(r)
                     s2 = setup(ww, r)
-                    st2, _, ph2 = time_layer(s2, 10 if ww.S >= 65536 else 20, 3)
+                    st2, _, ph2 = time_layer(s2, 10 if ww.S >= 65536 else 20, 3, warmup_s=0.2)
                     ms2 = st2["median"]
                     fl, afl = layer_flops(ww.B, ww.S, ww.D, ww.d_model, ww.n_heads, ww.head_dim, ww.ffn)
                     ams = ph2["attention"]
