@@ -296,8 +296,10 @@ TSP_API int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const
  *   copy stream   copies the shards into the slots (hipMemcpyDeviceToDeviceNoCU: the copy
  *                 engines), the one-GPU stand-in for receiving the broadcast. An attention
  *                 slot is refilled in two parts: its QKV rows once the QKV launch that read
- *                 them is done, its W_o columns once the W_O launch that read them is done.
- *                 The MLP shards 0 and 1 are copied right after the attention shards 0, 1.
+ *                 them is done, its W_o columns once the W_O launch that read them is done;
+ *                 an MLP slot likewise: its W1/W3 rows after the gate/up launch, its W2
+ *                 after the down projection. The MLP shards 0 and 1 are copied right after
+ *                 the attention shards 0, 1.
  *   attention     head groups t = j = 0 .. D-1 in pairs (t, t+1), one per attention slot;
  *                 pair p runs on streams[p % 2]: the QKV of each group (its Q columns, its
  *                 columns of the rank's K/V rows), then causal attention of the pair's
@@ -308,8 +310,11 @@ TSP_API int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const
  *                 registers) added to an fp32 accumulator, pairs in order; the last step
  *                 stores the sum as bf16 attn_out.
  *   streams[0]    the MLP ring after the last W_O step, t = 0 .. D-1 on shard
- *                 j = (r - t) mod D: the gated hidden of shard j, then its down projection
- *                 added to mlp_out.
+ *                 j = (r - t) mod D, one per MLP slot: the gated hidden of each step, and
+ *                 after steps t and t+1 (t even) one down projection that sums both shards
+ *                 in fp32 registers (step t first) and adds the sum to mlp_out. With D odd
+ *                 the last step's down projection runs alone; shard widths that are not a
+ *                 multiple of 8 run every step alone.
  * mlp_out doubles as the fp32 accumulator of the W_O partials before the MLP overwrites
  * it. The other streams first wait for the work already queued on streams[0]; on return
  * streams[0] waits for everything the call queued, so outputs are ready in its order.
@@ -321,9 +326,10 @@ TSP_API int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const
  * on first use, never freed); calls that overlap on the same streams from different
  * threads are not supported.
  * Workspace (tsp_layer_streamed_workspace_size; 0 if desc is invalid): Q and O bf16
- * [B 2C, d] each, the gated hidden of one shard bf16 [B 2C, round_up(Fs, 64)], two attention slots, two
- * MLP slots and, when D is odd, the fp32 O and log-sum-exp of the last group's attention
- * over keys [0, S/2) and [S/2, S) (merged into O).
+ * [B 2C, d] each, the gated hidden of two shards bf16 [B 2C, 2 round_up(Fs, 64)] (one shard
+ * if D = 1; the down projections run over pairs of steps), two attention slots, two MLP slots and,
+ * when D is odd, the fp32 O and log-sum-exp of the last group's attention over keys
+ * [0, S/2) and [S/2, S) (merged into O).
  * Errors: as tsp_layer_fwd; TSP_ERR_SHAPE if H % D != 0 or n_streams is not 1 or 4.
  */
 TSP_API size_t tsp_layer_streamed_workspace_size(const tsp_layer_desc* desc);

@@ -450,7 +450,7 @@ int tsp_layer_fwd(const tsp_layer_desc* desc, const void* x_shard, const void* w
                             "gate/up launch"))
       return rc;
     float* part = c.p_off ? reinterpret_cast<float*>(base + c.p_off) : nullptr;
-    if (int rc = hip_status(tsp::launch_down_ring(hbuf, ldh, ldseg, w2, ldw2, D, r, mlp_out, d, M, d, Fs, part, s),
+    if (int rc = hip_status(tsp::launch_down_ring(hbuf, ldh, ldseg, w2, ldw2, D, r, mlp_out, d, 0, M, d, Fs, part, s),
                             "down projection launch"))
       return rc;
     if (int rc = mark(4)) return rc;
@@ -678,7 +678,8 @@ StreamedCarve carve_streamed(const tsp_layer_desc* d) {
   c.o_off = at;
   at += act;
   c.h_off = at;
-  at += mlp_ws_bytes((int64_t)M, (int64_t)Fs);
+  // Gated hidden of two shards (the MLP ring runs in pairs of steps), one with D = 1.
+  at += round_up(M * (size_t)(d->fold >= 2 ? 2 : 1) * (size_t)c.fh * 2, kAlign);
   for (int i = 0; i < 2; ++i) {
     c.slot_a[i] = at;
     at += round_up(c.attn_shard * 2, kAlign);
@@ -757,12 +758,13 @@ int tsp_layer_fwd_streamed(const tsp_layer_desc* desc, const void* x_shard, cons
   hipStream_t cp = pick(3);
 
   hipEvent_t* ev = nullptr;
-  if (int rc = stream_events(&ev, 16)) return rc;
+  if (int rc = stream_events(&ev, 20)) return rc;
   hipEvent_t ev_start = ev[0], wo_last = ev[1];
-  hipEvent_t *q_full = ev + 2, *q_free = ev + 4;    // QKV part of an attention slot
-  hipEvent_t *o_full = ev + 6, *o_free = ev + 8;    // W_o part of an attention slot
-  hipEvent_t *m_full = ev + 10, *m_free = ev + 12;  // MLP slot
-  hipEvent_t* attn_done = ev + 14;                  // per attention stream
+  hipEvent_t *q_full = ev + 2, *q_free = ev + 4;      // QKV part of an attention slot
+  hipEvent_t *o_full = ev + 6, *o_free = ev + 8;      // W_o part of an attention slot
+  hipEvent_t *g_full = ev + 10, *g_free = ev + 12;    // W1/W3 part of an MLP slot
+  hipEvent_t *d_full = ev + 14, *d_free = ev + 16;    // W2 part of an MLP slot
+  hipEvent_t* attn_done = ev + 18;                    // per attention stream
   auto rec = [](hipEvent_t e, hipStream_t st) { return hip_status(hipEventRecord(e, st), "hipEventRecord"); };
   auto wait = [](hipStream_t st, hipEvent_t e) {
     return hip_status(hipStreamWaitEvent(st, e, 0), "hipStreamWaitEvent");
@@ -782,9 +784,17 @@ int tsp_layer_fwd_streamed(const tsp_layer_desc* desc, const void* x_shard, cons
     return fill(slot_a[t & 1] + qkv_part, static_cast<const tsp::bf16_t*>(w_attn[t]) + qkv_part, dg * d,
                 t >= 2 ? o_free[t & 1] : nullptr, o_full[t & 1]);
   };
-  auto fill_mlp = [&](int t) {
+  // An MLP slot is refilled in two parts: its W1/W3 rows once the gate/up launch that read
+  // them is done, its W2 once the down projection is done.
+  const size_t w13_part = 2 * (size_t)Fs * (size_t)d;
+  auto fill_mlp13 = [&](int t) {
     const int j = ((r - t) % D + D) % D;  // ring order
-    return fill(slot_m[t & 1], w_mlp[j], c.mlp_shard, t >= 2 ? m_free[t & 1] : nullptr, m_full[t & 1]);
+    return fill(slot_m[t & 1], w_mlp[j], w13_part, t >= 2 ? g_free[t & 1] : nullptr, g_full[t & 1]);
+  };
+  auto fill_mlp2 = [&](int t) {
+    const int j = ((r - t) % D + D) % D;
+    return fill(slot_m[t & 1] + w13_part, static_cast<const tsp::bf16_t*>(w_mlp[j]) + w13_part,
+                c.mlp_shard - w13_part, t >= 2 ? d_free[t & 1] : nullptr, d_full[t & 1]);
   };
 
   if (int rc = rec(ev_start, s0)) return rc;
@@ -794,8 +804,10 @@ int tsp_layer_fwd_streamed(const tsp_layer_desc* desc, const void* x_shard, cons
     if (int rc = fill_qkv(t)) return rc;
     if (int rc = fill_wo(t)) return rc;
   }
-  for (int t = 0; t < 2 && t < D; ++t)
-    if (int rc = fill_mlp(t)) return rc;
+  for (int t = 0; t < 2 && t < D; ++t) {
+    if (int rc = fill_mlp13(t)) return rc;
+    if (int rc = fill_mlp2(t)) return rc;
+  }
 
   // Head groups in pairs (t, t+1), one group per slot: the pair's QKV launches, then its
   // attention as one launch over both groups' heads, on comp[(t / 2) % 2]; then one W_O
@@ -853,21 +865,54 @@ int tsp_layer_fwd_streamed(const tsp_layer_desc* desc, const void* x_shard, cons
   if (int rc = rec(wo_last, s_wo)) return rc;
   if (int rc = wait(s0, wo_last)) return rc;
 
-  // MLP ring on streams[0], shard j = (r - t) mod D at step t.
+  // MLP ring on streams[0], shard j = (r - t) mod D at step t, one per slot: the gated hidden
+  // of each step into its own block of a two-shard hidden, and after every second step one
+  // down projection whose fp32 sum runs over both steps' shards in registers (step t - 1
+  // first) and is added to mlp_out once: half the read-modify-write passes over mlp_out. A
+  // slot's W1/W3 rows refill once its gate/up launch is done (in time for the step two later,
+  // a gate/up and a down projection later); its W2 once the pair's down projection is done.
+  // A lone last step (D odd) runs its down projection alone; shard widths the two-shard
+  // kernels cannot take run every step alone.
+  auto w1_of = [&](int sl) -> const tsp::bf16_t* { return slot_m[sl]; };
+  auto w3_of = [&](int sl) -> const tsp::bf16_t* { return slot_m[sl] + (size_t)Fs * d; };
+  auto w2_of = [&](int sl) -> const tsp::bf16_t* { return slot_m[sl] + 2 * (size_t)Fs * d; };
+  const void* w1p[2] = {w1_of(0), w1_of(1)};
+  const void* w3p[2] = {w3_of(0), w3_of(1)};
+  const void* w2p[2] = {w2_of(0), w2_of(1)};
+  const bool pairs = D >= 2 && tsp::mlp_ring_fusable(w1p, w3p, w2p, c.fp, 2, M, d, Fs, 2 * c.fh);
+  const int64_t ldh = pairs ? 2 * c.fh : c.fh;
   for (int t = 0; t < D; ++t) {
     const int sl = t & 1;
-    const tsp::bf16_t* w1 = slot_m[sl];
-    const tsp::bf16_t* w3 = slot_m[sl] + (size_t)Fs * d;
-    const tsp::bf16_t* w2 = slot_m[sl] + 2 * (size_t)Fs * d;
-    if (int rc = wait(s0, m_full[sl])) return rc;
-    if (int rc = hip_status(tsp::launch_gate_up(attn_out, d, w1, w3, d, hbuf, c.fh, M, Fs, d, s0), "gate/up launch"))
-      return rc;
-    if (int rc = hip_status(tsp::launch_down_acc(hbuf, c.fh, w2, c.fp, mlp_out, d, M, d, Fs, t > 0 ? 1 : 0, s0),
-                            "down projection launch"))
+    tsp::bf16_t* hb = static_cast<tsp::bf16_t*>(hbuf) + (pairs ? (size_t)sl * (size_t)c.fh : 0);
+    if (int rc = wait(s0, g_full[sl])) return rc;
+    if (int rc = hip_status(tsp::launch_gate_up(attn_out, d, w1_of(sl), w3_of(sl), d, hb, ldh, M, Fs, d, s0),
+                            "gate/up launch"))
       return rc;
     if (t + 2 < D) {
-      if (int rc = rec(m_free[sl], s0)) return rc;
-      if (int rc = fill_mlp(t + 2)) return rc;
+      if (int rc = rec(g_free[sl], s0)) return rc;
+      if (int rc = fill_mlp13(t + 2)) return rc;
+    }
+    if (pairs && sl == 1) {  // steps t - 1 (slot 0) and t (slot 1): ring order is slot order
+      for (int u = 0; u < 2; ++u)
+        if (int rc = wait(s0, d_full[u])) return rc;
+      if (int rc = hip_status(tsp::launch_down_ring(hbuf, ldh, c.fh, w2p, c.fp, 2, 0, mlp_out, d, t > 1 ? 1 : 0, M, d,
+                                                    Fs, nullptr, s0),
+                              "down projection launch"))
+        return rc;
+      for (int u = t - 1; u <= t; ++u)
+        if (u + 2 < D) {
+          if (int rc = rec(d_free[u & 1], s0)) return rc;
+          if (int rc = fill_mlp2(u + 2)) return rc;
+        }
+    } else if (!pairs || t == D - 1) {
+      if (int rc = wait(s0, d_full[sl])) return rc;
+      if (int rc = hip_status(tsp::launch_down_acc(hb, ldh, w2_of(sl), c.fp, mlp_out, d, M, d, Fs, t > 0 ? 1 : 0, s0),
+                              "down projection launch"))
+        return rc;
+      if (t + 2 < D) {
+        if (int rc = rec(d_free[sl], s0)) return rc;
+        if (int rc = fill_mlp2(t + 2)) return rc;
+      }
     }
   }
   return ok();

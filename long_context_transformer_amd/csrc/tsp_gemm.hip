@@ -1072,7 +1072,10 @@ void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
     Epi e = epi;
     if constexpr (SEG == SEG_N) e.shift_cols(tl.j * sg.out_col);
     if constexpr (SEG == SEG_K && std::is_same<Epi, EpiAcc>::value)
-      if (tl.p > 0) e.c = sg.part_c + (int64_t)(tl.p - 1) * sg.part_stride;
+      if (tl.p > 0) {
+        e.c = sg.part_c + (int64_t)(tl.p - 1) * sg.part_stride;
+        e.accumulate = 0;
+      }
     const int m0 = tl.m0, n0 = tl.n0;
     // Activation block mb, weight blocks 2 q and 2 q + 1 of each weight: lane l holds outputs
     // (m = l % 16, n = 4 (l / 16) .. + 3) of each block. A tile wholly inside C whose
@@ -1380,10 +1383,10 @@ __global__ __launch_bounds__(256) void add_rows_kernel(float* out, int64_t ldo, 
 }
 
 hipError_t launch_down_ring(const void* h, int64_t ldh, int64_t ldseg, const void* const* w2, int64_t ldw2, int D,
-                            int rank, float* out, int64_t ldout, int M, int N, int Fs, float* part,
+                            int rank, float* out, int64_t ldout, int accumulate, int M, int N, int Fs, float* part,
                             hipStream_t stream) {
   Operands op{static_cast<const bf16_t*>(h), ldh, nullptr, nullptr, ldw2, M, N, Fs};
-  EpiAcc epi{out, ldout, 0};
+  EpiAcc epi{out, ldout, accumulate ? 1 : 0};
   Shards sg{};
   for (int t = 0; t < D; ++t) {
     const int j = ((rank - t) % D + D) % D;  // shard held at ring step t

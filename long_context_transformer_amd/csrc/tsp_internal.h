@@ -50,13 +50,14 @@ bool mlp_ring_fusable(const void* const* w1, const void* const* w3, const void* 
 // H[:, j*ldseg + n] = silu(X W1_j^T) * (X W3_j^T) for every shard j and n < Fs.
 hipError_t launch_gate_up_ring(const void* x, const void* const* w1, const void* const* w3, int D, void* h,
                                int64_t ldh, int64_t ldseg, int M, int Fs, int d, hipStream_t stream);
-// out[M, N] = sum over ring steps t = 0..D-1 (shard j = (rank - t) mod D, in that order) of
-// H[:, j*ldseg : j*ldseg + Fs] W2_j^T, the fp32 sum held in registers and stored once.
-// part: NULL, or fp32 scratch [M, ldout] the call may use when the output tiles fill at most
-// half the CUs: the first and second halves of the ring then run as separate work items
-// (each summing its shards in ring order), the second into part, and out = first + second.
+// out[M, N] (+)= sum over ring steps t = 0..D-1 (shard j = (rank - t) mod D, in that order)
+// of H[:, j*ldseg : j*ldseg + Fs] W2_j^T, the fp32 sum held in registers and stored (or added,
+// accumulate != 0) once. part: NULL, or fp32 scratch [M, ldout] the call may use when the
+// output tiles fill at most half the CUs: the first and second halves of the ring then run as
+// separate work items (each summing its shards in ring order), the second into part, and
+// out = (out +) first + second.
 hipError_t launch_down_ring(const void* h, int64_t ldh, int64_t ldseg, const void* const* w2, int64_t ldw2, int D,
-                            int rank, float* out, int64_t ldout, int M, int N, int Fs, float* part,
+                            int rank, float* out, int64_t ldout, int accumulate, int M, int N, int Fs, float* part,
                             hipStream_t stream);
 
 // Causal attention of the rank's queries against full-sequence K/V (step a3).

@@ -86,13 +86,13 @@ def layer_workspace(s):
 
 
 def streamed_workspace(s):
-    """tsp_layer_streamed_workspace_size: Q, O, the gated hidden of one shard, two attention
-    slots, two MLP slots and, when D is odd, the two fp32 key halves of the lone last head
-    group's O and log-sum-exp (pairs of groups write O directly)."""
+    """tsp_layer_streamed_workspace_size: Q, O, the gated hidden of two shards (one if D = 1),
+    two attention slots, two MLP slots and, when D is odd, the two fp32 key halves of the lone
+    last head group's O and log-sum-exp (pairs of groups write O directly)."""
     dg = s.d // s.D
     hg = s.H // s.D
     act = _rup(s.M * s.d * BF16, ALIGN)
-    hid = _rup(s.M * s.Fh * BF16, ALIGN)
+    hid = _rup(s.M * (2 if s.D >= 2 else 1) * s.Fh * BF16, ALIGN)
     slot_a = _rup(4 * dg * s.d * BF16, ALIGN)
     slot_m = _rup((2 * s.Fs + s.Fp) * s.d * BF16, ALIGN)
     part = _rup(2 * s.M * dg * F32, ALIGN) + _rup(2 * s.M * hg * F32, ALIGN)

@@ -219,8 +219,8 @@ def test_streamed_layer_workspace_and_errors():
         act = M * d * 2
         # the lone last head group of an odd D: two key halves, fp32 O and lse
         part = rup(2 * M * dg * 4) + rup(2 * M * hg * 4) if odd else 0
-        return (2 * rup(act) + rup(M * fh * 2) + 2 * rup(4 * dg * d * 2) + 2 * rup((2 * Fs + fp) * d * 2)
-                + part)
+        hid = rup(M * (1 if odd and dg == d else 2) * fh * 2)   # two shards' gated hidden (one if D = 1)
+        return (2 * rup(act) + hid + 2 * rup(4 * dg * d * 2) + 2 * rup((2 * Fs + fp) * d * 2) + part)
 
     good = _desc()
     ws = tsp.layer_streamed_workspace_size(good)
