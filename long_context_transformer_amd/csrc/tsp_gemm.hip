@@ -776,17 +776,27 @@ int device_cus() {
   return cache[dev];
 }
 
-template <bool DUAL>
+// Tile shapes: 256 x 256 (one weight), 256 x (128 + 128) (DUAL: two weights) and, NARROW,
+// 256 x 128 (one weight; waves of 128 x 64) for launches where the 256 x 256 tiles would leave
+// much of the last round of CUs idle.
+template <bool DUAL, bool NARROW = false>
 struct PGeom {
   static constexpr int KB = 64, ROWB = KB * 2, CPR = KB / 8, RPI = 1024 / ROWB;
-  static constexpr int BM = 256, BN = DUAL ? 128 : 256, WM = 128, WN = DUAL ? 64 : 128;
+  static constexpr int BM = 256, BN = DUAL || NARROW ? 128 : 256, WM = 128, WN = DUAL || NARROW ? 64 : 128;
   static constexpr int NWN = BN / WN, NWAVE = 4;
   static constexpr int NB = DUAL ? 2 : 1;
   static constexpr int MB = WM / 16, NBK = WN / 16, NW = NB * NBK;  // activation / weight blocks of 16
   static constexpr int ATILE = BM * KB * 2, BTILE = BN * KB * 2;
   static constexpr int STAGE = ATILE + NB * BTILE;
   static constexpr int AINS = ATILE / 1024 / NWAVE, BINS = BTILE / 1024 / NWAVE;
-  static_assert(MB * NW == 64 && MB + NW == 16 && AINS + NB * BINS == 16, "64 MFMAs, 16 reads, 16 loads per step");
+  // Per 32-wide k step and wave: MFMAs, fragment reads, and (per stage) 16-byte load instructions.
+  static constexpr int NMF = MB * NW, NRD = MB + NW, NLD = AINS + NB * BINS;
+  // One read (load) every RS (DS) MFMAs of a step; in the half step of a half stage, every RSH (DSH).
+  static constexpr int RS = NMF / NRD, DS = NMF / NLD;
+  static constexpr int RSH = NMF / 2 / NRD > 0 ? NMF / 2 / NRD : 1, DSH = NMF / 2 / NLD > 0 ? NMF / 2 / NLD : 1;
+  static_assert(NWN * (BM / WM) == NWAVE && RS >= 1 && DS >= 1 && NRD <= NMF / 2 && NLD <= NMF / 2,
+                "four waves; every read and load fits its step");
+  static_assert(!(DUAL && NARROW), "the gated pair has one tile shape");
   // MFMA i of a k step: activation block mb = i / NW, weight block w = i % NW = (nb, nbk);
   // its accumulator a[4 (w MB + mb) ..].
   static constexpr int mb_of(int i) { return i / NW; }
@@ -804,10 +814,10 @@ __device__ __forceinline__ int swz8(int r) { return r & 7; }
 // prefetch, which the stage wait leaves in flight. It pays where the activation operand does
 // not fit the MALL and comes from HBM (the down projection's gated hidden at 7B S=128K:
 // 3600 -> 3310 cycles per stage); where the operands sit in the MALL it costs slightly.
-template <bool DUAL, int SEG, int GM, class Epi, int PF = 0>
+template <bool DUAL, int SEG, int GM, class Epi, int PF = 0, bool NARROW = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
-  using G = PGeom<DUAL>;
+  using G = PGeom<DUAL, NARROW>;
   constexpr int KB = G::KB, ROWB = G::ROWB, CPR = G::CPR, RPI = G::RPI;
   constexpr int BM = G::BM, BN = G::BN, WM = G::WM, WN = G::WN, NWN = G::NWN, NWAVE = G::NWAVE;
   constexpr int NB = G::NB, MB = G::MB, NBK = G::NBK, NW = G::NW;
@@ -952,7 +962,7 @@ void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
   // load number (i - lo) / ds of the stage *ld into the buffer at LDS address la (ds != 0).
   auto step = [&](const int set, const bool zero, auto LO, auto HI, const int rs, const char* rst, const int rset,
                   const int rks, const int ds, const Ld* ld, const uint32_t la) __attribute__((always_inline)) {
-    static_for<64>([&](auto I) __attribute__((always_inline)) {
+    static_for<G::NMF>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
       if constexpr (i >= decltype(LO)::value && i < decltype(HI)::value) {
         constexpr int j = i - decltype(LO)::value;
@@ -960,15 +970,15 @@ void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
           gmma0<G::acc_of(i)>(fw[set][G::w_of(i)], fa[set][G::mb_of(i)]);
         else
           gmma<G::acc_of(i)>(fw[set][G::w_of(i)], fa[set][G::mb_of(i)]);
-        if (rs && j % rs == 0 && j / rs < 16) rd(rset, rst, rks, j / rs);
-        if (ds && j % ds == ds / 2 && j / ds < 16) dma(j / ds, la, *ld);
+        if (rs && j % rs == 0 && j / rs < G::NRD) rd(rset, rst, rks, j / rs);
+        if (ds && j % ds == ds / 2 && j / ds < G::NLD) dma(j / ds, la, *ld);
         __builtin_amdgcn_sched_barrier(0);
       }
     });
   };
   using I0 = std::integral_constant<int, 0>;
-  using I32 = std::integral_constant<int, 32>;
-  using I64 = std::integral_constant<int, 64>;
+  using I32 = std::integral_constant<int, G::NMF / 2>;  // half a step
+  using I64 = std::integral_constant<int, G::NMF>;      // a whole step
 
   // Prologue: stages 0 and 1 of the first tile (every tile has at least two), then the
   // first step's fragments.
@@ -979,15 +989,15 @@ void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
     const Ld l0 = ld_of(s0, 0);
     const Ld l1 = ld_of(s0, 1);
 #pragma unroll
-    for (int p = 0; p < 16; ++p) dma(p, base, l0);
+    for (int p = 0; p < G::NLD; ++p) dma(p, base, l0);
 #pragma unroll
-    for (int p = 0; p < 16; ++p) dma(p, base + STAGE, l1);
+    for (int p = 0; p < G::NLD; ++p) dma(p, base + STAGE, l1);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 #pragma unroll
-  for (int r = 0; r < 16; ++r) rd(0, smem, 0, r);
+  for (int r = 0; r < G::NRD; ++r) rd(0, smem, 0, r);
 
   // Waits for this wave's reads of the stage and its loads of the next one, then meets the
   // other waves: past it every wave has read the stage and every load of the next has landed.
@@ -1039,10 +1049,10 @@ void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
         // the MFMAs that follow it.
         asm volatile("" ::"s"(l2.a), "s"(l2.b), "s"(l2.b2), "s"(l2.hm), "s"(la));
         if (kt + 1 < nks || !khalf) {
-          if (first) step(0, true, I0{}, I64{}, 4, cur, 1, 1, 0, nullptr, 0u);
-          else step(0, false, I0{}, I64{}, 4, cur, 1, 1, 0, nullptr, 0u);
+          if (first) step(0, true, I0{}, I64{}, G::RS, cur, 1, 1, 0, nullptr, 0u);
+          else step(0, false, I0{}, I64{}, G::RS, cur, 1, 1, 0, nullptr, 0u);
           sync();
-          step(1, false, I0{}, I64{}, 4, nxt, 0, 0, 4, &l2, la);
+          step(1, false, I0{}, I64{}, G::RS, nxt, 0, 0, G::DS, &l2, la);
           if constexpr (PF > 0) {
             pf_out = kt + PF < nks;
             if (pf_out) {
@@ -1056,7 +1066,7 @@ void gemm_p(Operands op, Epi epi, int tiles_m, int tiles_n, SegArg<SEG> sg) {
           // first fragments go to set 1 and move to set 0 afterwards.
           step(0, false, I0{}, I32{}, 0, cur, 0, 0, 0, nullptr, 0u);
           sync();
-          step(0, false, I32{}, I64{}, 2, nxt, 1, 0, 2, &l2, la);
+          step(0, false, I32{}, I64{}, G::RSH, nxt, 1, 0, G::DSH, &l2, la);
           pf_out = false;
 #pragma unroll
           for (int w = 0; w < NW; ++w) fw[0][w] = fw[1][w];
@@ -1171,9 +1181,9 @@ hipError_t run_fast(const Operands& op, const Epi& epi, hipStream_t s, SegArg<SE
 // hold at least two 64-wide stages.
 inline bool persist_ok(const Operands& op) { return op.K % 32 == 0 && op.K > 64; }
 
-template <bool DUAL, int SEG = SEG_NONE, int GM = kGroupM, int PF = 0, class Epi>
+template <bool DUAL, int SEG = SEG_NONE, int GM = kGroupM, int PF = 0, bool NARROW = false, class Epi>
 hipError_t run_persist(const Operands& op, const Epi& epi, hipStream_t s, SegArg<SEG> sg = {}) {
-  constexpr int BM = 256, BN = DUAL ? 128 : 256, KB = 64;
+  constexpr int BM = PGeom<DUAL, NARROW>::BM, BN = PGeom<DUAL, NARROW>::BN, KB = 64;
   const int tm = (op.M + BM - 1) / BM;
   int tn = (op.N + BN - 1) / BN;
   if constexpr (SEG == SEG_N) {
@@ -1184,7 +1194,7 @@ hipError_t run_persist(const Operands& op, const Epi& epi, hipStream_t s, SegArg
   int total = tm * tn;
   if constexpr (SEG == SEG_K) total *= sg.parts > 1 ? sg.parts : 1;
   const int grid = total < device_cus() ? total : device_cus();
-  hipLaunchKernelGGL((gemm_p<DUAL, SEG, GM, Epi, PF>), dim3(grid), dim3(256), 0, s, op, epi, tm, tn, sg);
+  hipLaunchKernelGGL((gemm_p<DUAL, SEG, GM, Epi, PF, NARROW>), dim3(grid), dim3(256), 0, s, op, epi, tm, tn, sg);
   return hipGetLastError();
 }
 
@@ -1234,7 +1244,9 @@ hipError_t run_single(const Operands& op, const Epi& epi, hipStream_t s) {
     case Tile::k256x256:
       if (persist_ok(op)) return run_persist<false>(op, epi, s);
       return run_fast<256, 256, 128, 64, false>(op, epi, s);
-    case Tile::k256x128: return run_fast<256, 128, 64, 64, false>(op, epi, s);
+    case Tile::k256x128:
+      if (persist_ok(op)) return run_persist<false, SEG_NONE, kGroupM, 0, true>(op, epi, s);
+      return run_fast<256, 128, 64, 64, false>(op, epi, s);
     default: return run_fast<128, 128, 64, 64, false>(op, epi, s);
   }
 }

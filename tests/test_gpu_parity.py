@@ -34,6 +34,7 @@ QKV_CASES = [  # B, S, D, rank, H, hd
     (2, 1200, 3, 1, 4, 128),   # C = 200: ragged row tiles
     (1, 640, 1, 0, 2, 128),    # D = 1
     (1, 4096, 2, 1, 32, 128),  # M = 2048, N = 12288: 384 tiles of 256 x 256 (the large-tile kernel)
+    (1, 8192, 8, 3, 32, 128),  # M = 1024, N = 12288: 384 tiles of 256 x 128 (the narrow persistent tile)
 ]
 
 
@@ -170,8 +171,9 @@ MLP_CASES = [  # M, d, Fs, ld_w2 (0 = Fs)
     (4096, 4096, 4096, 0),
     (4000, 4096, 4104, 0),   # ragged: M tail 160, gate/up N tail 8, down K tail 8
     # down 256 x 128 (M = 2048, N = 4096: 256 x 256 tiles would fill half the CUs)
-    (2048, 4096, 1376, 0),
-    (1900, 4096, 1000, 0),   # ragged: M tail 108, down K tail 40
+    (2048, 4096, 1376, 0),   # the narrow persistent tile, a half stage at the end of K
+    (1950, 4096, 1024, 0),   # the narrow persistent tile, ragged M (tail 158)
+    (1900, 4096, 1000, 0),   # ragged: M tail 108, down K tail 40 (8-wave kernel)
 ]
 
 
