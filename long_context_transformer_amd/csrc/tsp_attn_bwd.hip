@@ -253,18 +253,25 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         s = mfma32x32x16(row_frag<HD>(ktile, 32 * kb, l32, hl, ks), qf[ks], s);
         dp = mfma32x32x16(row_frag<HD>(vtile, 32 * kb, l32, hl, ks), df[ks], dp);
       }
+      // Where some row of the wave may not see some key of the block (a wave-uniform test), the
+      // scores of keys past the row's position become -inf, so that their P is 0; other blocks
+      // carry no mask.
+      if (k0 + 31 > wave_pos0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (key > qpos) s[r] = -INFINITY;
+        }
+      }
       // dS one half of the block (registers 8 half .. 8 half + 7) at a time, packed and
       // consumed by the dQ products before the next half is computed
-      const bool whole = k0 + 31 <= wave_pos0;  // every row of the wave sees every key of the block
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         float ds[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * half + e;
-          const float ex = __builtin_amdgcn_exp2f(s[r] * c2 - lse2);
-          const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const float p = (whole || key <= qpos) ? ex : 0.0f;
+          const float p = __builtin_amdgcn_exp2f(s[r] * c2 - lse2);
           ds[e] = p * (dp[r] - dsum);
         }
         const bf16x8 dsf = pack8(ds);
