@@ -418,12 +418,29 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       s = mfma32x32x16(row_frag<HD>(qtile, 0, l32, hl, ks), kf[ks], s);
       dp = mfma32x32x16(row_frag<HD>(otile, 0, l32, hl, ks), row_frag<HD>(vkeys, 32 * wave, l32, hl, ks), dp);
     }
-    // P and dS one half of the block (registers 8 half .. 8 half + 7) at a time, each packed
-    // and consumed by the dV and dK products before the next half is computed. The block's
-    // first row has its lowest position: if that row sees the wave's last key, every row
-    // sees every key and the mask is skipped.
+    // The block's first row has its lowest position: if that row sees the wave's last key,
+    // every row sees every key (a wave-uniform test). Otherwise each register whose (row, key)
+    // pair is not visible gets score -inf (so P = 0) and dP = D (so dP - D = 0: a key past
+    // the rank's last position has K and V rows the caller need not fill, and its score and
+    // dP may be NaN); the P and dS code below is then the same for every block, with no
+    // per-register compare or select.
     const bool whole =
         q0 + 31 < a.rows && wave_klast < a.S && wave_klast <= (int)zigzag_pos(q0, a.C, a.rank, a.D);
+    if (!whole) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
+        const int row = q0 + qr;
+        const bool ok =
+            kvalid & (row < a.rows) & (kj <= (int)zigzag_pos(min(row, a.rows - 1), a.C, a.rank, a.D));
+        if (!ok) {
+          s[r] = -INFINITY;
+          dp[r] = d_s[qr];
+        }
+      }
+    }
+    // P and dS one half of the block (registers 8 half .. 8 half + 7) at a time, each packed
+    // and consumed by the dV and dK products before the next half is computed.
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       float p[8], ds[8];
@@ -431,22 +448,9 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * half + e;
         const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
-        // every operand read and the exponential unconditionally, then a select: a load
-        // under the condition would make a branch and a wait per register
         const float ex = __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[qr] * kLog2e);
-        const float dsub = dp[r] - d_s[qr];
-        if (whole) {
-          p[e] = ex;
-          ds[e] = ex * dsub;
-        } else {
-          // A key past the rank's last position has K and V rows the caller need not fill:
-          // dsub may then be NaN, so dS is selected, not multiplied by a zero P.
-          const int row = q0 + qr;
-          const bool ok =
-              kvalid & (row < a.rows) & (kj <= (int)zigzag_pos(min(row, a.rows - 1), a.C, a.rank, a.D));
-          p[e] = ok ? ex : 0.0f;
-          ds[e] = ok ? ex * dsub : 0.0f;
-        }
+        p[e] = ex;
+        ds[e] = ex * (dp[r] - d_s[qr]);
       }
       const bf16x8 pf = pack8(p);
       const bf16x8 dsf = pack8(ds);
