@@ -444,13 +444,20 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       float p[8], ds[8];
+      // registers 4 j .. 4 j + 3 hold query rows 8 j + 4 hl .. + 3: their lse and D as one
+      // 16-byte read each
+      f32x4 lq[2], dq4[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        lq[jj] = *reinterpret_cast<const f32x4*>(lse_s + 8 * (2 * half + jj) + 4 * hl);
+        dq4[jj] = *reinterpret_cast<const f32x4*>(d_s + 8 * (2 * half + jj) + 4 * hl);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * half + e;
-        const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
-        const float ex = __builtin_amdgcn_exp2f(s[r] * c2 - lse_s[qr] * kLog2e);
+        const float ex = __builtin_amdgcn_exp2f(s[r] * c2 - lq[e >> 2][e & 3] * kLog2e);
         p[e] = ex;
-        ds[e] = ex * (dp[r] - d_s[qr]);
+        ds[e] = ex * (dp[r] - dq4[e >> 2][e & 3]);
       }
       const bf16x8 pf = pack8(p);
       const bf16x8 dsf = pack8(ds);
