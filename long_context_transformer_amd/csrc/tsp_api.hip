@@ -44,8 +44,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 constexpr int64_t kMaxI32 = 2147483647;
 
 // Checks shared by every entry point that knows (B, S, D, rank): S % 2D == 0, rank
-// in range, and local-row counts that fit the kernels' 32-bit row indices. B = 0 or S = 0
-// is a valid empty problem (callers return before touching any pointer).
+// in range, and local-row counts and key positions that fit the kernels' 32-bit indices.
+// B = 0 or S = 0 is a valid empty problem (callers return before touching any pointer).
 int check_fold(int64_t B, int64_t S, int64_t D, int64_t rank) {
   if (B < 0) return fail(TSP_ERR_SHAPE, "batch must be >= 0 (got %lld)", (long long)B);
   if (D < 1) return fail(TSP_ERR_SHAPE, "fold D must be >= 1 (got %lld)", (long long)D);
@@ -54,6 +54,7 @@ int check_fold(int64_t B, int64_t S, int64_t D, int64_t rank) {
                 (long long)(2 * D));
   if (rank < 0 || rank >= D) return fail(TSP_ERR_RANK, "rank %lld outside [0, %lld)", (long long)rank, (long long)D);
   if (B * (S / D) > kMaxI32 / 4) return fail(TSP_ERR_UNSUPPORTED, "B*S/D too large for 32-bit row indices");
+  if (S > kMaxI32 / 2) return fail(TSP_ERR_UNSUPPORTED, "S too large for 32-bit key positions");
   return TSP_OK;
 }
 

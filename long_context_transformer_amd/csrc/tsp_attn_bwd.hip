@@ -145,6 +145,12 @@ __device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
   return as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
 }
 
+// zigzag_pos in 32-bit arithmetic for the per-block tests (the positions of one sequence, and
+// S itself, stay below 2^31: the launcher checks).
+__device__ __forceinline__ int zz_pos(int i, int C, int r, int D) {
+  return i < C ? r * C + i : (2 * D - 1 - r) * C + (i - C);
+}
+
 template <int HD>
 __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq(BwdArgs a) {
   using L = BLay<HD>;
@@ -318,6 +324,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const int key0 = kt * kKeysPerWg;
   const int64_t tok = (int64_t)a.H * HD;
 
+  const int C32 = (int)a.C, S32 = (int)a.S;
   const int kw0 = key0 + 32 * wave;  // the wave's first key
   const int kj = kw0 + l32;
   const int wave_klast = kw0 + 31;
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const float* lse_s = &lsed[st][0];  // natural log
     const float* d_s = &lsed[st][kKvStage];
     // no row of the block sees the wave's keys (its last row has the highest position)
-    if (kw0 > (int)zigzag_pos(min(q0 + kKvStage - 1, a.rows - 1), a.C, a.rank, a.D)) continue;
+    if (kw0 > zz_pos(min(q0 + kKvStage - 1, a.rows - 1), C32, a.rank, a.D)) continue;
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -425,14 +432,14 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // dP may be NaN); the P and dS code below is then the same for every block, with no
     // per-register compare or select.
     const bool whole =
-        q0 + 31 < a.rows && wave_klast < a.S && wave_klast <= (int)zigzag_pos(q0, a.C, a.rank, a.D);
+        q0 + 31 < a.rows && wave_klast < S32 && wave_klast <= zz_pos(q0, C32, a.rank, a.D);
     if (!whole) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qr = 8 * (r >> 2) + 4 * hl + (r & 3);  // query row of register r in the block
         const int row = q0 + qr;
         const bool ok =
-            kvalid & (row < a.rows) & (kj <= (int)zigzag_pos(min(row, a.rows - 1), a.C, a.rank, a.D));
+            kvalid & (row < a.rows) & (kj <= zz_pos(min(row, a.rows - 1), C32, a.rank, a.D));
         if (!ok) {
           s[r] = -INFINITY;
           dp[r] = d_s[qr];

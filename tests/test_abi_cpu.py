@@ -158,6 +158,8 @@ def test_layer_desc_and_workspace():
     assert tsp.layer_workspace_size(_desc(d_model=250)) == 0  # d != H*hd
     assert tsp.layer_workspace_size(_desc(head_dim=80, d_model=320)) == 0
     assert tsp.layer_workspace_size(_desc(rank=4)) == 0
+    assert tsp.layer_workspace_size(_desc(S=2**31, D=8, ffn=1024)) == 0  # key positions beyond 32 bits
+    assert tsp.layer_workspace_size(_desc(S=2**29, D=8, ffn=1024)) > 0
 
 
 def test_layer_errors():
