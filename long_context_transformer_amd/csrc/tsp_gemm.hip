@@ -11,10 +11,12 @@
 //   EpiAcc      fp32 accumulator, overwrite or add (the down projection of a shard)
 //
 // Three kernels share the epilogues. gemm_p (the persistent path, below) takes the large
-// shapes: 256 x 256 tiles, one wave per SIMD, the 16 x 16 x 32 MFMA, one workgroup per CU
-// walking its tiles. gemm_fast (the "fast path") serves the other operands that take
-// 16-byte chunks, with smaller tiles or k extents gemm_p does not take; gemm_nt,
-// register-staged, serves the rest (only the tiny workload's odd shard width):
+// shapes: 256 x 256 tiles (256 x 128 per weight for the gated pair; 256 x 128 for a single
+// weight where 256 x 256 tiles would leave much of a round of CUs idle), one wave per SIMD,
+// the 16 x 16 x 32 MFMA, one workgroup per CU walking its tiles. gemm_fast (the "fast
+// path") serves the other operands that take 16-byte chunks, with smaller tiles or k extents
+// gemm_p does not take; gemm_nt, register-staged, serves the rest (only the tiny workload's
+// odd shard width):
 // Tiling of gemm_nt: 256 threads = 4 waves in a 2 x 2 grid over a BM x BN output tile;
 // each wave owns a (BM/2) x (BN/2) block made of 32 x 32 MFMA tiles
 // (v_mfma_f32_32x32x16_bf16). K advances in stages of 64 through a double-buffered LDS
