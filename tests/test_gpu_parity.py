@@ -34,6 +34,7 @@ QKV_CASES = [  # B, S, D, rank, H, hd
     (2, 1200, 3, 1, 4, 128),   # C = 200: ragged row tiles
     (1, 640, 1, 0, 2, 128),    # D = 1
     (1, 4096, 2, 1, 32, 128),  # M = 2048, N = 12288: 384 tiles of 256 x 256 (the large-tile kernel)
+    (1, 8192, 2, 0, 32, 128),  # M = 4096, N = 12288: 768 tiles of 256 x 256 in one launch
     (1, 8192, 8, 3, 32, 128),  # M = 1024, N = 12288: 384 tiles of 256 x 128 (the narrow persistent tile)
 ]
 
